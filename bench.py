@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Throughput of the biased-sigmoid top-4 MoE layer on one MI355X.
+
+One step = one lfm_moe_forward (router, dispatch, gate/up, down, combine)
+over one batch of synthetic tokens whose inputs and weights are already
+resident in HBM.  The headline workload is the decode-shaped layer (N = 64
+tokens, seed 1); the prefill-shaped layer (N = 4096, seed 2) is measured in
+the same run and reported beside it.  Expert weights are cycled over
+`--copies` identical device copies so that the 256 MB Infinity Cache does
+not serve repeated steps.
+
+Prints ONE JSON line (rank 0, N = 1 GPU).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s at N=64 and N=4096; % HBM BW / % bf16 MFMA peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+D, E, K, FF = 2048, 64, 4, 1536
+GATEUP_W_BYTES = 2 * FF * D * 2            # 12,582,912 per active expert
+DOWN_W_BYTES = D * FF * 2                  # 6,291,456 per active expert
+EXPERT_BYTES = GATEUP_W_BYTES + DOWN_W_BYTES  # 18,874,368
+ROUTER_BYTES = E * D * 2 + E * 4
+FLOP_PER_TOKEN = 2 * E * D + K * 2 * 3 * D * FF  # 75,759,616
+
+
+def layer_bytes(A, N):
+    """Algorithmic HBM bytes of one layer call: active experts' weights once,
+    the router, x read in bf16 and out written in fp32."""
+    return A * EXPERT_BYTES + ROUTER_BYTES + N * (D * 2 + D * 4)
+
+
+def gateup_bytes(A, N):
+    """Algorithmic bytes of the gate/up kernel: active gate/up weights once,
+    the token rows once, H written once in bf16."""
+    return A * GATEUP_W_BYTES + N * D * 2 + K * N * FF * 2
+
+
+def gateup_flops(N):
+    return K * N * 2 * (2 * FF) * D
+
+
+def down_bytes(A, N):
+    return A * DOWN_W_BYTES + K * N * FF * 2 + K * N * D * 4
+
+
+def down_flops(N):
+    return K * N * 2 * D * FF
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def prepare(name, copies):
+    import torch
+    import synth
+    import biased_sigmoid_top_amd as moe
+    w = synth.WORKLOADS[name]
+    N = w["N"]
+    log(f"generating {name}: N={N} seed={w['seed']} skew={w['skew']}")
+    layer = synth.layer_inputs(N, w["seed"], w["skew"])
+    dev = torch.device("cuda")
+    X = moe.rmsnorm(layer["z"].to(dev))          # input preparation, not timed
+    W_r, bias = layer["W_r"].to(dev), layer["bias"].to(dev)
+    Wgu0 = synth.pack_gateup(layer["W_gate"], layer["W_up"]).to(dev)
+    Wd0 = layer["W_down"].contiguous().to(dev)
+    Wgu = [Wgu0] + [Wgu0.clone() for _ in range(copies - 1)]
+    Wd = [Wd0] + [Wd0.clone() for _ in range(copies - 1)]
+    out = torch.empty(N, D, dtype=torch.float32, device=dev)
+    # Routing structure of this input (one untimed call through the _ws form).
+    from biased_sigmoid_top_amd import _lib
+    ws = moe.alloc_workspace(N)
+    moe.forward(X, W_r, bias, Wgu0, Wd0, out, workspace=ws)
+    offs = moe.workspace_view(ws, N, _lib.WS_OFFSETS, torch.int32, (65,)).cpu()
+    counts = (offs[1:] - offs[:-1]).tolist()
+    del ws
+    torch.cuda.synchronize()
+    return dict(name=name, N=N, seed=w["seed"], layer=layer, X=X, W_r=W_r, bias=bias,
+                Wgu=Wgu, Wd=Wd, out=out, counts=counts)
+
+
+def time_steps(p, steps, warmup):
+    import torch
+    import biased_sigmoid_top_amd as moe
+    c = len(p["Wgu"])
+
+    def step(i):
+        moe.forward(p["X"], p["W_r"], p["bias"], p["Wgu"][i % c], p["Wd"][i % c], p["out"])
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+
+    # Second pass over the same steps with per-kernel hipEvents recorded by
+    # the library on the launch stream.
+    moe.timing_enable(True)
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    stages = moe.timing_read()
+    moe.timing_enable(False)
+    per_kernel = {s: (ms / n if n else 0.0) for s, (ms, n) in stages.items()}
+    assert torch.isfinite(p["out"]).all().item(), "non-finite layer output"
+    return wall_ms, per_kernel
+
+
+def summarize(p, wall_ms, per_kernel):
+    N = p["N"]
+    A = sum(1 for c in p["counts"] if c > 0)
+    s = wall_ms * 1e-3
+    tok_s = N / s
+    gbs = layer_bytes(A, N) / s / 1e9
+    tflops = N * FLOP_PER_TOKEN / s / 1e12
+    gu_ms = per_kernel["gateup"]
+    dn_ms = per_kernel["down"]
+    return dict(
+        N=N, active_experts=A, max_tokens_per_expert=max(p["counts"]),
+        ms_per_step=wall_ms, tokens_per_s=tok_s,
+        layer_gbs=gbs, layer_hbm_frac=gbs / HBM_PEAK_GBS,
+        layer_tflops=tflops, layer_mfma_frac=tflops / BF16_PEAK_TFLOPS,
+        kernel_ms=per_kernel,
+        gateup_gbs=gateup_bytes(A, N) / (gu_ms * 1e-3) / 1e9 if gu_ms else None,
+        gateup_tflops=gateup_flops(N) / (gu_ms * 1e-3) / 1e12 if gu_ms else None,
+        down_gbs=down_bytes(A, N) / (dn_ms * 1e-3) / 1e9 if dn_ms else None,
+        down_tflops=down_flops(N) / (dn_ms * 1e-3) / 1e12 if dn_ms else None,
+    )
+
+
+def cpu_baseline(p, budget_s):
+    """The oracle as it stands, timed on this host's cores on the same workload."""
+    import numpy as np
+    import threadpoolctl
+    import oracle
+    layer = p["layer"]
+    X = oracle.block_input(layer["z"].numpy())
+    args = (X, layer["W_r"].float().numpy(), layer["bias"].numpy(), layer["W_gate"].float().numpy(),
+            layer["W_up"].float().numpy(), layer["W_down"].float().numpy())
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.moe_forward(*args)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()
+                   if i.get("user_api") == "blas"), default=1)
+    return dict(value=reps * p["N"] / el, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"{reps} whole-layer oracle forwards of the {p['name']} workload "
+                       f"({p['N']} tokens each, float64 NumPy), {el:.1f} s")
+
+
+def copy_probe():
+    """A plain 1 GiB device copy, for calibrating HBM byte counters."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "copies": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=3, help="device copies of the expert weights")
+    ap.add_argument("--secondary", default="prefill_n4096",
+                    help="second workload reported beside the headline one ('none' for none)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="time budget of the oracle baseline (0 leaves it out)")
+    ap.add_argument("--copy-probe", action="store_true", help="only run a plain 1 GiB copy")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one MI355X: multi-GPU runs are not part of this build "
+              "(the layer would shard by tokens or by experts; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs the GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    import biased_sigmoid_top_amd  # noqa: F401  (fails loudly without the built library)
+
+    head = prepare("decode_n64", args.copies)
+    log(f"timing decode_n64: {args.steps} steps after {args.warmup} warm-up")
+    wall_ms, per_kernel = time_steps(head, args.steps, args.warmup)
+    h = summarize(head, wall_ms, per_kernel)
+    log(json.dumps(h))
+
+    second = None
+    if args.secondary != "none":
+        p2 = prepare(args.secondary, args.copies)
+        steps2 = max(5, args.steps // 10)
+        log(f"timing {args.secondary}: {steps2} steps")
+        w2, k2 = time_steps(p2, steps2, max(2, args.warmup // 10))
+        second = summarize(p2, w2, k2)
+        log(json.dumps(second))
+        del p2
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log(f"timing the oracle for ~{args.cpu_seconds:.0f} s on host cores")
+        cpu = cpu_baseline(head, args.cpu_seconds)
+
+    gu_ms = h["kernel_ms"]["gateup"]
+    A, N = h["active_experts"], h["N"]
+    roof = dict(bound="hbm", kernel="gateup_stream", achieved=h["gateup_gbs"], peak=HBM_PEAK_GBS,
+                unit="GB/s", frac=h["gateup_gbs"] / HBM_PEAK_GBS, traffic=None,
+                bytes_per_launch=gateup_bytes(A, N), avg_launch_ms=gu_ms)
+    line = dict(
+        metric=METRIC, value=h["tokens_per_s"], unit="tokens/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=h["ms_per_step"], higher_is_better=True, scaling="weak",
+        vs_baseline=None, dtype="bf16", data="synthetic",
+        config=dict(workload="decode_n64", N=N, d=D, experts=E, top_k=K, ff=FF, seed=head["seed"],
+                    active_experts=A, max_tokens_per_expert=h["max_tokens_per_expert"],
+                    weight_copies=args.copies),
+        layer=dict(gbs=h["layer_gbs"], hbm_frac=h["layer_hbm_frac"], tflops=h["layer_tflops"],
+                   mfma_frac=h["layer_mfma_frac"], kernel_ms=h["kernel_ms"]),
+        roofline=roof, cpu_baseline=cpu,
+    )
+    if second is not None:
+        line["prefill"] = dict(
+            workload=args.secondary, N=second["N"], active_experts=second["active_experts"],
+            ms_per_step=second["ms_per_step"], tokens_per_s=second["tokens_per_s"],
+            gbs=second["layer_gbs"], hbm_frac=second["layer_hbm_frac"],
+            tflops=second["layer_tflops"], mfma_frac=second["layer_mfma_frac"],
+            kernel_ms=second["kernel_ms"],
+            roofline=dict(bound="mfma", kernel="gateup", achieved=second["gateup_tflops"],
+                          peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                          frac=second["gateup_tflops"] / BF16_PEAK_TFLOPS,
+                          flops_per_launch=gateup_flops(second["N"]),
+                          avg_launch_ms=second["kernel_ms"]["gateup"]))
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,139 @@
+"""Python face of the C ABI: same names as include/lfm_moe.h, torch tensors in.
+
+PyTorch only provides device memory and streams here; every call goes
+straight to the HIP library through ctypes.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+HIDDEN, EXPERTS, TOP_K, FF = 2048, 64, 4, 1536
+
+
+def _stream(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _req(t: torch.Tensor, name: str, dtype, shape) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _weights(W_r, bias, W_gateup, W_down):
+    return (_req(W_r, "W_r", torch.bfloat16, (EXPERTS, HIDDEN)),
+            _req(bias, "bias", torch.float32, (EXPERTS,)),
+            _req(W_gateup, "W_gateup", torch.bfloat16, (EXPERTS, 2 * FF, HIDDEN)),
+            _req(W_down, "W_down", torch.bfloat16, (EXPERTS, HIDDEN, FF)))
+
+
+def abi_version() -> int:
+    return _lib.load().lfm_moe_abi_version()
+
+
+def workspace_bytes(N: int) -> int:
+    return int(_lib.load().lfm_moe_workspace_bytes(N))
+
+
+def workspace_offset(N: int, region: int) -> int:
+    return int(_lib.load().lfm_moe_workspace_offset(N, region))
+
+
+def alloc_workspace(N: int, device=None) -> torch.Tensor:
+    """A byte tensor big enough for lfm_moe_forward_ws at N tokens."""
+    return torch.empty(max(workspace_bytes(N), 256), dtype=torch.uint8,
+                       device=device if device is not None else "cuda")
+
+
+def workspace_view(ws: torch.Tensor, N: int, region: int, dtype, shape) -> torch.Tensor:
+    """A typed view of one workspace region (see lfm_moe_ws_region)."""
+    off = workspace_offset(N, region)
+    n = 1
+    for s in shape:
+        n *= s
+    nbytes = n * torch.empty((), dtype=dtype).element_size()
+    return ws[off:off + nbytes].view(dtype).view(*shape)
+
+
+def rmsnorm(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    N = x.shape[0]
+    px = _req(x, "x", torch.float32, (N, HIDDEN))
+    if out is None:
+        out = torch.empty(N, HIDDEN, dtype=torch.bfloat16, device=x.device)
+    po = _req(out, "out", torch.bfloat16, (N, HIDDEN))
+    _lib.call("lfm_moe_rmsnorm", px, po, N, _stream(stream))
+    return out
+
+
+def route(X, W_r, bias, idx=None, w=None, stream=None):
+    N = X.shape[0]
+    pX = _req(X, "X", torch.bfloat16, (N, HIDDEN))
+    pW = _req(W_r, "W_r", torch.bfloat16, (EXPERTS, HIDDEN))
+    pb = _req(bias, "bias", torch.float32, (EXPERTS,))
+    if idx is None:
+        idx = torch.empty(N, TOP_K, dtype=torch.int32, device=X.device)
+    if w is None:
+        w = torch.empty(N, TOP_K, dtype=torch.float32, device=X.device)
+    pi = _req(idx, "idx", torch.int32, (N, TOP_K))
+    pw = _req(w, "w", torch.float32, (N, TOP_K))
+    _lib.call("lfm_moe_route", pX, pW, pb, pi, pw, N, _stream(stream))
+    return idx, w
+
+
+def forward(X, W_r, bias, W_gateup, W_down, out=None, workspace=None, stream=None):
+    """out [N, 2048] fp32.  With ``workspace`` the _ws entry point is used."""
+    N = X.shape[0]
+    pX = _req(X, "X", torch.bfloat16, (N, HIDDEN))
+    pw = _weights(W_r, bias, W_gateup, W_down)
+    if out is None:
+        out = torch.empty(N, HIDDEN, dtype=torch.float32, device=X.device)
+    po = _req(out, "out", torch.float32, (N, HIDDEN))
+    if workspace is None:
+        _lib.call("lfm_moe_forward", pX, *pw, po, N, _stream(stream))
+    else:
+        _lib.call("lfm_moe_forward_ws", pX, *pw, po, N, workspace.data_ptr(),
+                  workspace.numel() * workspace.element_size(), _stream(stream))
+    return out
+
+
+def block_forward(x, W_r, bias, W_gateup, W_down, workspace=None, stream=None):
+    """x <- x + MoE(bf16(RMSNorm(x))) in place; returns x."""
+    N = x.shape[0]
+    px = _req(x, "x", torch.float32, (N, HIDDEN))
+    pw = _weights(W_r, bias, W_gateup, W_down)
+    if workspace is None:
+        _lib.call("lfm_moe_block_forward", px, *pw, N, _stream(stream))
+    else:
+        _lib.call("lfm_moe_block_forward_ws", px, *pw, N, workspace.data_ptr(),
+                  workspace.numel() * workspace.element_size(), _stream(stream))
+    return x
+
+
+def release() -> None:
+    _lib.load().lfm_moe_release()
+
+
+def timing_enable(on: bool) -> None:
+    """Per-kernel event timing of later layer calls (clears the totals)."""
+    _lib.call("lfm_moe_timing_enable", 1 if on else 0)
+
+
+def timing_read() -> dict:
+    """{stage: (total_ms, launches)} of the calls timed since timing_enable."""
+    import ctypes
+    ms = (ctypes.c_double * len(_lib.STAGES))()
+    n = (ctypes.c_int64 * len(_lib.STAGES))()
+    _lib.call("lfm_moe_timing_read", ctypes.addressof(ms), ctypes.addressof(n))
+    return {s: (ms[i], n[i]) for i, s in enumerate(_lib.STAGES)}

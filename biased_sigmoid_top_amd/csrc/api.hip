@@ -1,0 +1,395 @@
+// C ABI of the MoE layer: argument checks, workspace layout and the launch
+// sequence route -> dispatch -> gate/up -> down -> combine on one stream.
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/lfm_moe.h"
+#include "common.hpp"
+#include "launch.hpp"
+
+using namespace lfm;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+lfm_moe_status fail(lfm_moe_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+lfm_moe_status hip_fail(hipError_t e, const char* what) {
+  return fail(LFM_MOE_ERR_HIP, std::string(what) + ": " + hipGetErrorName(e) + " (" +
+                                   hipGetErrorString(e) + ")");
+}
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Sizes of the workspace regions, in lfm_moe_ws_region order.
+void region_sizes(int64_t N, size_t (&sz)[LFM_MOE_WS_REGIONS]) {
+  const size_t n = static_cast<size_t>(N);
+  const size_t rows = n * kTopK;
+  const size_t nrb = (n + route_block_tokens(N) - 1) / route_block_tokens(N);
+  sz[LFM_MOE_WS_IDX] = rows * sizeof(int32_t);
+  sz[LFM_MOE_WS_W] = rows * sizeof(float);
+  sz[LFM_MOE_WS_BLOCKCOUNTS] = nrb * kExperts * sizeof(int32_t);
+  sz[LFM_MOE_WS_OFFSETS] = (kExperts + 1) * sizeof(int32_t);
+  sz[LFM_MOE_WS_ROW2TOK] = rows * sizeof(int32_t);
+  sz[LFM_MOE_WS_SLOT2ROW] = rows * sizeof(int32_t);
+  sz[LFM_MOE_WS_H] = rows * kFF * sizeof(uint16_t);
+  sz[LFM_MOE_WS_Y] = rows * kHidden * sizeof(float);
+  sz[LFM_MOE_WS_X] = n * kHidden * sizeof(uint16_t);
+}
+
+size_t region_offset(int64_t N, int region) {
+  size_t sz[LFM_MOE_WS_REGIONS];
+  region_sizes(N, sz);
+  size_t off = 0;
+  for (int r = 0; r < region; ++r) off += align_up(sz[r]);
+  return off;
+}
+
+size_t workspace_bytes(int64_t N) { return region_offset(N, LFM_MOE_WS_REGIONS); }
+
+bool misaligned(const void* p, size_t a = 16) {
+  return (reinterpret_cast<uintptr_t>(p) % a) != 0;
+}
+
+struct Span {
+  const void* p;
+  size_t bytes;
+};
+
+bool overlap(Span a, Span b) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Checks shared by every layer entry point.  Returns OK, or the error.
+lfm_moe_status check_layer_args(const void* x, size_t x_bytes, const uint16_t* W_r,
+                                const float* bias, const uint16_t* W_gateup,
+                                const uint16_t* W_down, const void* out, size_t out_bytes,
+                                int64_t N, bool out_is_input) {
+  if (N < 0) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "N must be >= 0");
+  if (N > LFM_MOE_MAX_TOKENS) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "N exceeds LFM_MOE_MAX_TOKENS");
+  if (N == 0) return LFM_MOE_OK;
+  if (!x || !W_r || !bias || !W_gateup || !W_down || !out)
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if (misaligned(x) || misaligned(W_r) || misaligned(bias) || misaligned(W_gateup) ||
+      misaligned(W_down) || misaligned(out))
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  const Span o{out, out_bytes};
+  const Span ins[] = {{W_r, sizeof(uint16_t) * kExperts * kHidden},
+                      {bias, sizeof(float) * kExperts},
+                      {W_gateup, sizeof(uint16_t) * kExperts * 2 * kFF * kHidden},
+                      {W_down, sizeof(uint16_t) * kExperts * kHidden * kFF}};
+  for (const Span& s : ins)
+    if (overlap(o, s)) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "output overlaps a weight tensor");
+  if (!out_is_input && overlap(o, Span{x, x_bytes}))
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "output overlaps the input");
+  return LFM_MOE_OK;
+}
+
+lfm_moe_status check_ws(void* ws, size_t ws_bytes, int64_t N, Span out) {
+  if (!ws) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "null workspace");
+  if (misaligned(ws, kAlign)) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (ws_bytes < workspace_bytes(N))
+    return fail(LFM_MOE_ERR_WORKSPACE_TOO_SMALL,
+                "workspace of " + std::to_string(ws_bytes) + " bytes, need " +
+                    std::to_string(workspace_bytes(N)));
+  if (overlap(Span{ws, ws_bytes}, out)) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "workspace overlaps the output");
+  return LFM_MOE_OK;
+}
+
+// Library-owned workspace, one per device, grown on demand.
+constexpr int kMaxDevices = 64;
+std::mutex g_ws_mu;
+void* g_ws[kMaxDevices] = {};
+size_t g_ws_bytes[kMaxDevices] = {};
+
+lfm_moe_status internal_ws(int64_t N, void** ws, size_t* bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "device ordinal out of range");
+  const size_t need = workspace_bytes(N);
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  if (g_ws_bytes[dev] < need) {
+    if (g_ws[dev]) {
+      e = hipFree(g_ws[dev]);  // hipFree waits for work that may still use it
+      g_ws[dev] = nullptr;
+      g_ws_bytes[dev] = 0;
+      if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
+    }
+    e = hipMalloc(&g_ws[dev], need);
+    if (e != hipSuccess) {
+      g_ws[dev] = nullptr;
+      (void)hipGetLastError();
+      return fail(LFM_MOE_ERR_OUT_OF_MEMORY, "hipMalloc of " + std::to_string(need) + " workspace bytes failed");
+    }
+    g_ws_bytes[dev] = need;
+  }
+  *ws = g_ws[dev];
+  *bytes = g_ws_bytes[dev];
+  return LFM_MOE_OK;
+}
+
+// Per-kernel timing for measurements (lfm_moe_timing_*).
+constexpr int kStages = LFM_MOE_STAGES;
+constexpr int kMaxMarks = kStages + 1;
+constexpr size_t kMaxPending = 4096;
+
+struct TimedCall {
+  hipEvent_t ev[kMaxMarks];
+  int stage[kStages];
+  int n = 0;  // kernels recorded
+};
+
+struct TimingState {
+  std::mutex mu;
+  bool on = false;
+  std::vector<TimedCall> pending;
+  double total_ms[kStages] = {};
+  int64_t launches[kStages] = {};
+} g_timing;
+
+// Waits for and folds the pending records into the totals (mu held).
+hipError_t drain_pending() {
+  hipError_t first = hipSuccess;
+  for (TimedCall& c : g_timing.pending) {
+    hipError_t e = hipEventSynchronize(c.ev[c.n]);
+    for (int i = 0; i < c.n && e == hipSuccess; ++i) {
+      float ms = 0.f;
+      e = hipEventElapsedTime(&ms, c.ev[i], c.ev[i + 1]);
+      if (e == hipSuccess) {
+        g_timing.total_ms[c.stage[i]] += ms;
+        g_timing.launches[c.stage[i]] += 1;
+      }
+    }
+    if (e != hipSuccess && first == hipSuccess) first = e;
+    for (int i = 0; i <= c.n; ++i) (void)hipEventDestroy(c.ev[i]);
+  }
+  g_timing.pending.clear();
+  return first;
+}
+
+// Records an event before the first kernel of a call and after each kernel.
+class StageTimer {
+ public:
+  explicit StageTimer(hipStream_t s) : stream_(s) {
+    std::lock_guard<std::mutex> lock(g_timing.mu);
+    on_ = g_timing.on;
+    if (on_) on_ = record(0);
+  }
+  void after(int stage) {
+    if (!on_) return;
+    call_.stage[call_.n] = stage;
+    if (record(call_.n + 1)) ++call_.n;
+    else on_ = false;
+  }
+  ~StageTimer() {
+    if (!on_ || call_.n == 0) return;
+    std::lock_guard<std::mutex> lock(g_timing.mu);
+    if (g_timing.pending.size() >= kMaxPending) (void)drain_pending();
+    g_timing.pending.push_back(call_);
+  }
+
+ private:
+  bool record(int i) {
+    if (hipEventCreate(&call_.ev[i]) != hipSuccess) return false;
+    return hipEventRecord(call_.ev[i], stream_) == hipSuccess;
+  }
+  hipStream_t stream_;
+  bool on_ = false;
+  TimedCall call_;
+};
+
+template <typename T>
+T* region(void* ws, int64_t N, lfm_moe_ws_region r) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + region_offset(N, r));
+}
+
+int expert_tile_rows(int64_t N) { return N <= 16 ? 16 : 32; }
+
+// route -> dispatch -> gate/up -> down -> combine.  Arguments already checked.
+lfm_moe_status run_layer(const uint16_t* X, const uint16_t* W_r, const float* bias,
+                         const uint16_t* W_gateup, const uint16_t* W_down, const float* resid,
+                         float* out, int64_t N, void* ws, hipStream_t stream, StageTimer& timer) {
+  int32_t* idx = region<int32_t>(ws, N, LFM_MOE_WS_IDX);
+  float* w = region<float>(ws, N, LFM_MOE_WS_W);
+  int32_t* blockcounts = region<int32_t>(ws, N, LFM_MOE_WS_BLOCKCOUNTS);
+  int32_t* offsets = region<int32_t>(ws, N, LFM_MOE_WS_OFFSETS);
+  int32_t* row2tok = region<int32_t>(ws, N, LFM_MOE_WS_ROW2TOK);
+  int32_t* slot2row = region<int32_t>(ws, N, LFM_MOE_WS_SLOT2ROW);
+  uint16_t* H = region<uint16_t>(ws, N, LFM_MOE_WS_H);
+  float* Y = region<float>(ws, N, LFM_MOE_WS_Y);
+  const int n = static_cast<int>(N);
+  const int tile_rows = expert_tile_rows(N);
+  hipError_t e;
+  if ((e = launch_route(X, W_r, bias, idx, w, blockcounts, n, stream)) != hipSuccess)
+    return hip_fail(e, "route kernel launch");
+  timer.after(1);
+  if ((e = launch_dispatch(idx, blockcounts, route_block_tokens(N), offsets, row2tok, slot2row, n,
+                           stream)) != hipSuccess)
+    return hip_fail(e, "dispatch kernel launch");
+  timer.after(2);
+  if ((e = launch_gateup_stream(X, W_gateup, offsets, row2tok, H, N, tile_rows, stream)) != hipSuccess)
+    return hip_fail(e, "gate/up kernel launch");
+  timer.after(3);
+  if ((e = launch_down_stream(H, W_down, offsets, Y, N, tile_rows, stream)) != hipSuccess)
+    return hip_fail(e, "down kernel launch");
+  timer.after(4);
+  if ((e = launch_combine(Y, slot2row, w, resid, out, N, stream)) != hipSuccess)
+    return hip_fail(e, "combine kernel launch");
+  timer.after(5);
+  return LFM_MOE_OK;
+}
+
+size_t act_bytes(int64_t N, size_t elem) {
+  return static_cast<size_t>(N < 0 ? 0 : N) * kHidden * elem;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lfm_moe_abi_version(void) { return LFM_MOE_ABI_VERSION; }
+
+const char* lfm_moe_last_error(void) { return g_last_error.c_str(); }
+
+size_t lfm_moe_workspace_bytes(int64_t N) {
+  if (N < 0 || N > LFM_MOE_MAX_TOKENS) return 0;
+  return workspace_bytes(N);
+}
+
+size_t lfm_moe_workspace_offset(int64_t N, int region) {
+  if (N < 0 || N > LFM_MOE_MAX_TOKENS || region < 0 || region >= LFM_MOE_WS_REGIONS)
+    return static_cast<size_t>(-1);
+  return region_offset(N, region);
+}
+
+lfm_moe_status lfm_moe_rmsnorm(const float* x, uint16_t* X, int64_t N, hipStream_t stream) {
+  g_last_error.clear();
+  if (N < 0 || N > LFM_MOE_MAX_TOKENS) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "N out of range");
+  if (N == 0) return LFM_MOE_OK;
+  if (!x || !X) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if (misaligned(x) || misaligned(X)) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  if (overlap(Span{x, act_bytes(N, 4)}, Span{X, act_bytes(N, 2)}))
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "output overlaps the input");
+  hipError_t e = launch_rmsnorm(x, X, N, stream);
+  return e == hipSuccess ? LFM_MOE_OK : hip_fail(e, "rmsnorm kernel launch");
+}
+
+lfm_moe_status lfm_moe_route(const uint16_t* X, const uint16_t* W_r, const float* bias,
+                             int32_t* idx, float* w, int64_t N, hipStream_t stream) {
+  g_last_error.clear();
+  if (N < 0 || N > LFM_MOE_MAX_TOKENS) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "N out of range");
+  if (N == 0) return LFM_MOE_OK;
+  if (!X || !W_r || !bias || !idx || !w) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if (misaligned(X) || misaligned(W_r) || misaligned(bias) || misaligned(idx) || misaligned(w))
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  const size_t sel = static_cast<size_t>(N) * kTopK * 4;
+  if (overlap(Span{idx, sel}, Span{w, sel})) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "idx overlaps w");
+  hipError_t e = launch_route(X, W_r, bias, idx, w, nullptr, static_cast<int>(N), stream);
+  return e == hipSuccess ? LFM_MOE_OK : hip_fail(e, "route kernel launch");
+}
+
+lfm_moe_status lfm_moe_forward_ws(const uint16_t* X, const uint16_t* W_r, const float* bias,
+                                  const uint16_t* W_gateup, const uint16_t* W_down, float* out,
+                                  int64_t N, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  lfm_moe_status st = check_layer_args(X, act_bytes(N, 2), W_r, bias, W_gateup, W_down, out,
+                                       act_bytes(N, 4), N, false);
+  if (st != LFM_MOE_OK || N == 0) return st;
+  if ((st = check_ws(ws, ws_bytes, N, Span{out, act_bytes(N, 4)})) != LFM_MOE_OK) return st;
+  StageTimer timer(stream);
+  return run_layer(X, W_r, bias, W_gateup, W_down, nullptr, out, N, ws, stream, timer);
+}
+
+lfm_moe_status lfm_moe_forward(const uint16_t* X, const uint16_t* W_r, const float* bias,
+                               const uint16_t* W_gateup, const uint16_t* W_down, float* out,
+                               int64_t N, hipStream_t stream) {
+  g_last_error.clear();
+  lfm_moe_status st = check_layer_args(X, act_bytes(N, 2), W_r, bias, W_gateup, W_down, out,
+                                       act_bytes(N, 4), N, false);
+  if (st != LFM_MOE_OK || N == 0) return st;
+  void* ws = nullptr;
+  size_t bytes = 0;
+  if ((st = internal_ws(N, &ws, &bytes)) != LFM_MOE_OK) return st;
+  StageTimer timer(stream);
+  return run_layer(X, W_r, bias, W_gateup, W_down, nullptr, out, N, ws, stream, timer);
+}
+
+lfm_moe_status lfm_moe_block_forward_ws(float* x_inout, const uint16_t* W_r, const float* bias,
+                                        const uint16_t* W_gateup, const uint16_t* W_down,
+                                        int64_t N, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  lfm_moe_status st = check_layer_args(x_inout, act_bytes(N, 4), W_r, bias, W_gateup, W_down,
+                                       x_inout, act_bytes(N, 4), N, true);
+  if (st != LFM_MOE_OK || N == 0) return st;
+  if ((st = check_ws(ws, ws_bytes, N, Span{x_inout, act_bytes(N, 4)})) != LFM_MOE_OK) return st;
+  uint16_t* X = region<uint16_t>(ws, N, LFM_MOE_WS_X);
+  StageTimer timer(stream);
+  hipError_t e = launch_rmsnorm(x_inout, X, N, stream);
+  if (e != hipSuccess) return hip_fail(e, "rmsnorm kernel launch");
+  timer.after(0);
+  return run_layer(X, W_r, bias, W_gateup, W_down, x_inout, x_inout, N, ws, stream, timer);
+}
+
+lfm_moe_status lfm_moe_block_forward(float* x_inout, const uint16_t* W_r, const float* bias,
+                                     const uint16_t* W_gateup, const uint16_t* W_down, int64_t N,
+                                     hipStream_t stream) {
+  g_last_error.clear();
+  lfm_moe_status st = check_layer_args(x_inout, act_bytes(N, 4), W_r, bias, W_gateup, W_down,
+                                       x_inout, act_bytes(N, 4), N, true);
+  if (st != LFM_MOE_OK || N == 0) return st;
+  void* ws = nullptr;
+  size_t bytes = 0;
+  if ((st = internal_ws(N, &ws, &bytes)) != LFM_MOE_OK) return st;
+  return lfm_moe_block_forward_ws(x_inout, W_r, bias, W_gateup, W_down, N, ws, bytes, stream);
+}
+
+void lfm_moe_release(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  bool any = false;
+  for (int d = 0; d < kMaxDevices; ++d) any = any || g_ws[d] != nullptr;
+  if (!any) return;  // nothing to free: no HIP call at all
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return;
+  for (int d = 0; d < kMaxDevices; ++d) {
+    if (!g_ws[d]) continue;
+    if (hipSetDevice(d) == hipSuccess) (void)hipFree(g_ws[d]);
+    g_ws[d] = nullptr;
+    g_ws_bytes[d] = 0;
+  }
+  (void)hipSetDevice(cur);
+}
+
+lfm_moe_status lfm_moe_timing_enable(int on) {
+  g_last_error.clear();
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  hipError_t e = drain_pending();
+  g_timing.on = on != 0;
+  for (int i = 0; i < kStages; ++i) {
+    g_timing.total_ms[i] = 0.0;
+    g_timing.launches[i] = 0;
+  }
+  return e == hipSuccess ? LFM_MOE_OK : hip_fail(e, "timing events");
+}
+
+lfm_moe_status lfm_moe_timing_read(double* total_ms, int64_t* launches) {
+  g_last_error.clear();
+  if (!total_ms || !launches) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "null output pointer");
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  hipError_t e = drain_pending();
+  for (int i = 0; i < kStages; ++i) {
+    total_ms[i] = g_timing.total_ms[i];
+    launches[i] = g_timing.launches[i];
+  }
+  return e == hipSuccess ? LFM_MOE_OK : hip_fail(e, "timing events");
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// Shared device helpers for the gfx950 kernels of the MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lfm {
+
+constexpr int kHidden = 2048;   // d
+constexpr int kExperts = 64;    // E
+constexpr int kTopK = 4;        // k
+constexpr int kFF = 1536;       // expert intermediate width
+constexpr int kWave = 64;       // CDNA wavefront width
+constexpr float kRouterEps = 1e-6f;
+constexpr float kRmsEps = 1e-6f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// 16 bytes of bf16 values as loaded from memory.
+struct alignas(16) Pack8 {
+  uint4 u;
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// Widening a bf16 bit pattern to fp32 is exact.
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN stays NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// D = A * B + C on a 16x16 tile with K = 32 (bf16 in, fp32 accumulate).
+// Lane l supplies row (l % 16) of A and column (l % 16) of B, eight K
+// elements each; the accumulator of lane l holds column (l % 16), rows
+// 4 * (l / 16) + r for r = 0..3.
+__device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu(float g) {
+  return g / (1.0f + __expf(-g));
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    int o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Maps a linear m-tile id to (expert, first row) given the expert row
+// offsets: expert e owns ceil(count_e / tile_rows) consecutive m-tiles.
+// Returns false when the id is past the last tile.  Every lane of the wave
+// must call it (it uses cross-lane operations).
+struct MTile {
+  int expert;
+  int row_begin;  // first grouped row of the tile
+  int rows;       // valid rows in the tile (<= tile_rows)
+};
+
+__device__ __forceinline__ bool map_mtile(const int* __restrict__ offsets, int mt, int tile_rows,
+                                          MTile& t) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int beg = offsets[lane];
+  const int cnt = offsets[lane + 1] - beg;
+  const int nt = (cnt + tile_rows - 1) / tile_rows;
+  const int incl = wave_inclusive_scan(nt, lane);
+  const int total = __shfl(incl, kWave - 1, kWave);
+  if (mt >= total) return false;
+  const unsigned long long ball = __ballot(incl > mt);
+  const int e = __ffsll(static_cast<long long>(ball)) - 1;
+  const int excl_e = __shfl(incl - nt, e, kWave);
+  const int beg_e = __shfl(beg, e, kWave);
+  const int cnt_e = __shfl(cnt, e, kWave);
+  const int m0 = (mt - excl_e) * tile_rows;
+  t.expert = e;
+  t.row_begin = beg_e + m0;
+  t.rows = min(tile_rows, cnt_e - m0);
+  return true;
+}
+
+}  // namespace lfm

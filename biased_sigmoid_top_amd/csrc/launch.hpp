@@ -1,0 +1,35 @@
+// Host-side launchers of the device kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lfm {
+
+// Tokens per router workgroup for N tokens (16 or 64); the per-block
+// histogram has ceil(N / route_block_tokens(N)) rows.
+int route_block_tokens(int64_t N);
+
+// Upper bound of the number of m-tiles of tile_rows rows over all experts.
+int64_t max_mtiles(int64_t N, int tile_rows);
+
+hipError_t launch_rmsnorm(const float* x, uint16_t* X, int64_t N, hipStream_t stream);
+
+hipError_t launch_route(const uint16_t* X, const uint16_t* Wr, const float* bias, int32_t* idx,
+                        float* w, int32_t* blockcounts, int N, hipStream_t stream);
+
+hipError_t launch_dispatch(const int32_t* idx, const int32_t* blockcounts, int route_tokens,
+                           int32_t* offsets, int32_t* row2tok, int32_t* slot2row, int N,
+                           hipStream_t stream);
+
+hipError_t launch_gateup_stream(const uint16_t* X, const uint16_t* Wgu, const int32_t* offsets,
+                                const int32_t* row2tok, uint16_t* H, int64_t N, int tile_rows,
+                                hipStream_t stream);
+
+hipError_t launch_down_stream(const uint16_t* H, const uint16_t* Wd, const int32_t* offsets,
+                              float* Y, int64_t N, int tile_rows, hipStream_t stream);
+
+hipError_t launch_combine(const float* Y, const int32_t* slot2row, const float* w,
+                          const float* resid, float* out, int64_t N, hipStream_t stream);
+
+}  // namespace lfm

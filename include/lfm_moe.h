@@ -1,0 +1,183 @@
+/*
+ * lfm_moe.h -- C ABI of the biased-sigmoid top-4 sparse feed-forward (MoE)
+ * layer of LFM2.5-24B-A2B on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one defined in the flozi.net guide "LFM2.5-24B-A2B:
+ * Biased Routing, Short Convolutions and Ten KV Caches" (English edition),
+ * section "The router has two different scores":
+ *
+ *   l_t   = W_r x_t                        64 router logits per token
+ *   s_t   = sigmoid(l_t)                   applied to each logit on its own
+ *   c_t   = s_t + bias                     stored bias, selection only
+ *   S_t   = the 4 experts with largest c_t (ties: lower expert id first)
+ *   w_tj  = s_t[S_tj] / (sum_j' s_t[S_tj'] + 1e-6) * 1.0   (routed scale 1)
+ *   y_e(x)= W_down_e (silu(W_gate_e x) * (W_up_e x))       2048->1536->2048
+ *   out_t = sum_j w_tj y_{S_tj}(x_t)       tokens grouped by expert, weighted
+ *                                          outputs accumulated (section
+ *                                          "What to verify in a deployment")
+ *
+ * Fixed shapes: d = 2048, E = 64 experts, top-k = 4, ff = 1536.
+ *
+ * Conventions for every entry point:
+ *  - Tensor arguments are DEVICE pointers to contiguous row-major arrays,
+ *    16-byte aligned.  bf16 arguments are raw bfloat16 bit patterns
+ *    (uint16_t).  Weights are stored [out_features, in_features].
+ *  - Ownership: the caller owns every tensor argument; the library never
+ *    frees or keeps them.  Work is enqueued asynchronously on `stream`, so
+ *    the caller keeps them alive until the stream has passed this call.
+ *  - Synchrony: no host synchronisation and no device-to-host copy happens
+ *    inside a call.  LFM_MOE_OK means "enqueued"; a fault inside a kernel
+ *    surfaces at the caller's next synchronisation.
+ *  - Errors: return codes only, nothing aborts.  Argument checks run before
+ *    any HIP call.  N == 0 returns LFM_MOE_OK and launches nothing.
+ *    lfm_moe_last_error() gives a thread-local message for the last failure.
+ *  - Determinism: bitwise reproducible for fixed inputs, N and build (no
+ *    floating-point atomics; fixed reduction and combine orders).
+ */
+#ifndef LFM_MOE_H
+#define LFM_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LFM_MOE_ABI_VERSION 1
+#define LFM_MOE_HIDDEN 2048
+#define LFM_MOE_EXPERTS 64
+#define LFM_MOE_TOPK 4
+#define LFM_MOE_FF 1536
+/* Largest N accepted: grouped rows (4N) and their element offsets stay in range. */
+#define LFM_MOE_MAX_TOKENS (1LL << 24)
+
+typedef enum {
+  LFM_MOE_OK = 0,
+  LFM_MOE_ERR_INVALID_ARGUMENT = 1, /* NULL with N > 0, N < 0, N too large, misaligned */
+  LFM_MOE_ERR_WORKSPACE_TOO_SMALL = 2,
+  LFM_MOE_ERR_OUT_OF_MEMORY = 3,    /* the internal workspace could not grow */
+  LFM_MOE_ERR_HIP = 4               /* a HIP runtime or launch error */
+} lfm_moe_status;
+
+/* Returns LFM_MOE_ABI_VERSION of the built library. */
+int lfm_moe_abi_version(void);
+
+/* Message of the last failed call on this thread ("" if none).  Valid until
+ * the next call on the same thread. */
+const char* lfm_moe_last_error(void);
+
+/*
+ * RMS normalisation of the residual stream, the step before the
+ * feed-forward network (guide, section "The exact checkpoint"):
+ *   X[t, :] = bf16( x[t, :] / sqrt(mean(x[t, :]^2) + 1e-6) )   (unit weight)
+ * x: [N, 2048] fp32 (read).  X: [N, 2048] bf16 (written).  Sums in fp32,
+ * in a fixed order; rounding to bf16 is round-to-nearest-even.
+ */
+lfm_moe_status lfm_moe_rmsnorm(const float* x, uint16_t* X, int64_t N, hipStream_t stream);
+
+/*
+ * Router (guide, section "The router has two different scores"): logits
+ * X W_r^T in fp32 (bf16 inputs, fp32 accumulation), sigmoid per logit in
+ * fp32, biased top-4 selection, unbiased weights normalised by sum + 1e-6.
+ *   X:    [N, 2048] bf16, the normalised hidden states (read)
+ *   W_r:  [64, 2048] bf16 router matrix (read)
+ *   bias: [64] fp32 stored expert bias (read; used for selection only)
+ *   idx:  [N, 4] int32 (written): selected experts by descending selection
+ *         score s + bias, equal scores ordered by lower expert id
+ *   w:    [N, 4] fp32 (written): w[t, j] = s[idx[t, j]] / (sum_j s + 1e-6)
+ */
+lfm_moe_status lfm_moe_route(const uint16_t* X, const uint16_t* W_r, const float* bias,
+                             int32_t* idx, float* w, int64_t N, hipStream_t stream);
+
+/*
+ * The whole layer: out[N, 2048] fp32 = sum_j w[t, j] * y_{idx[t, j]}(X[t]).
+ *   X:        [N, 2048] bf16 normalised hidden states (read)
+ *   W_r:      [64, 2048] bf16, bias: [64] fp32 (read), as for lfm_moe_route
+ *   W_gateup: [64, 3072, 2048] bf16 (read): per expert, rows 0..1535 are
+ *             W_gate and rows 1536..3071 are W_up (the guide allows the two
+ *             input matrices to be packed; packing does not change the
+ *             function)
+ *   W_down:   [64, 2048, 1536] bf16 (read)
+ *   out:      [N, 2048] fp32 (written; must not overlap any input)
+ * Expert hidden activations are rounded to bf16 before the down
+ * projection; every accumulation is fp32.  Uses a workspace that the
+ * library owns (one per device, grown on demand with hipMalloc and kept
+ * until lfm_moe_release()); calls that overlap in time on one device must
+ * use lfm_moe_forward_ws with separate workspaces instead.
+ */
+lfm_moe_status lfm_moe_forward(const uint16_t* X, const uint16_t* W_r, const float* bias,
+                               const uint16_t* W_gateup, const uint16_t* W_down,
+                               float* out, int64_t N, hipStream_t stream);
+
+/* Bytes of workspace lfm_moe_forward_ws / lfm_moe_block_forward_ws need for N tokens. */
+size_t lfm_moe_workspace_bytes(int64_t N);
+
+/* Regions of the workspace, for inspection of the intermediate steps. */
+typedef enum {
+  LFM_MOE_WS_IDX = 0,       /* [N, 4] int32 selected experts */
+  LFM_MOE_WS_W = 1,         /* [N, 4] fp32 mixture weights */
+  LFM_MOE_WS_BLOCKCOUNTS = 2, /* [ceil(N / route block), 64] int32 per-block histogram */
+  LFM_MOE_WS_OFFSETS = 3,   /* [65] int32: offsets[e] = first grouped row of expert e, offsets[64] = 4N */
+  LFM_MOE_WS_ROW2TOK = 4,   /* [4N] int32 grouped row -> token */
+  LFM_MOE_WS_SLOT2ROW = 5,  /* [N, 4] int32 slot (t, j) -> grouped row */
+  LFM_MOE_WS_H = 6,         /* [4N, 1536] bf16 expert hidden rows, grouped order */
+  LFM_MOE_WS_Y = 7,         /* [4N, 2048] fp32 expert output rows, grouped order */
+  LFM_MOE_WS_X = 8,         /* [N, 2048] bf16 normalised input (block forward only) */
+  LFM_MOE_WS_REGIONS = 9
+} lfm_moe_ws_region;
+
+/* Byte offset of `region` inside a workspace sized for N tokens; (size_t)-1 if invalid. */
+size_t lfm_moe_workspace_offset(int64_t N, int region);
+
+/*
+ * lfm_moe_forward with a caller-owned workspace `ws` of `ws_bytes` bytes
+ * (device memory, 256-byte aligned, at least lfm_moe_workspace_bytes(N)).
+ * The workspace holds the intermediate results listed in lfm_moe_ws_region
+ * after the call completes.  Concurrent calls need distinct workspaces.
+ */
+lfm_moe_status lfm_moe_forward_ws(const uint16_t* X, const uint16_t* W_r, const float* bias,
+                                  const uint16_t* W_gateup, const uint16_t* W_down,
+                                  float* out, int64_t N, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
+/*
+ * One block's feed-forward half (guide, section "The exact checkpoint":
+ * normalise, feed-forward network, residual):
+ *   x_inout[t] <- x_inout[t] + MoE(bf16(RMSNorm(x_inout[t])))
+ * x_inout: [N, 2048] fp32 residual stream (read and written in place);
+ * other arguments as for lfm_moe_forward.  The _ws form takes a caller
+ * workspace of lfm_moe_workspace_bytes(N) bytes.
+ */
+lfm_moe_status lfm_moe_block_forward(float* x_inout, const uint16_t* W_r, const float* bias,
+                                     const uint16_t* W_gateup, const uint16_t* W_down,
+                                     int64_t N, hipStream_t stream);
+lfm_moe_status lfm_moe_block_forward_ws(float* x_inout, const uint16_t* W_r, const float* bias,
+                                        const uint16_t* W_gateup, const uint16_t* W_down,
+                                        int64_t N, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Frees the library-owned workspaces (call with no work of this library in flight). */
+void lfm_moe_release(void);
+
+/*
+ * Measurement support: device time per kernel of the layer.  While timing
+ * is on, every layer call records a hipEvent on its stream before its first
+ * kernel and after each kernel; lfm_moe_timing_read() waits for those
+ * events and returns, per stage, the summed milliseconds between
+ * consecutive events and the number of launches.  Stages: 0 rmsnorm,
+ * 1 route, 2 dispatch, 3 gate/up, 4 down, 5 combine.  Turning timing on
+ * clears the totals.  The events cost a little host time per call; leave
+ * timing off outside measurements.  Not meant for concurrent use from
+ * several threads.
+ */
+#define LFM_MOE_STAGES 6
+lfm_moe_status lfm_moe_timing_enable(int on);
+lfm_moe_status lfm_moe_timing_read(double* total_ms /* [LFM_MOE_STAGES] */,
+                                   int64_t* launches /* [LFM_MOE_STAGES] */);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LFM_MOE_H */

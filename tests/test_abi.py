@@ -1,0 +1,106 @@
+"""The C ABI library loads, exports what include/lfm_moe.h declares, and
+rejects bad arguments before any HIP call (so these run without a GPU)."""
+
+import ctypes
+import re
+
+import pytest
+
+from biased_sigmoid_top_amd import _lib
+
+FAKE = 1 << 40  # aligned host-side stand-in addresses: never dereferenced here
+
+
+def _addr(i):
+    return FAKE + i * (1 << 34)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_every_declared_function_is_exported(lib):
+    names = _lib.declared_functions()
+    assert len(names) == len(_lib.SIGNATURES)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_abi_version_matches_header(lib):
+    with open(_lib.HEADER) as f:
+        v = int(re.search(r"#define LFM_MOE_ABI_VERSION (\d+)", f.read()).group(1))
+    assert lib.lfm_moe_abi_version() == v
+
+
+def test_workspace_layout(lib):
+    for N in [1, 16, 17, 64, 255, 4096, 16384]:
+        total = lib.lfm_moe_workspace_bytes(N)
+        offs = [lib.lfm_moe_workspace_offset(N, r) for r in range(9)]
+        assert offs[0] == 0
+        assert all(o % 256 == 0 for o in offs)
+        assert offs == sorted(offs) and offs[-1] < total
+        # H and Y regions hold 4N rows.
+        assert offs[_lib.WS_Y] - offs[_lib.WS_H] >= 4 * N * 1536 * 2
+        assert offs[_lib.WS_X] - offs[_lib.WS_Y] >= 4 * N * 2048 * 4
+        assert total - offs[_lib.WS_X] >= N * 2048 * 2
+    assert lib.lfm_moe_workspace_bytes(-1) == 0
+    assert lib.lfm_moe_workspace_offset(10, 99) == ctypes.c_size_t(-1).value
+
+
+def _fwd(lib, X, Wr, b, Wgu, Wd, out, N):
+    return lib.lfm_moe_forward(X, Wr, b, Wgu, Wd, out, N, None)
+
+
+def test_forward_argument_checks(lib):
+    a = [_addr(i) for i in range(6)]
+    assert _fwd(lib, *a, 0) == _lib.OK  # N == 0: nothing launched
+    assert _fwd(lib, *a, -1) == _lib.ERR_INVALID_ARGUMENT
+    assert _fwd(lib, *a, (1 << 24) + 1) == _lib.ERR_INVALID_ARGUMENT
+    for i in range(6):
+        b = list(a)
+        b[i] = None
+        assert _fwd(lib, *b, 8) == _lib.ERR_INVALID_ARGUMENT
+        assert b"null" in lib.lfm_moe_last_error()
+        b = list(a)
+        b[i] = a[i] + 4
+        assert _fwd(lib, *b, 8) == _lib.ERR_INVALID_ARGUMENT
+        assert b"aligned" in lib.lfm_moe_last_error()
+    # Output overlapping an input.
+    b = list(a)
+    b[5] = a[0] + 1024
+    assert _fwd(lib, *b, 8) == _lib.ERR_INVALID_ARGUMENT
+    b = list(a)
+    b[5] = a[3] + 4096
+    assert _fwd(lib, *b, 8) == _lib.ERR_INVALID_ARGUMENT
+
+
+def test_forward_ws_checks(lib):
+    a = [_addr(i) for i in range(6)]
+    need = lib.lfm_moe_workspace_bytes(100)
+    ws = _addr(7)
+    f = lib.lfm_moe_forward_ws
+    assert f(*a, 100, ws, need - 1, None) == _lib.ERR_WORKSPACE_TOO_SMALL
+    assert f(*a, 100, None, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert f(*a, 100, ws + 16, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert f(*a, 100, a[5], need, None) == _lib.ERR_INVALID_ARGUMENT  # overlaps out
+    assert f(*a, 0, None, 0, None) == _lib.OK
+
+
+def test_route_rmsnorm_block_checks(lib):
+    a = [_addr(i) for i in range(5)]
+    assert lib.lfm_moe_route(*a, 0, None) == _lib.OK
+    assert lib.lfm_moe_route(*a, -3, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.lfm_moe_route(a[0], None, a[2], a[3], a[4], 4, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.lfm_moe_route(a[0], a[1], a[2], a[3], a[3] + 16, 4, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.lfm_moe_rmsnorm(a[0], a[1], 0, None) == _lib.OK
+    assert lib.lfm_moe_rmsnorm(a[0], a[0] + 64, 4, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.lfm_moe_rmsnorm(None, a[1], 4, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.lfm_moe_block_forward(a[0], a[1], a[2], a[3], a[4], 0, None) == _lib.OK
+    assert lib.lfm_moe_block_forward(a[0], a[1], a[2], a[3], None, 4, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.lfm_moe_block_forward_ws(a[0], a[1], a[2], a[3], a[4], 4, None, 0, None) == _lib.ERR_INVALID_ARGUMENT
+
+
+def test_release_without_allocation_is_a_no_op(lib):
+    lib.lfm_moe_release()
