@@ -75,8 +75,8 @@ def prepare(name, copies):
     dev = torch.device("cuda")
     X = moe.rmsnorm(layer["z"].to(dev))          # input preparation, not timed
     W_r, bias = layer["W_r"].to(dev), layer["bias"].to(dev)
-    Wgu0 = synth.pack_gateup(layer["W_gate"], layer["W_up"]).to(dev)
-    Wd0 = layer["W_down"].contiguous().to(dev)
+    Wgu0 = moe.pack_gateup(layer["W_gate"].to(dev), layer["W_up"].to(dev))
+    Wd0 = moe.pack_down(layer["W_down"].contiguous().to(dev))
     Wgu = [Wgu0] + [Wgu0.clone() for _ in range(copies - 1)]
     Wd = [Wd0] + [Wd0.clone() for _ in range(copies - 1)]
     out = torch.empty(N, D, dtype=torch.float32, device=dev)

@@ -32,6 +32,8 @@ SIGNATURES = {
     "lfm_moe_last_error": (ctypes.c_char_p, []),
     "lfm_moe_rmsnorm": (ctypes.c_int, [_P, _P, _I64, _P]),
     "lfm_moe_route": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _P]),
+    "lfm_moe_pack_gateup": (ctypes.c_int, [_P, _P, _P, _P]),
+    "lfm_moe_pack_down": (ctypes.c_int, [_P, _P, _P]),
     "lfm_moe_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _P]),
     "lfm_moe_workspace_bytes": (_SZ, [_I64]),
     "lfm_moe_workspace_offset": (_SZ, [_I64, ctypes.c_int]),

@@ -35,8 +35,29 @@ def _req(t: torch.Tensor, name: str, dtype, shape) -> int:
 def _weights(W_r, bias, W_gateup, W_down):
     return (_req(W_r, "W_r", torch.bfloat16, (EXPERTS, HIDDEN)),
             _req(bias, "bias", torch.float32, (EXPERTS,)),
-            _req(W_gateup, "W_gateup", torch.bfloat16, (EXPERTS, 2 * FF, HIDDEN)),
-            _req(W_down, "W_down", torch.bfloat16, (EXPERTS, HIDDEN, FF)))
+            _req(W_gateup, "W_gateup (packed)", torch.bfloat16, (EXPERTS * 2 * FF * HIDDEN,)),
+            _req(W_down, "W_down (packed)", torch.bfloat16, (EXPERTS * HIDDEN * FF,)))
+
+
+def pack_gateup(W_gate, W_up, out=None, stream=None):
+    """Packs [64, 1536, 2048] gate and up matrices into the fragment layout."""
+    pg = _req(W_gate, "W_gate", torch.bfloat16, (EXPERTS, FF, HIDDEN))
+    pu = _req(W_up, "W_up", torch.bfloat16, (EXPERTS, FF, HIDDEN))
+    if out is None:
+        out = torch.empty(EXPERTS * 2 * FF * HIDDEN, dtype=torch.bfloat16, device=W_gate.device)
+    po = _req(out, "W_gateup", torch.bfloat16, (EXPERTS * 2 * FF * HIDDEN,))
+    _lib.call("lfm_moe_pack_gateup", pg, pu, po, _stream(stream))
+    return out
+
+
+def pack_down(W_down, out=None, stream=None):
+    """Packs the [64, 2048, 1536] down matrices into the fragment layout."""
+    pd = _req(W_down, "W_down", torch.bfloat16, (EXPERTS, HIDDEN, FF))
+    if out is None:
+        out = torch.empty(EXPERTS * HIDDEN * FF, dtype=torch.bfloat16, device=W_down.device)
+    po = _req(out, "W_down_packed", torch.bfloat16, (EXPERTS * HIDDEN * FF,))
+    _lib.call("lfm_moe_pack_down", pd, po, _stream(stream))
+    return out
 
 
 def abi_version() -> int:

@@ -283,6 +283,33 @@ lfm_moe_status lfm_moe_rmsnorm(const float* x, uint16_t* X, int64_t N, hipStream
   return e == hipSuccess ? LFM_MOE_OK : hip_fail(e, "rmsnorm kernel launch");
 }
 
+lfm_moe_status lfm_moe_pack_gateup(const uint16_t* W_gate, const uint16_t* W_up,
+                                   uint16_t* W_gateup, hipStream_t stream) {
+  g_last_error.clear();
+  if (!W_gate || !W_up || !W_gateup) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if (misaligned(W_gate) || misaligned(W_up) || misaligned(W_gateup))
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  const size_t half = sizeof(uint16_t) * kExperts * kFF * kHidden;
+  const Span o{W_gateup, 2 * half};
+  if (overlap(o, Span{W_gate, half}) || overlap(o, Span{W_up, half}))
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "output overlaps an input");
+  hipError_t e = launch_pack_gateup(W_gate, W_up, W_gateup, stream);
+  return e == hipSuccess ? LFM_MOE_OK : hip_fail(e, "pack kernel launch");
+}
+
+lfm_moe_status lfm_moe_pack_down(const uint16_t* W_down, uint16_t* W_down_packed,
+                                 hipStream_t stream) {
+  g_last_error.clear();
+  if (!W_down || !W_down_packed) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if (misaligned(W_down) || misaligned(W_down_packed))
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  const size_t bytes = sizeof(uint16_t) * kExperts * kHidden * kFF;
+  if (overlap(Span{W_down, bytes}, Span{W_down_packed, bytes}))
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "output overlaps the input");
+  hipError_t e = launch_pack_down(W_down, W_down_packed, stream);
+  return e == hipSuccess ? LFM_MOE_OK : hip_fail(e, "pack kernel launch");
+}
+
 lfm_moe_status lfm_moe_route(const uint16_t* X, const uint16_t* W_r, const float* bias,
                              int32_t* idx, float* w, int64_t N, hipStream_t stream) {
   g_last_error.clear();

@@ -6,17 +6,14 @@
 //   H = silu(X_e W_gate_e^T) * (X_e W_up_e^T)    (bf16 out, fp32 accumulate)
 //   Y = H_e W_down_e^T                           (fp32 out)
 //
-// With a handful of tokens per expert the work is bound by streaming each
-// active expert's weights from HBM exactly once.  Weights therefore go
-// straight from global memory into MFMA operand registers (no LDS), each
-// weight row is read by exactly one wavefront, the loads for the next
-// 128-wide K step are issued before the MFMAs of the current one, and the
-// token rows (few, shared by every workgroup of the expert) come through
-// the caches.  The weight rows are the MFMA A operand (16 rows) and the
-// tokens the B operand (16 columns); the K dimension inside a 128-wide step
-// is visited in an order that lets every lane read 16 contiguous bytes per
-// load (the same order on both operands, so the dot products are
-// unchanged).
+// With a handful of tokens per expert the work is bound by reading each
+// active expert's weights from HBM once.  Weights are in the packed
+// fragment layout (pack.hip), so each wavefront load is one contiguous 1 KB
+// non-temporal read that lands directly in the MFMA A-operand registers;
+// every weight fragment is read by exactly one wavefront.  The token rows
+// (B operand: few rows, shared by all workgroups of an expert) come through
+// the caches.  Loads for the next K step are issued before the MFMAs of the
+// current one.
 //
 // Workgroups walk a linear (m-tile, column block) grid; the m-tile list is
 // derived on the device from the expert row offsets, and workgroups past
@@ -29,16 +26,17 @@ namespace lfm {
 namespace {
 
 constexpr int kStreamThreads = 256;
-constexpr int kGateUpCols = 64;                    // H columns per workgroup (16 per wave)
-constexpr int kGateUpBlocks = kFF / kGateUpCols;   // 24
-constexpr int kDownRowsPerWave = 32;               // output features per wave
-constexpr int kDownCols = 4 * kDownRowsPerWave;    // 128 per workgroup
-constexpr int kDownBlocks = kHidden / kDownCols;   // 16
+constexpr int kFrag = 512;                         // bf16 elements per 16x32 fragment
+constexpr int kGateUpBlocks = kFF / 64;            // 24: 4 waves x 16 H columns
+constexpr int kDownBlocks = kHidden / 128;         // 16: 4 waves x 32 features
+constexpr int kStepFrags = 2;                      // K fragments (of 32) per pipeline step
 
-// Loads the 16-byte pieces a lane needs for one 128-wide K step of a row.
-__device__ __forceinline__ void load_step(const uint16_t* row, int kb, int g, uint4 (&v)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = ld16(row + kb + (4 * i + g) * 8);
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming read: used once, so marked non-temporal.
+__device__ __forceinline__ uint4 ld_stream(const uint16_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 template <int TT>
@@ -46,6 +44,7 @@ __global__ __launch_bounds__(kStreamThreads) void gateup_stream_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wgu,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ row2tok,
     uint16_t* __restrict__ H) {
+  constexpr int kSteps = (kHidden / 32) / kStepFrags;
   const int nb = blockIdx.x % kGateUpBlocks;
   const int mt = blockIdx.x / kGateUpBlocks;
   MTile tile;
@@ -55,52 +54,66 @@ __global__ __launch_bounds__(kStreamThreads) void gateup_stream_kernel(
   const int wave = threadIdx.x / kWave;
   const int r16 = lane & 15;
   const int g = lane >> 4;
-  const int n = nb * kGateUpCols + wave * 16;  // first H column of this wave
+  const int hb = nb * 4 + wave;  // 16-column block of H
+  const int ntt = __builtin_amdgcn_readfirstlane((tile.rows + 15) / 16);
 
-  const uint16_t* wg = Wgu + (static_cast<size_t>(tile.expert) * 2 * kFF + n + r16) * kHidden;
-  const uint16_t* wu = wg + static_cast<size_t>(kFF) * kHidden;
+  const uint16_t* wg =
+      Wgu + (static_cast<size_t>(tile.expert) * (kFF / 16) + hb) * 2 * (kHidden / 32) * kFrag +
+      lane * 8;
+  const uint16_t* wu = wg + (kHidden / 32) * kFrag;
   const uint16_t* xr[TT];
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) {
     const int r = tt * 16 + r16;
     const int tok = row2tok[tile.row_begin + (r < tile.rows ? r : 0)];
-    xr[tt] = X + static_cast<size_t>(tok) * kHidden;
+    xr[tt] = X + static_cast<size_t>(tok) * kHidden + g * 8;
   }
 
   f32x4 accg[TT], accu[TT];
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) { accg[tt] = f32x4{0, 0, 0, 0}; accu[tt] = accg[tt]; }
 
-  uint4 cg[4], cu[4], cx[TT][4];
-  load_step(wg, 0, g, cg);
-  load_step(wu, 0, g, cu);
+  uint4 cg[kStepFrags], cu[kStepFrags], cx[TT][kStepFrags];
+  auto load = [&](int s, uint4 (&ag)[kStepFrags], uint4 (&au)[kStepFrags],
+                  uint4 (&bx)[TT][kStepFrags]) {
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt) load_step(xr[tt], 0, g, cx[tt]);
+    for (int f = 0; f < kStepFrags; ++f) {
+      const int kf = s * kStepFrags + f;
+      ag[f] = ld_stream(wg + kf * kFrag);
+      au[f] = ld_stream(wu + kf * kFrag);
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+        bx[tt][f] = (tt == 0 || tt < ntt) ? ld16(xr[tt] + kf * 32) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto compute = [&](const uint4 (&ag)[kStepFrags], const uint4 (&au)[kStepFrags],
+                     const uint4 (&bx)[TT][kStepFrags]) {
+#pragma unroll
+    for (int f = 0; f < kStepFrags; ++f)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+        if (tt == 0 || tt < ntt) {
+          accg[tt] = mfma16(ag[f], bx[tt][f], accg[tt]);
+          accu[tt] = mfma16(au[f], bx[tt][f], accu[tt]);
+        }
+  };
 
-  for (int kb = 0; kb < kHidden; kb += 128) {
-    uint4 ng[4], nu[4], nx[TT][4];
-    const int kn = kb + 128 < kHidden ? kb + 128 : kb;  // last step reloads (cached) data
-    load_step(wg, kn, g, ng);
-    load_step(wu, kn, g, nu);
+  load(0, cg, cu, cx);
+  for (int s = 0; s < kSteps - 1; ++s) {
+    uint4 ng[kStepFrags], nu[kStepFrags], nx[TT][kStepFrags];
+    load(s + 1, ng, nu, nx);
+    compute(cg, cu, cx);
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) load_step(xr[tt], kn, g, nx[tt]);
+    for (int f = 0; f < kStepFrags; ++f) {
+      cg[f] = ng[f];
+      cu[f] = nu[f];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        accg[tt] = mfma16(cg[i], cx[tt][i], accg[tt]);
-        accu[tt] = mfma16(cu[i], cx[tt][i], accu[tt]);
-      }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      cg[i] = ng[i];
-      cu[i] = nu[i];
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) cx[tt][i] = nx[tt][i];
+      for (int tt = 0; tt < TT; ++tt) cx[tt][f] = nx[tt][f];
     }
   }
+  compute(cg, cu, cx);
 
-  // Lane holds token (tt*16 + r16) and H columns n + 4g + r, r = 0..3.
+  // Lane holds token (tt*16 + r16) and H columns hb*16 + 4g + r, r = 0..3.
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) {
     const int r = tt * 16 + r16;
@@ -112,7 +125,7 @@ __global__ __launch_bounds__(kStreamThreads) void gateup_stream_kernel(
         const float h1 = silu(accg[tt][2 * q + 1]) * accu[tt][2 * q + 1];
         p[q] = static_cast<uint32_t>(f32_to_bf16(h0)) | (static_cast<uint32_t>(f32_to_bf16(h1)) << 16);
       }
-      uint16_t* dst = H + static_cast<size_t>(tile.row_begin + r) * kFF + n + 4 * g;
+      uint16_t* dst = H + static_cast<size_t>(tile.row_begin + r) * kFF + hb * 16 + 4 * g;
       *reinterpret_cast<uint2*>(dst) = make_uint2(p[0], p[1]);
     }
   }
@@ -122,6 +135,7 @@ template <int TT>
 __global__ __launch_bounds__(kStreamThreads) void down_stream_kernel(
     const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wd,
     const int32_t* __restrict__ offsets, float* __restrict__ Y) {
+  constexpr int kSteps = (kFF / 32) / kStepFrags;
   const int nb = blockIdx.x % kDownBlocks;
   const int mt = blockIdx.x / kDownBlocks;
   MTile tile;
@@ -131,17 +145,19 @@ __global__ __launch_bounds__(kStreamThreads) void down_stream_kernel(
   const int wave = threadIdx.x / kWave;
   const int r16 = lane & 15;
   const int g = lane >> 4;
-  const int f0 = nb * kDownCols + wave * kDownRowsPerWave;  // first output feature
+  const int rt0 = nb * 8 + wave * 2;  // two 16-row tiles of output features
+  const int ntt = __builtin_amdgcn_readfirstlane((tile.rows + 15) / 16);
 
   const uint16_t* wr[2];
 #pragma unroll
   for (int ft = 0; ft < 2; ++ft)
-    wr[ft] = Wd + (static_cast<size_t>(tile.expert) * kHidden + f0 + ft * 16 + r16) * kFF;
+    wr[ft] = Wd + (static_cast<size_t>(tile.expert) * (kHidden / 16) + rt0 + ft) * (kFF / 32) * kFrag +
+             lane * 8;
   const uint16_t* hr[TT];
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) {
     const int r = tt * 16 + r16;
-    hr[tt] = H + static_cast<size_t>(tile.row_begin + (r < tile.rows ? r : 0)) * kFF;
+    hr[tt] = H + static_cast<size_t>(tile.row_begin + (r < tile.rows ? r : 0)) * kFF + g * 8;
   }
 
   f32x4 acc[2][TT];
@@ -150,40 +166,49 @@ __global__ __launch_bounds__(kStreamThreads) void down_stream_kernel(
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) acc[ft][tt] = f32x4{0, 0, 0, 0};
 
-  uint4 cw[2][4], ch[TT][4];
+  uint4 cw[2][kStepFrags], ch[TT][kStepFrags];
+  auto load = [&](int s, uint4 (&aw)[2][kStepFrags], uint4 (&bh)[TT][kStepFrags]) {
 #pragma unroll
-  for (int ft = 0; ft < 2; ++ft) load_step(wr[ft], 0, g, cw[ft]);
+    for (int f = 0; f < kStepFrags; ++f) {
+      const int kf = s * kStepFrags + f;
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt) load_step(hr[tt], 0, g, ch[tt]);
-
-  for (int kb = 0; kb < kFF; kb += 128) {
-    uint4 nw[2][4], nh[TT][4];
-    const int kn = kb + 128 < kFF ? kb + 128 : kb;
+      for (int ft = 0; ft < 2; ++ft) aw[ft][f] = ld_stream(wr[ft] + kf * kFrag);
 #pragma unroll
-    for (int ft = 0; ft < 2; ++ft) load_step(wr[ft], kn, g, nw[ft]);
+      for (int tt = 0; tt < TT; ++tt)
+        bh[tt][f] = (tt == 0 || tt < ntt) ? ld16(hr[tt] + kf * 32) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto compute = [&](const uint4 (&aw)[2][kStepFrags], const uint4 (&bh)[TT][kStepFrags]) {
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) load_step(hr[tt], kn, g, nh[tt]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int f = 0; f < kStepFrags; ++f)
 #pragma unroll
       for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt) acc[ft][tt] = mfma16(cw[ft][i], ch[tt][i], acc[ft][tt]);
+        for (int tt = 0; tt < TT; ++tt)
+          if (tt == 0 || tt < ntt) acc[ft][tt] = mfma16(aw[ft][f], bh[tt][f], acc[ft][tt]);
+  };
+
+  load(0, cw, ch);
+  for (int s = 0; s < kSteps - 1; ++s) {
+    uint4 nw[2][kStepFrags], nh[TT][kStepFrags];
+    load(s + 1, nw, nh);
+    compute(cw, ch);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int f = 0; f < kStepFrags; ++f) {
 #pragma unroll
-      for (int ft = 0; ft < 2; ++ft) cw[ft][i] = nw[ft][i];
+      for (int ft = 0; ft < 2; ++ft) cw[ft][f] = nw[ft][f];
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) ch[tt][i] = nh[tt][i];
+      for (int tt = 0; tt < TT; ++tt) ch[tt][f] = nh[tt][f];
     }
   }
+  compute(cw, ch);
 
-  // Lane holds token (tt*16 + r16) and features f0 + ft*16 + 4g + r.
+  // Lane holds token (tt*16 + r16) and features (rt0 + ft)*16 + 4g + r.
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) {
     const int r = tt * 16 + r16;
     if (r < tile.rows) {
-      float* dst = Y + static_cast<size_t>(tile.row_begin + r) * kHidden + f0 + 4 * g;
+      float* dst = Y + static_cast<size_t>(tile.row_begin + r) * kHidden + rt0 * 16 + 4 * g;
 #pragma unroll
       for (int ft = 0; ft < 2; ++ft)
         *reinterpret_cast<float4*>(dst + ft * 16) =

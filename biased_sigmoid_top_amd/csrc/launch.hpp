@@ -13,6 +13,10 @@ int route_block_tokens(int64_t N);
 // Upper bound of the number of m-tiles of tile_rows rows over all experts.
 int64_t max_mtiles(int64_t N, int tile_rows);
 
+hipError_t launch_pack_gateup(const uint16_t* Wg, const uint16_t* Wu, uint16_t* out,
+                              hipStream_t stream);
+hipError_t launch_pack_down(const uint16_t* Wd, uint16_t* out, hipStream_t stream);
+
 hipError_t launch_rmsnorm(const float* x, uint16_t* X, int64_t N, hipStream_t stream);
 
 hipError_t launch_route(const uint16_t* X, const uint16_t* Wr, const float* bias, int32_t* idx,

@@ -92,14 +92,37 @@ lfm_moe_status lfm_moe_route(const uint16_t* X, const uint16_t* W_r, const float
                              int32_t* idx, float* w, int64_t N, hipStream_t stream);
 
 /*
+ * Expert weight packing (guide, section "The router has two different
+ * scores": the runtime representation may pack the two input matrices of
+ * an expert together; packing does not change the function).
+ *
+ * The packed layout is made of 1 KB fragments of 16 rows x 32 columns of
+ * one matrix; bytes [16 l, 16 l + 16) of a fragment hold row (l % 16),
+ * columns 8 (l / 16) .. 8 (l / 16) + 7 -- the order in which the 64 lanes
+ * of a wavefront hold a 16x16x32 MFMA operand.
+ *
+ * lfm_moe_pack_gateup: W_gate, W_up [64, 1536, 2048] bf16 row-major (read)
+ *   -> W_gateup [64 * 3072 * 2048] bf16 (written): fragment
+ *   ((e * 96 + hb) * 2 + p) * 64 + kf holds rows hb*16 .. hb*16+15 of
+ *   W_gate (p = 0) or W_up (p = 1) of expert e, columns kf*32 .. kf*32+31.
+ * lfm_moe_pack_down: W_down [64, 2048, 1536] bf16 row-major (read)
+ *   -> W_down_packed [64 * 2048 * 1536] bf16 (written): fragment
+ *   (e * 128 + rt) * 48 + kf holds rows rt*16 .. rt*16+15 of W_down of
+ *   expert e, columns kf*32 .. kf*32+31.
+ * Outputs must not overlap the inputs.  A pure permutation: bit exact.
+ */
+lfm_moe_status lfm_moe_pack_gateup(const uint16_t* W_gate, const uint16_t* W_up,
+                                   uint16_t* W_gateup, hipStream_t stream);
+lfm_moe_status lfm_moe_pack_down(const uint16_t* W_down, uint16_t* W_down_packed,
+                                 hipStream_t stream);
+
+/*
  * The whole layer: out[N, 2048] fp32 = sum_j w[t, j] * y_{idx[t, j]}(X[t]).
  *   X:        [N, 2048] bf16 normalised hidden states (read)
  *   W_r:      [64, 2048] bf16, bias: [64] fp32 (read), as for lfm_moe_route
- *   W_gateup: [64, 3072, 2048] bf16 (read): per expert, rows 0..1535 are
- *             W_gate and rows 1536..3071 are W_up (the guide allows the two
- *             input matrices to be packed; packing does not change the
- *             function)
- *   W_down:   [64, 2048, 1536] bf16 (read)
+ *   W_gateup: packed gate/up weights of all 64 experts, as written by
+ *             lfm_moe_pack_gateup (read)
+ *   W_down:   packed down weights, as written by lfm_moe_pack_down (read)
  *   out:      [N, 2048] fp32 (written; must not overlap any input)
  * Expert hidden activations are rounded to bf16 before the down
  * projection; every accumulation is fp32.  Uses a workspace that the

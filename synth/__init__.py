@@ -87,11 +87,6 @@ def layer_params(seed: int, N_skip: int = 0, skew: bool = False, d: int = HIDDEN
     return dict(W_r=W_r, bias=bias, W_gate=W_gate, W_up=W_up, W_down=W_down)
 
 
-def pack_gateup(W_gate: torch.Tensor, W_up: torch.Tensor) -> torch.Tensor:
-    """[E, 2*ff, d]: rows 0..ff-1 are the gate matrix, rows ff..2ff-1 the up matrix."""
-    return torch.cat([W_gate, W_up], dim=1).contiguous()
-
-
 def layer_inputs(N: int, seed: int, skew: bool = False, d: int = HIDDEN,
                  E: int = EXPERTS, ff: int = FF) -> dict:
     """z plus all parameters of one single-layer workload."""

@@ -30,16 +30,24 @@ def oracle_inputs(layer: dict) -> dict:
     )
 
 
+def device_weights(layer: dict, device="cuda") -> dict:
+    """Router, bias and packed expert weights on the device (packed by the library)."""
+    import biased_sigmoid_top_amd as moe
+    Wg, Wu = layer["W_gate"].to(device), layer["W_up"].to(device)
+    W_gateup = moe.pack_gateup(Wg, Wu)
+    del Wg, Wu
+    Wd = layer["W_down"].contiguous().to(device)
+    W_down = moe.pack_down(Wd)
+    del Wd
+    return dict(W_r=layer["W_r"].to(device), bias=layer["bias"].to(device),
+                W_gateup=W_gateup, W_down=W_down)
+
+
 def device_inputs(layer: dict, X: np.ndarray, device="cuda") -> dict:
     """Device tensors for the HIP path; X is the oracle's bf16-valued input."""
-    from synth import pack_gateup
-    return dict(
-        X=torch.from_numpy(X).to(torch.bfloat16).to(device),
-        W_r=layer["W_r"].to(device),
-        bias=layer["bias"].to(device),
-        W_gateup=pack_gateup(layer["W_gate"], layer["W_up"]).to(device),
-        W_down=layer["W_down"].contiguous().to(device),
-    )
+    d = device_weights(layer, device)
+    d["X"] = torch.from_numpy(X).to(torch.bfloat16).to(device)
+    return d
 
 
 def check_route(idx_gpu: np.ndarray, w_gpu: np.ndarray, r: oracle.Routing, tokens=None):

@@ -102,5 +102,14 @@ def test_route_rmsnorm_block_checks(lib):
     assert lib.lfm_moe_block_forward_ws(a[0], a[1], a[2], a[3], a[4], 4, None, 0, None) == _lib.ERR_INVALID_ARGUMENT
 
 
+def test_pack_checks(lib):
+    a = [_addr(i) for i in range(3)]
+    assert lib.lfm_moe_pack_gateup(a[0], None, a[2], None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.lfm_moe_pack_gateup(a[0], a[1], a[0] + 256, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.lfm_moe_pack_gateup(a[0] + 2, a[1], a[2], None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.lfm_moe_pack_down(a[0], a[0], None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.lfm_moe_pack_down(None, a[1], None) == _lib.ERR_INVALID_ARGUMENT
+
+
 def test_release_without_allocation_is_a_no_op(lib):
     lib.lfm_moe_release()

@@ -13,7 +13,7 @@ import oracle
 import synth
 from conftest import cached_layer
 from parity import (check_grouping_valid, check_out, check_route, device_inputs,
-                    expected_outputs, oracle_inputs)
+                    device_weights, expected_outputs, oracle_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -52,6 +52,23 @@ def _np(t):
 
 
 ALL = list(synth.WORKLOADS)
+
+
+def test_weight_packing_is_the_documented_permutation(moe):
+    """Packed fragment layout: fragment ((e*96 + hb)*2 + p)*64 + kf, lane
+    l = 16 g + r holds row hb*16 + r, columns kf*32 + 8 g .. + 7 (gate p = 0,
+    up p = 1); down: fragment (e*128 + rt)*48 + kf likewise."""
+    w = synth.WORKLOADS["tiny_n32"]
+    layer = cached_layer(w["N"], w["seed"], w["skew"])
+    Wg, Wu, Wd = layer["W_gate"], layer["W_up"], layer["W_down"]
+    _step("pack gate/up and down")
+    got_gu = moe.pack_gateup(Wg.cuda(), Wu.cuda()).cpu()
+    got_d = moe.pack_down(Wd.cuda()).cpu()
+    frag = lambda W, R, K: W.view(64, R // 16, 16, K // 32, 4, 8).permute(0, 1, 3, 4, 2, 5)
+    ref_gu = torch.stack([frag(Wg, 1536, 2048), frag(Wu, 1536, 2048)], dim=2).reshape(-1)
+    ref_d = frag(Wd, 2048, 1536).reshape(-1)
+    assert torch.equal(got_gu.view(torch.int16), ref_gu.contiguous().view(torch.int16))
+    assert torch.equal(got_d.view(torch.int16), ref_d.contiguous().view(torch.int16))
 
 
 @pytest.mark.parametrize("name", ["tiny_n32", "prefill_n4096"])
@@ -241,9 +258,7 @@ def _stack_block(l):
         inp = dict(W_r=p["W_r"].float().numpy(), bias=p["bias"].numpy(),
                    W_gate=p["W_gate"].float().numpy(), W_up=p["W_up"].float().numpy(),
                    W_down=p["W_down"].float().numpy())
-        dev = dict(W_r=p["W_r"].cuda(), bias=p["bias"].cuda(),
-                   W_gateup=synth.pack_gateup(p["W_gate"], p["W_up"]).cuda(),
-                   W_down=p["W_down"].cuda())
+        dev = device_weights(p)
         _STACK[l] = (inp, dev)
     return _STACK[l]
 
