@@ -84,8 +84,8 @@ def prepare(name, copies):
     from biased_sigmoid_top_amd import _lib
     ws = moe.alloc_workspace(N)
     moe.forward(X, W_r, bias, Wgu0, Wd0, out, workspace=ws)
-    offs = moe.workspace_view(ws, N, _lib.WS_OFFSETS, torch.int32, (65,)).cpu()
-    counts = (offs[1:] - offs[:-1]).tolist()
+    sel = moe.workspace_view(ws, N, _lib.WS_IDX, torch.int32, (N, 4)).cpu().long()
+    counts = torch.bincount(sel.reshape(-1), minlength=E).tolist()
     del ws
     torch.cuda.synchronize()
     return dict(name=name, N=N, seed=w["seed"], layer=layer, X=X, W_r=W_r, bias=bias,
@@ -193,6 +193,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the oracle baseline (0 leaves it out)")
     ap.add_argument("--copy-probe", action="store_true", help="only run a plain 1 GiB copy")
+    ap.add_argument("--workload", default="decode_n64", help="headline workload")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -210,8 +211,8 @@ def main():
 
     import biased_sigmoid_top_amd  # noqa: F401  (fails loudly without the built library)
 
-    head = prepare("decode_n64", args.copies)
-    log(f"timing decode_n64: {args.steps} steps after {args.warmup} warm-up")
+    head = prepare(args.workload, args.copies)
+    log(f"timing {args.workload}: {args.steps} steps after {args.warmup} warm-up")
     wall_ms, per_kernel = time_steps(head, args.steps, args.warmup)
     h = summarize(head, wall_ms, per_kernel)
     log(json.dumps(h))
@@ -241,7 +242,7 @@ def main():
         metric=METRIC, value=h["tokens_per_s"], unit="tokens/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=h["ms_per_step"], higher_is_better=True, scaling="weak",
         vs_baseline=None, dtype="bf16", data="synthetic",
-        config=dict(workload="decode_n64", N=N, d=D, experts=E, top_k=K, ff=FF, seed=head["seed"],
+        config=dict(workload=args.workload, N=N, d=D, experts=E, top_k=K, ff=FF, seed=head["seed"],
                     active_experts=A, max_tokens_per_expert=h["max_tokens_per_expert"],
                     weight_copies=args.copies),
         layer=dict(gbs=h["layer_gbs"], hbm_frac=h["layer_hbm_frac"], tflops=h["layer_tflops"],

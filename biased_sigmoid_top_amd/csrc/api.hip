@@ -4,7 +4,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/lfm_moe.h"
+#include "lfm_moe.h"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -37,11 +37,11 @@ void region_sizes(int64_t N, size_t (&sz)[LFM_MOE_WS_REGIONS]) {
   sz[LFM_MOE_WS_W] = rows * sizeof(float);
   sz[LFM_MOE_WS_BLOCKCOUNTS] = nrb * kExperts * sizeof(int32_t);
   sz[LFM_MOE_WS_OFFSETS] = (kExperts + 1) * sizeof(int32_t);
-  sz[LFM_MOE_WS_ROW2TOK] = rows * sizeof(int32_t);
-  sz[LFM_MOE_WS_SLOT2ROW] = rows * sizeof(int32_t);
+  sz[LFM_MOE_WS_ROW2SLOT] = rows * sizeof(int32_t);
   sz[LFM_MOE_WS_H] = rows * kFF * sizeof(uint16_t);
   sz[LFM_MOE_WS_Y] = rows * kHidden * sizeof(float);
   sz[LFM_MOE_WS_X] = n * kHidden * sizeof(uint16_t);
+  sz[LFM_MOE_WS_ROUTER_PARTIAL] = route_partial_bytes(N);
 }
 
 size_t region_offset(int64_t N, int region) {
@@ -212,9 +212,11 @@ T* region(void* ws, int64_t N, lfm_moe_ws_region r) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + region_offset(N, r));
 }
 
-int expert_tile_rows(int64_t N) { return N <= 16 ? 16 : 32; }
+// Decode-shaped batches take the expert-major streaming kernels, which
+// group their own tokens; larger batches go through the dispatch step.
+bool use_decode_path(int64_t N) { return N <= kDecodeMaxTokens; }
 
-// route -> dispatch -> gate/up -> down -> combine.  Arguments already checked.
+// route -> [dispatch] -> gate/up -> down -> combine.  Arguments already checked.
 lfm_moe_status run_layer(const uint16_t* X, const uint16_t* W_r, const float* bias,
                          const uint16_t* W_gateup, const uint16_t* W_down, const float* resid,
                          float* out, int64_t N, void* ws, hipStream_t stream, StageTimer& timer) {
@@ -222,27 +224,35 @@ lfm_moe_status run_layer(const uint16_t* X, const uint16_t* W_r, const float* bi
   float* w = region<float>(ws, N, LFM_MOE_WS_W);
   int32_t* blockcounts = region<int32_t>(ws, N, LFM_MOE_WS_BLOCKCOUNTS);
   int32_t* offsets = region<int32_t>(ws, N, LFM_MOE_WS_OFFSETS);
-  int32_t* row2tok = region<int32_t>(ws, N, LFM_MOE_WS_ROW2TOK);
-  int32_t* slot2row = region<int32_t>(ws, N, LFM_MOE_WS_SLOT2ROW);
+  int32_t* row2slot = region<int32_t>(ws, N, LFM_MOE_WS_ROW2SLOT);
   uint16_t* H = region<uint16_t>(ws, N, LFM_MOE_WS_H);
   float* Y = region<float>(ws, N, LFM_MOE_WS_Y);
+  float* part = region<float>(ws, N, LFM_MOE_WS_ROUTER_PARTIAL);
   const int n = static_cast<int>(N);
-  const int tile_rows = expert_tile_rows(N);
+  const bool decode = use_decode_path(N);
   hipError_t e;
-  if ((e = launch_route(X, W_r, bias, idx, w, blockcounts, n, stream)) != hipSuccess)
+  if ((e = launch_route(X, W_r, bias, idx, w, decode ? nullptr : blockcounts, part, n, stream)) != hipSuccess)
     return hip_fail(e, "route kernel launch");
   timer.after(1);
-  if ((e = launch_dispatch(idx, blockcounts, route_block_tokens(N), offsets, row2tok, slot2row, n,
-                           stream)) != hipSuccess)
-    return hip_fail(e, "dispatch kernel launch");
-  timer.after(2);
-  if ((e = launch_gateup_stream(X, W_gateup, offsets, row2tok, H, N, tile_rows, stream)) != hipSuccess)
-    return hip_fail(e, "gate/up kernel launch");
-  timer.after(3);
-  if ((e = launch_down_stream(H, W_down, offsets, Y, N, tile_rows, stream)) != hipSuccess)
-    return hip_fail(e, "down kernel launch");
-  timer.after(4);
-  if ((e = launch_combine(Y, slot2row, w, resid, out, N, stream)) != hipSuccess)
+  if (decode) {
+    if ((e = launch_gateup_decode(X, W_gateup, idx, H, n, stream)) != hipSuccess)
+      return hip_fail(e, "gate/up kernel launch");
+    timer.after(3);
+    if ((e = launch_down_decode(H, W_down, idx, Y, n, stream)) != hipSuccess)
+      return hip_fail(e, "down kernel launch");
+    timer.after(4);
+  } else {
+    if ((e = launch_dispatch(idx, blockcounts, offsets, row2slot, n, stream)) != hipSuccess)
+      return hip_fail(e, "dispatch kernel launch");
+    timer.after(2);
+    if ((e = launch_gateup_tiled(X, W_gateup, offsets, row2slot, H, N, stream)) != hipSuccess)
+      return hip_fail(e, "gate/up kernel launch");
+    timer.after(3);
+    if ((e = launch_down_tiled(H, W_down, offsets, row2slot, Y, N, stream)) != hipSuccess)
+      return hip_fail(e, "down kernel launch");
+    timer.after(4);
+  }
+  if ((e = launch_combine(Y, w, resid, out, N, stream)) != hipSuccess)
     return hip_fail(e, "combine kernel launch");
   timer.after(5);
   return LFM_MOE_OK;
@@ -320,7 +330,13 @@ lfm_moe_status lfm_moe_route(const uint16_t* X, const uint16_t* W_r, const float
     return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
   const size_t sel = static_cast<size_t>(N) * kTopK * 4;
   if (overlap(Span{idx, sel}, Span{w, sel})) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "idx overlaps w");
-  hipError_t e = launch_route(X, W_r, bias, idx, w, nullptr, static_cast<int>(N), stream);
+  void* ws = nullptr;
+  size_t bytes = 0;
+  lfm_moe_status st = internal_ws(N, &ws, &bytes);
+  if (st != LFM_MOE_OK) return st;
+  hipError_t e = launch_route(X, W_r, bias, idx, w, nullptr,
+                              region<float>(ws, N, LFM_MOE_WS_ROUTER_PARTIAL), static_cast<int>(N),
+                              stream);
   return e == hipSuccess ? LFM_MOE_OK : hip_fail(e, "route kernel launch");
 }
 

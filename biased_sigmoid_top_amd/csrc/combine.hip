@@ -8,9 +8,9 @@
 //  - section "The exact checkpoint": RMS normalisation before the
 //    feed-forward network and a residual add after it.
 //
-// The combine gathers the four expert rows of a token in slot order j =
-// 0..3 and accumulates in fp32 (no atomics), so the result is the same on
-// every run.
+// The combine reads the four expert rows of a token (stored in slot order)
+// and accumulates them in the fixed order j = 0..3 in fp32 (no atomics), so
+// the result is the same on every run.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -20,17 +20,17 @@ namespace {
 
 constexpr int kRowThreads = 256;  // one token row of 2048 values per workgroup
 
-// out[t] = (resid[t] +) sum_j w[t, j] * Y[slot2row[t, j]]; resid may alias out.
-__global__ __launch_bounds__(kRowThreads) void combine_kernel(
-    const float* __restrict__ Y, const int32_t* __restrict__ slot2row,
-    const float* __restrict__ w, const float* resid, float* out) {
+// out[t] = (resid[t] +) sum_j w[t, j] * Y[t*4 + j]; resid may alias out.
+// Y rows are in slot order, so a token's four rows are contiguous.
+__global__ __launch_bounds__(kRowThreads) void combine_kernel(const float* __restrict__ Y,
+                                                              const float* __restrict__ w,
+                                                              const float* resid, float* out) {
   const size_t t = blockIdx.x;
-  const int4 rows = *reinterpret_cast<const int4*>(slot2row + t * kTopK);
   const float4 wt = *reinterpret_cast<const float4*>(w + t * kTopK);
-  const float* y0 = Y + static_cast<size_t>(rows.x) * kHidden;
-  const float* y1 = Y + static_cast<size_t>(rows.y) * kHidden;
-  const float* y2 = Y + static_cast<size_t>(rows.z) * kHidden;
-  const float* y3 = Y + static_cast<size_t>(rows.w) * kHidden;
+  const float* y0 = Y + t * kTopK * kHidden;
+  const float* y1 = y0 + kHidden;
+  const float* y2 = y1 + kHidden;
+  const float* y3 = y2 + kHidden;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int col = (h * kRowThreads + threadIdx.x) * 4;
@@ -90,10 +90,9 @@ __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const float* __res
 
 }  // namespace
 
-hipError_t launch_combine(const float* Y, const int32_t* slot2row, const float* w,
-                          const float* resid, float* out, int64_t N, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(N), dim3(kRowThreads), 0, stream, Y, slot2row, w, resid,
-                     out);
+hipError_t launch_combine(const float* Y, const float* w, const float* resid, float* out,
+                          int64_t N, hipStream_t stream) {
+  hipLaunchKernelGGL(combine_kernel, dim3(N), dim3(kRowThreads), 0, stream, Y, w, resid, out);
   return hipGetLastError();
 }
 

@@ -13,6 +13,9 @@ constexpr int kFF = 1536;       // expert intermediate width
 constexpr int kWave = 64;       // CDNA wavefront width
 constexpr float kRouterEps = 1e-6f;
 constexpr float kRmsEps = 1e-6f;
+// Largest N taken by the expert-major decode path (its per-expert slot list
+// lives in LDS).
+constexpr int kDecodeMaxTokens = 512;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -19,21 +19,36 @@ hipError_t launch_pack_down(const uint16_t* Wd, uint16_t* out, hipStream_t strea
 
 hipError_t launch_rmsnorm(const float* x, uint16_t* X, int64_t N, hipStream_t stream);
 
+// Scratch bytes of the router's partial logits for N tokens.
+size_t route_partial_bytes(int64_t N);
 hipError_t launch_route(const uint16_t* X, const uint16_t* Wr, const float* bias, int32_t* idx,
-                        float* w, int32_t* blockcounts, int N, hipStream_t stream);
+                        float* w, int32_t* blockcounts, float* part, int N, hipStream_t stream);
 
-hipError_t launch_dispatch(const int32_t* idx, const int32_t* blockcounts, int route_tokens,
-                           int32_t* offsets, int32_t* row2tok, int32_t* slot2row, int N,
-                           hipStream_t stream);
+hipError_t launch_dispatch(const int32_t* idx, const int32_t* blockcounts, int32_t* offsets,
+                           int32_t* row2slot, int N, hipStream_t stream);
 
-hipError_t launch_gateup_stream(const uint16_t* X, const uint16_t* Wgu, const int32_t* offsets,
-                                const int32_t* row2tok, uint16_t* H, int64_t N, int tile_rows,
-                                hipStream_t stream);
+// Decode path: expert-major grids that group their own tokens (N <= kDecodeMaxTokens).
+hipError_t launch_gateup_decode(const uint16_t* X, const uint16_t* Wgu, const int32_t* idx,
+                                uint16_t* H, int N, hipStream_t stream);
+hipError_t launch_down_decode(const uint16_t* H, const uint16_t* Wd, const int32_t* idx,
+                              float* Y, int N, hipStream_t stream);
 
-hipError_t launch_down_stream(const uint16_t* H, const uint16_t* Wd, const int32_t* offsets,
-                              float* Y, int64_t N, int tile_rows, hipStream_t stream);
+// Grouped path over the dispatch step's expert-grouped rows.
+hipError_t launch_gateup_grouped_stream(const uint16_t* X, const uint16_t* Wgu,
+                                        const int32_t* offsets, const int32_t* row2slot,
+                                        uint16_t* H, int64_t N, hipStream_t stream);
+hipError_t launch_down_grouped_stream(const uint16_t* H, const uint16_t* Wd,
+                                      const int32_t* offsets, const int32_t* row2slot, float* Y,
+                                      int64_t N, hipStream_t stream);
 
-hipError_t launch_combine(const float* Y, const int32_t* slot2row, const float* w,
-                          const float* resid, float* out, int64_t N, hipStream_t stream);
+// Grouped path, LDS-tiled MFMA kernels (prefill-shaped batches).
+hipError_t launch_gateup_tiled(const uint16_t* X, const uint16_t* Wgu, const int32_t* offsets,
+                               const int32_t* row2slot, uint16_t* H, int64_t N,
+                               hipStream_t stream);
+hipError_t launch_down_tiled(const uint16_t* H, const uint16_t* Wd, const int32_t* offsets,
+                             const int32_t* row2slot, float* Y, int64_t N, hipStream_t stream);
+
+hipError_t launch_combine(const float* Y, const float* w, const float* resid, float* out,
+                          int64_t N, hipStream_t stream);
 
 }  // namespace lfm

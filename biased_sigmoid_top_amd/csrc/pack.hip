@@ -10,11 +10,14 @@
 // 8 (l / 16) .. 8 (l / 16) + 7.  A wavefront then loads one operand with a
 // single contiguous 1 KB read.
 //
-//   gate/up: fragment ((e * 96 + hb) * 2 + p) * 64 + kf holds rows
-//            hb*16 .. hb*16+15 of W_gate (p = 0) or W_up (p = 1) of expert
-//            e, columns kf*32 .. kf*32+31.
-//   down:    fragment (e * 128 + rt) * 48 + kf holds rows rt*16 .. rt*16+15
-//            of W_down of expert e, columns kf*32 .. kf*32+31.
+// Fragments are ordered so that, for one 32-wide K step, everything a
+// workgroup of the expert kernels needs is one contiguous 8 KB run:
+//   gate/up: fragment ((e * 24 + nb) * 64 + kf) * 8 + cb * 2 + p holds rows
+//            nb*64 + cb*16 .. +15 of W_gate (p = 0) or W_up (p = 1) of
+//            expert e, columns kf*32 .. kf*32+31   (nb < 24, cb < 4).
+//   down:    fragment ((e * 16 + rb) * 48 + kf) * 8 + rt holds rows
+//            rb*128 + rt*16 .. +15 of W_down of expert e, columns
+//            kf*32 .. kf*32+31                     (rb < 16, rt < 8).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -30,13 +33,14 @@ __global__ __launch_bounds__(kPackThreads) void pack_gateup_kernel(
   const size_t piece = static_cast<size_t>(blockIdx.x) * kPackThreads + threadIdx.x;
   const int lane = static_cast<int>(piece % kWave);
   const size_t frag = piece / kWave;
-  const int kf = static_cast<int>(frag % (kHidden / 32));
-  const size_t t = frag / (kHidden / 32);
-  const int p = static_cast<int>(t % 2);
-  const size_t ehb = t / 2;  // e * 96 + hb
-  const size_t e = ehb / (kFF / 16);
-  const int hb = static_cast<int>(ehb % (kFF / 16));
-  const int row = hb * 16 + (lane % 16);
+  const int q = static_cast<int>(frag % 8);  // cb * 2 + p
+  const size_t t = frag / 8;
+  const int kf = static_cast<int>(t % (kHidden / 32));
+  const size_t enb = t / (kHidden / 32);     // e * 24 + nb
+  const size_t e = enb / (kFF / 64);
+  const int nb = static_cast<int>(enb % (kFF / 64));
+  const int cb = q / 2, p = q % 2;
+  const int row = nb * 64 + cb * 16 + (lane % 16);
   const int col = kf * 32 + (lane / 16) * 8;
   const uint16_t* src = (p == 0 ? Wg : Wu) + (e * kFF + row) * static_cast<size_t>(kHidden) + col;
   *reinterpret_cast<uint4*>(out + piece * 8) = ld16(src);
@@ -47,11 +51,13 @@ __global__ __launch_bounds__(kPackThreads) void pack_down_kernel(const uint16_t*
   const size_t piece = static_cast<size_t>(blockIdx.x) * kPackThreads + threadIdx.x;
   const int lane = static_cast<int>(piece % kWave);
   const size_t frag = piece / kWave;
-  const int kf = static_cast<int>(frag % (kFF / 32));
-  const size_t ert = frag / (kFF / 32);  // e * 128 + rt
-  const size_t e = ert / (kHidden / 16);
-  const int rt = static_cast<int>(ert % (kHidden / 16));
-  const int row = rt * 16 + (lane % 16);
+  const int rt = static_cast<int>(frag % 8);
+  const size_t t = frag / 8;
+  const int kf = static_cast<int>(t % (kFF / 32));
+  const size_t erb = t / (kFF / 32);         // e * 16 + rb
+  const size_t e = erb / (kHidden / 128);
+  const int rb = static_cast<int>(erb % (kHidden / 128));
+  const int row = rb * 128 + rt * 16 + (lane % 16);
   const int col = kf * 32 + (lane / 16) * 8;
   const uint16_t* src = Wd + (e * kHidden + row) * static_cast<size_t>(kFF) + col;
   *reinterpret_cast<uint4*>(out + piece * 8) = ld16(src);

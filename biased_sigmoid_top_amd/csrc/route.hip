@@ -8,6 +8,14 @@
 // scores" -- sigmoid on each logit, the stored bias added after the
 // activation takes part in the selection only, weights from the unbiased
 // scores, normalised with an epsilon, routed scale 1.
+//
+// Two kernels.  route_partial: one wavefront per (16-token tile, 128-wide K
+// slice) multiplies the 16 token rows by all 64 router rows over its slice
+// and stores the 16 x 64 fp32 partial tile; with N = 64 that is 64
+// wavefronts on 64 CUs, so the router matrix is pulled through many CUs at
+// once (one CU alone reads it too slowly).  route_select: one wavefront per
+// token adds the 16 partials of each logit in a fixed order, applies the
+// sigmoid and the bias, takes the top 4 and normalises the weights.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -15,8 +23,9 @@ namespace lfm {
 
 namespace {
 
-constexpr int kRouteThreads = 512;  // 8 wavefronts
-constexpr int kRouteWaves = kRouteThreads / kWave;
+constexpr int kRouteTokens = 16;
+constexpr int kSlices = kHidden / 128;              // 16 K slices
+constexpr int kSelectThreads = kRouteTokens * kWave;  // one wavefront per token
 
 // Orders floats like their values as unsigned integers.
 __device__ __forceinline__ uint32_t orderable(float f) {
@@ -24,108 +33,103 @@ __device__ __forceinline__ uint32_t orderable(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// One workgroup routes TM tokens.  Wave w multiplies token tile
-// (w % (TM/16)) against all 64 router rows over K range number
-// (w / (TM/16)); the K partials are summed in LDS in a fixed order.
-template <int TM>
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wr,
-    const float* __restrict__ bias, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
-    int32_t* __restrict__ blockcounts, int N) {
-  constexpr int kTileT = TM / 16;            // token tiles per workgroup
-  constexpr int kSplits = kRouteWaves / kTileT;
-  constexpr int kChunk = kHidden / kSplits;  // K elements per wave
-  static_assert(kChunk % 128 == 0, "K chunk must be a multiple of 128");
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) {
+    const uint32_t o = __shfl_xor(v, off, kWave);
+    v = o > v ? o : v;
+  }
+  return v;
+}
 
-  __shared__ float part[kSplits][TM][kExperts + 1];
-  __shared__ int wave_counts[kRouteWaves][kExperts];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int tt = wave % kTileT;
-  const int ks = wave / kTileT;
-  const int t0 = blockIdx.x * TM;
-
-  // ---- logits: 16 tokens x 64 experts per wave over its K chunk ----
+// part layout: [token tile][slice][16 tokens][64 experts] fp32.
+__global__ __launch_bounds__(kWave) void route_partial_kernel(const uint16_t* __restrict__ X,
+                                                              const uint16_t* __restrict__ Wr,
+                                                              float* __restrict__ part, int N) {
+  const int lane = threadIdx.x;
+  const int tile = blockIdx.x / kSlices;
+  const int slice = blockIdx.x % kSlices;
   const int r16 = lane & 15;
   const int g = lane >> 4;
-  int tok = t0 + tt * 16 + r16;
+  int tok = tile * kRouteTokens + r16;
   tok = tok < N ? tok : N - 1;  // rows past N are computed and discarded
-  const uint16_t* xrow = X + static_cast<size_t>(tok) * kHidden;
-  f32x4 acc[4] = {};
-  for (int kb = ks * kChunk; kb < (ks + 1) * kChunk; kb += 128) {
-    uint4 a[4], b[4][4];
+  const int kb = slice * 128;
+  const uint16_t* xrow = X + static_cast<size_t>(tok) * kHidden + kb;
+  uint4 a[4], b[4][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = ld16(xrow + kb + (4 * i + g) * 8);
+  for (int i = 0; i < 4; ++i) a[i] = ld16(xrow + (4 * i + g) * 8);
 #pragma unroll
-    for (int et = 0; et < 4; ++et) {
-      const uint16_t* wrow = Wr + static_cast<size_t>(et * 16 + r16) * kHidden + kb;
+  for (int et = 0; et < 4; ++et) {
+    const uint16_t* wrow = Wr + static_cast<size_t>(et * 16 + r16) * kHidden + kb;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) b[et][i] = ld16(wrow + (4 * i + g) * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int et = 0; et < 4; ++et) acc[et] = mfma16(a[i], b[et][i], acc[et]);
+    for (int i = 0; i < 4; ++i) b[et][i] = ld16(wrow + (4 * i + g) * 8);
   }
+  // Keep every load above this point: one memory round trip.
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 acc[4] = {};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int et = 0; et < 4; ++et) acc[et] = mfma16(a[i], b[et][i], acc[et]);
+  // Accumulator of lane: expert et*16 + r16, tokens 4g + r.
+  float* dst = part + static_cast<size_t>(blockIdx.x) * kRouteTokens * kExperts;
 #pragma unroll
   for (int et = 0; et < 4; ++et)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) part[ks][tt * 16 + 4 * g + r][et * 16 + r16] = acc[et][r];
-  __syncthreads();
+    for (int r = 0; r < 4; ++r) dst[(4 * g + r) * kExperts + et * 16 + r16] = acc[et][r];
+}
 
-  // ---- selection: one wavefront per token, lane e holds expert e ----
+__global__ __launch_bounds__(kSelectThreads) void route_select_kernel(
+    const float* __restrict__ part, const float* __restrict__ bias, int32_t* __restrict__ idx_out,
+    float* __restrict__ w_out, int32_t* __restrict__ blockcounts, int N) {
+  __shared__ int wave_counts[kRouteTokens][kExperts];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = threadIdx.x / kWave;  // token of this wavefront within the tile
+  const int tg = blockIdx.x * kRouteTokens + t;
+  const float* src = part + static_cast<size_t>(blockIdx.x) * kSlices * kRouteTokens * kExperts +
+                     t * kExperts + lane;
   const float b_e = bias[lane];
-  int my_count = 0;
-  for (int t = wave; t < TM; t += kRouteWaves) {
-    float l = 0.0f;
+  float p[kSlices];
 #pragma unroll
-    for (int s = 0; s < kSplits; ++s) l += part[s][t][lane];
-    const float s_e = 1.0f / (1.0f + expf(-l));
-    const float c_e = s_e + b_e;
-    const uint64_t key = (static_cast<uint64_t>(orderable(c_e)) << 32) |
-                         static_cast<uint32_t>(kExperts - 1 - lane);
-    bool taken = false;
-    int sel[kTopK];
-    float sel_s[kTopK];
-    float sum = 0.0f;
+  for (int s = 0; s < kSlices; ++s) p[s] = src[s * kRouteTokens * kExperts];
+  float l = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kTopK; ++j) {
-      uint64_t k = taken ? 0ull : key;
+  for (int s = 0; s < kSlices; ++s) l += p[s];
+  const float s_e = 1.0f / (1.0f + expf(-l));
+  const float c_e = s_e + b_e;
+  const uint32_t key = orderable(c_e);
+  bool taken = false;
+  int sel[kTopK];
+  float sel_s[kTopK];
+  float sum = 0.0f;
 #pragma unroll
-      for (int off = kWave / 2; off >= 1; off >>= 1) {
-        const uint64_t o = __shfl_xor(k, off, kWave);
-        k = o > k ? o : k;
-      }
-      const int win = kExperts - 1 - static_cast<int>(k & 0xffffffffu);
-      taken = taken || (lane == win);
-      sel[j] = win;
-      sel_s[j] = __shfl(s_e, win, kWave);
-      sum += sel_s[j];
-    }
-    const int tg = t0 + t;
-    if (tg < N) {
-      my_count += taken ? 1 : 0;
-      if (lane < kTopK) {
-        const float denom = sum + kRouterEps;
-        int e_out = sel[0];
-        float s_out = sel_s[0];
+  for (int j = 0; j < kTopK; ++j) {
+    const uint32_t m = wave_max_u32(taken ? 0u : key);
+    // Equal scores: the lowest expert id among them wins.
+    const unsigned long long ball = __ballot(!taken && key == m);
+    const int win = __ffsll(static_cast<long long>(ball)) - 1;
+    taken = taken || (lane == win);
+    sel[j] = win;
+    sel_s[j] = __shfl(s_e, win, kWave);
+    sum += sel_s[j];
+  }
+  const bool valid = tg < N;
+  if (valid && lane < kTopK) {
+    int e_out = sel[0];
+    float s_out = sel_s[0];
 #pragma unroll
-        for (int j = 1; j < kTopK; ++j)
-          if (lane == j) { e_out = sel[j]; s_out = sel_s[j]; }
-        idx_out[static_cast<size_t>(tg) * kTopK + lane] = e_out;
-        w_out[static_cast<size_t>(tg) * kTopK + lane] = s_out / denom;
-      }
-    }
+    for (int j = 1; j < kTopK; ++j)
+      if (lane == j) { e_out = sel[j]; s_out = sel_s[j]; }
+    idx_out[static_cast<size_t>(tg) * kTopK + lane] = e_out;
+    w_out[static_cast<size_t>(tg) * kTopK + lane] = s_out / (sum + kRouterEps);
   }
   if (blockcounts != nullptr) {
-    wave_counts[wave][lane] = my_count;
+    wave_counts[t][lane] = (valid && taken) ? 1 : 0;
     __syncthreads();
-    if (wave == 0) {
+    if (t == 0) {
       int c = 0;
 #pragma unroll
-      for (int w = 0; w < kRouteWaves; ++w) c += wave_counts[w][lane];
+      for (int w = 0; w < kRouteTokens; ++w) c += wave_counts[w][lane];
       blockcounts[static_cast<size_t>(blockIdx.x) * kExperts + lane] = c;
     }
   }
@@ -133,18 +137,22 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 
 }  // namespace
 
-int route_block_tokens(int64_t N) { return N <= 2048 ? 16 : 64; }
+int route_block_tokens(int64_t) { return kRouteTokens; }
+
+size_t route_partial_bytes(int64_t N) {
+  const size_t tiles = static_cast<size_t>((N + kRouteTokens - 1) / kRouteTokens);
+  return tiles * kSlices * kRouteTokens * kExperts * sizeof(float);
+}
 
 hipError_t launch_route(const uint16_t* X, const uint16_t* Wr, const float* bias, int32_t* idx,
-                        float* w, int32_t* blockcounts, int N, hipStream_t stream) {
-  const int tm = route_block_tokens(N);
-  const int grid = (N + tm - 1) / tm;
-  if (tm == 16)
-    hipLaunchKernelGGL(route_kernel<16>, dim3(grid), dim3(kRouteThreads), 0, stream, X, Wr, bias,
-                       idx, w, blockcounts, N);
-  else
-    hipLaunchKernelGGL(route_kernel<64>, dim3(grid), dim3(kRouteThreads), 0, stream, X, Wr, bias,
-                       idx, w, blockcounts, N);
+                        float* w, int32_t* blockcounts, float* part, int N, hipStream_t stream) {
+  const int tiles = (N + kRouteTokens - 1) / kRouteTokens;
+  hipLaunchKernelGGL(route_partial_kernel, dim3(tiles * kSlices), dim3(kWave), 0, stream, X, Wr,
+                     part, N);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(route_select_kernel, dim3(tiles), dim3(kSelectThreads), 0, stream, part, bias,
+                     idx, w, blockcounts, N);
   return hipGetLastError();
 }
 

@@ -87,6 +87,9 @@ lfm_moe_status lfm_moe_rmsnorm(const float* x, uint16_t* X, int64_t N, hipStream
  *   idx:  [N, 4] int32 (written): selected experts by descending selection
  *         score s + bias, equal scores ordered by lower expert id
  *   w:    [N, 4] fp32 (written): w[t, j] = s[idx[t, j]] / (sum_j s + 1e-6)
+ * The logits are summed from 16 partial products over 128-wide K slices,
+ * in a fixed order, in the library-owned workspace of the current device
+ * (grown on demand as for lfm_moe_forward).
  */
 lfm_moe_status lfm_moe_route(const uint16_t* X, const uint16_t* W_r, const float* bias,
                              int32_t* idx, float* w, int64_t N, hipStream_t stream);
@@ -101,14 +104,18 @@ lfm_moe_status lfm_moe_route(const uint16_t* X, const uint16_t* W_r, const float
  * columns 8 (l / 16) .. 8 (l / 16) + 7 -- the order in which the 64 lanes
  * of a wavefront hold a 16x16x32 MFMA operand.
  *
+ * Fragments are ordered so that, for one 32-wide K step, the fragments a
+ * workgroup of the expert kernels reads are one contiguous 8 KB run.
+ *
  * lfm_moe_pack_gateup: W_gate, W_up [64, 1536, 2048] bf16 row-major (read)
  *   -> W_gateup [64 * 3072 * 2048] bf16 (written): fragment
- *   ((e * 96 + hb) * 2 + p) * 64 + kf holds rows hb*16 .. hb*16+15 of
- *   W_gate (p = 0) or W_up (p = 1) of expert e, columns kf*32 .. kf*32+31.
+ *   ((e * 24 + nb) * 64 + kf) * 8 + cb * 2 + p holds rows
+ *   nb*64 + cb*16 .. +15 of W_gate (p = 0) or W_up (p = 1) of expert e,
+ *   columns kf*32 .. kf*32+31 (nb < 24, cb < 4, kf < 64).
  * lfm_moe_pack_down: W_down [64, 2048, 1536] bf16 row-major (read)
  *   -> W_down_packed [64 * 2048 * 1536] bf16 (written): fragment
- *   (e * 128 + rt) * 48 + kf holds rows rt*16 .. rt*16+15 of W_down of
- *   expert e, columns kf*32 .. kf*32+31.
+ *   ((e * 16 + rb) * 48 + kf) * 8 + rt holds rows rb*128 + rt*16 .. +15 of
+ *   W_down of expert e, columns kf*32 .. kf*32+31 (rb < 16, rt < 8).
  * Outputs must not overlap the inputs.  A pure permutation: bit exact.
  */
 lfm_moe_status lfm_moe_pack_gateup(const uint16_t* W_gate, const uint16_t* W_up,
@@ -141,13 +148,13 @@ size_t lfm_moe_workspace_bytes(int64_t N);
 typedef enum {
   LFM_MOE_WS_IDX = 0,       /* [N, 4] int32 selected experts */
   LFM_MOE_WS_W = 1,         /* [N, 4] fp32 mixture weights */
-  LFM_MOE_WS_BLOCKCOUNTS = 2, /* [ceil(N / route block), 64] int32 per-block histogram */
+  LFM_MOE_WS_BLOCKCOUNTS = 2, /* [ceil(N / 16), 64] int32 per-16-token histogram (grouped path) */
   LFM_MOE_WS_OFFSETS = 3,   /* [65] int32: offsets[e] = first grouped row of expert e, offsets[64] = 4N */
-  LFM_MOE_WS_ROW2TOK = 4,   /* [4N] int32 grouped row -> token */
-  LFM_MOE_WS_SLOT2ROW = 5,  /* [N, 4] int32 slot (t, j) -> grouped row */
-  LFM_MOE_WS_H = 6,         /* [4N, 1536] bf16 expert hidden rows, grouped order */
-  LFM_MOE_WS_Y = 7,         /* [4N, 2048] fp32 expert output rows, grouped order */
-  LFM_MOE_WS_X = 8,         /* [N, 2048] bf16 normalised input (block forward only) */
+  LFM_MOE_WS_ROW2SLOT = 4,  /* [4N] int32 grouped row -> slot t*4 + j (stable: token order inside an expert) */
+  LFM_MOE_WS_H = 5,         /* [4N, 1536] bf16 expert hidden rows, slot order (row t*4 + j) */
+  LFM_MOE_WS_Y = 6,         /* [4N, 2048] fp32 expert output rows, slot order (row t*4 + j) */
+  LFM_MOE_WS_X = 7,         /* [N, 2048] bf16 normalised input (block forward only) */
+  LFM_MOE_WS_ROUTER_PARTIAL = 8, /* [ceil(N/16), 16, 16, 64] fp32 router partial logits per K slice */
   LFM_MOE_WS_REGIONS = 9
 } lfm_moe_ws_region;
 
@@ -158,7 +165,10 @@ size_t lfm_moe_workspace_offset(int64_t N, int region);
  * lfm_moe_forward with a caller-owned workspace `ws` of `ws_bytes` bytes
  * (device memory, 256-byte aligned, at least lfm_moe_workspace_bytes(N)).
  * The workspace holds the intermediate results listed in lfm_moe_ws_region
- * after the call completes.  Concurrent calls need distinct workspaces.
+ * after the call completes.  Batches of up to 512 tokens take the
+ * decode-shaped path, whose expert kernels group their own tokens and leave
+ * BLOCKCOUNTS, OFFSETS and ROW2SLOT unwritten; larger batches write them.
+ * Concurrent calls need distinct workspaces.
  */
 lfm_moe_status lfm_moe_forward_ws(const uint16_t* X, const uint16_t* W_r, const float* bias,
                                   const uint16_t* W_gateup, const uint16_t* W_down,

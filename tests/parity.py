@@ -102,21 +102,16 @@ def check_out(out_gpu: np.ndarray, expect: np.ndarray, rms: float | None = None)
     return err / rms
 
 
-def check_grouping_valid(idx: np.ndarray, offsets: np.ndarray, row2tok: np.ndarray,
-                         slot2row: np.ndarray) -> None:
+def check_grouping_valid(idx: np.ndarray, offsets: np.ndarray, row2slot: np.ndarray) -> None:
     """The grouping is THE stable counting sort of idx (it is unique)."""
     N = idx.shape[0]
     flat = idx.reshape(-1).astype(np.int64)
     counts = np.bincount(flat, minlength=64)
     assert offsets[0] == 0 and offsets[64] == 4 * N
     np.testing.assert_array_equal(np.diff(offsets), counts)
-    s2r = slot2row.reshape(-1).astype(np.int64)
-    assert np.array_equal(np.sort(s2r), np.arange(4 * N)), "slot2row is not a permutation"
-    tok_of_slot = np.repeat(np.arange(N), 4)
-    np.testing.assert_array_equal(row2tok[s2r], tok_of_slot)
-    row_expert = np.empty(4 * N, dtype=np.int64)
-    row_expert[s2r] = flat
+    r2s = row2slot.astype(np.int64)
+    assert np.array_equal(np.sort(r2s), np.arange(4 * N)), "row2slot is not a permutation"
     for e in range(64):
         a, b = offsets[e], offsets[e + 1]
-        assert np.all(row_expert[a:b] == e)
-        assert np.all(np.diff(row2tok[a:b]) > 0), f"expert {e} rows not in token order"
+        assert np.all(flat[r2s[a:b]] == e)
+        assert np.all(np.diff(r2s[a:b] // 4) > 0), f"expert {e} rows not in token order"

@@ -44,7 +44,8 @@ def test_workspace_layout(lib):
         # H and Y regions hold 4N rows.
         assert offs[_lib.WS_Y] - offs[_lib.WS_H] >= 4 * N * 1536 * 2
         assert offs[_lib.WS_X] - offs[_lib.WS_Y] >= 4 * N * 2048 * 4
-        assert total - offs[_lib.WS_X] >= N * 2048 * 2
+        assert offs[_lib.WS_ROUTER_PARTIAL] - offs[_lib.WS_X] >= N * 2048 * 2
+        assert total - offs[_lib.WS_ROUTER_PARTIAL] >= -(-N // 16) * 16 * 16 * 64 * 4
     assert lib.lfm_moe_workspace_bytes(-1) == 0
     assert lib.lfm_moe_workspace_offset(10, 99) == ctypes.c_size_t(-1).value
 
