@@ -144,6 +144,45 @@ def summarize(p, wall_ms, per_kernel):
     )
 
 
+def kernel_source_digest(path):
+    import hashlib
+    with open(os.path.join(ROOT, "biased_sigmoid_top_amd", "csrc", path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per gate/up launch from the committed rocprofv3 counter
+    summary of this workload, or None when it is missing or was taken on a
+    different version of the kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_gateup_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    start = text.find("```json")
+    if start < 0:
+        return None
+    rec = json.loads(text[start + 7:text.index("```", start + 7)])
+    if rec.get("source_digest") != kernel_source_digest(rec["source"]):
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+def roofline(h, workload):
+    """Roofline object of the dominant kernel (gate/up): HBM-bound for the
+    decode-shaped path (N <= 512), bf16-MFMA-bound for the grouped path."""
+    N, A = h["N"], h["active_experts"]
+    ms = h["kernel_ms"]["gateup"]
+    if N <= 512:
+        return dict(bound="hbm", kernel="gateup_decode", achieved=h["gateup_gbs"],
+                    peak=HBM_PEAK_GBS, unit="GB/s", frac=h["gateup_gbs"] / HBM_PEAK_GBS,
+                    traffic=measured_traffic(workload), bytes_per_launch=gateup_bytes(A, N),
+                    avg_launch_ms=ms)
+    return dict(bound="mfma", kernel="gateup_tiled", achieved=h["gateup_tflops"],
+                peak=BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=h["gateup_tflops"] / BF16_PEAK_TFLOPS,
+                traffic=measured_traffic(workload), flops_per_launch=gateup_flops(N),
+                avg_launch_ms=ms)
+
+
 def cpu_baseline(p, budget_s):
     """The oracle as it stands, timed on this host's cores on the same workload."""
     import numpy as np
@@ -182,7 +221,7 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": n, "copies": 3}))
 
 
-def main():
+def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -194,11 +233,15 @@ def main():
                     help="time budget of the oracle baseline (0 leaves it out)")
     ap.add_argument("--copy-probe", action="store_true", help="only run a plain 1 GiB copy")
     ap.add_argument("--workload", default="decode_n64", help="headline workload")
-    args = ap.parse_args()
+    return ap.parse_args(argv)
+
+
+def main():
+    args = parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one MI355X: multi-GPU runs are not part of this build "
-              "(the layer would shard by tokens or by experts; see the design notes).",
+        print("bench.py measures one MI355X; it does not run on several GPUs (the layer would "
+              "shard by tokens, or by experts with an all-to-all, across them).",
               file=sys.stderr)
         sys.exit(2)
     import torch
@@ -233,21 +276,21 @@ def main():
         log(f"timing the oracle for ~{args.cpu_seconds:.0f} s on host cores")
         cpu = cpu_baseline(head, args.cpu_seconds)
 
-    gu_ms = h["kernel_ms"]["gateup"]
-    A, N = h["active_experts"], h["N"]
-    roof = dict(bound="hbm", kernel="gateup_stream", achieved=h["gateup_gbs"], peak=HBM_PEAK_GBS,
-                unit="GB/s", frac=h["gateup_gbs"] / HBM_PEAK_GBS, traffic=None,
-                bytes_per_launch=gateup_bytes(A, N), avg_launch_ms=gu_ms)
+    print(json.dumps(build_line(args, h, head["seed"], second, cpu)), flush=True)
+
+
+def build_line(args, h, seed, second=None, cpu=None):
+    """The one JSON result line from the measured summaries."""
     line = dict(
         metric=METRIC, value=h["tokens_per_s"], unit="tokens/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=h["ms_per_step"], higher_is_better=True, scaling="weak",
         vs_baseline=None, dtype="bf16", data="synthetic",
-        config=dict(workload=args.workload, N=N, d=D, experts=E, top_k=K, ff=FF, seed=head["seed"],
-                    active_experts=A, max_tokens_per_expert=h["max_tokens_per_expert"],
-                    weight_copies=args.copies),
+        config=dict(workload=args.workload, N=h["N"], d=D, experts=E, top_k=K, ff=FF, seed=seed,
+                    active_experts=h["active_experts"],
+                    max_tokens_per_expert=h["max_tokens_per_expert"], weight_copies=args.copies),
         layer=dict(gbs=h["layer_gbs"], hbm_frac=h["layer_hbm_frac"], tflops=h["layer_tflops"],
                    mfma_frac=h["layer_mfma_frac"], kernel_ms=h["kernel_ms"]),
-        roofline=roof, cpu_baseline=cpu,
+        roofline=roofline(h, args.workload), cpu_baseline=cpu,
     )
     if second is not None:
         line["prefill"] = dict(
@@ -256,11 +299,8 @@ def main():
             gbs=second["layer_gbs"], hbm_frac=second["layer_hbm_frac"],
             tflops=second["layer_tflops"], mfma_frac=second["layer_mfma_frac"],
             kernel_ms=second["kernel_ms"],
-            roofline=dict(bound="mfma", kernel="gateup", achieved=second["gateup_tflops"],
-                          peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                          frac=second["gateup_tflops"] / BF16_PEAK_TFLOPS,
-                          flops_per_launch=gateup_flops(second["N"]),
-                          avg_launch_ms=second["kernel_ms"]["gateup"]))
+            roofline=roofline(second, args.secondary))
+    return line
     print(json.dumps(line), flush=True)
 
 
