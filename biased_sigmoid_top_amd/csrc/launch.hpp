@@ -27,19 +27,12 @@ hipError_t launch_route(const uint16_t* X, const uint16_t* Wr, const float* bias
 hipError_t launch_dispatch(const int32_t* idx, const int32_t* blockcounts, int32_t* offsets,
                            int32_t* row2slot, int N, hipStream_t stream);
 
-// Decode path: expert-major grids that group their own tokens (N <= kDecodeMaxTokens).
+// Decode path: persistent kernels (one workgroup per CU) that group their
+// own tokens (N <= kDecodeMaxTokens).
 hipError_t launch_gateup_decode(const uint16_t* X, const uint16_t* Wgu, const int32_t* idx,
                                 uint16_t* H, int N, hipStream_t stream);
 hipError_t launch_down_decode(const uint16_t* H, const uint16_t* Wd, const int32_t* idx,
                               float* Y, int N, hipStream_t stream);
-
-// Grouped path over the dispatch step's expert-grouped rows.
-hipError_t launch_gateup_grouped_stream(const uint16_t* X, const uint16_t* Wgu,
-                                        const int32_t* offsets, const int32_t* row2slot,
-                                        uint16_t* H, int64_t N, hipStream_t stream);
-hipError_t launch_down_grouped_stream(const uint16_t* H, const uint16_t* Wd,
-                                      const int32_t* offsets, const int32_t* row2slot, float* Y,
-                                      int64_t N, hipStream_t stream);
 
 // Grouped path, LDS-tiled MFMA kernels (prefill-shaped batches).
 hipError_t launch_gateup_tiled(const uint16_t* X, const uint16_t* Wgu, const int32_t* offsets,
