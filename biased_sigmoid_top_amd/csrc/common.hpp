@@ -19,6 +19,7 @@ constexpr int kDecodeMaxTokens = 512;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // 16 bytes of bf16 values as loaded from memory.
 struct alignas(16) Pack8 {
@@ -53,6 +54,32 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 __device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
+
+// D = A * B + C on a 32x32 tile with K = 16 (bf16 in, fp32 accumulate).
+// Lane l supplies row (l % 32) of A and column (l % 32) of B, K elements
+// 8 (l / 32) .. 8 (l / 32) + 7 each; accumulator value r of lane l is
+// column (l % 32), row 8 (r / 4) + 4 (l / 32) + (r % 4).  On gfx950 this
+// form runs at twice the bf16 rate of the 16x16x32 one.
+__device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// Row of the 32-row tile held by accumulator value r of lane l.
+__device__ __forceinline__ int mfma32_row(int r, int lane) {
+  return 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+}
+
+// Packed expert weights: 1 KB fragments of 32 rows x 16 K, lane-major
+// (bytes [16 l, 16 l + 16) hold row l % 32, K 8 (l / 32) .. + 7), ordered
+// (expert, 32-row block, K step) with the K steps of a block contiguous.
+// Gate/up: block b has W_gate rows 16 b .. 16 b + 15 as rows 0..15 and the
+// W_up rows 16 b .. 16 b + 15 as rows 16..31 (96 blocks, 128 K steps);
+// down: block b has W_down rows 32 b .. 32 b + 31 (64 blocks, 96 K steps).
+constexpr int kGateupBlocks = kFF / 16;
+constexpr int kGateupSteps = kHidden / 16;
+constexpr int kDownBlocks = kHidden / 32;
+constexpr int kDownSteps = kFF / 16;
+constexpr uint32_t kFragBytes = 1024;
 
 __device__ __forceinline__ float silu(float g) {
   return g / (1.0f + __expf(-g));

@@ -12,8 +12,9 @@
 // With a handful of tokens per expert the work is bound by reading each
 // active expert's weights from HBM once.  Weights are in the packed
 // fragment layout (pack.hip), so each wavefront load of a weight operand is
-// one contiguous 1 KB non-temporal read that lands directly in the MFMA A
-// registers, and every weight fragment is read once.
+// one contiguous 1 KB non-temporal read that lands directly in the A
+// registers of a 32x32x16 MFMA, and every weight fragment is read once.  Up
+// to 32 tokens of an expert form the B operand of one pass.
 //
 // Work split: the work is cut into units -- one expert's 16 H columns (128
 // KB of gate/up weights) or 32 output features (96 KB of down weights) --
@@ -41,9 +42,7 @@ namespace lfm {
 
 namespace {
 
-constexpr int kFrag = 512;                         // bf16 elements per 16x32 fragment
-constexpr int kDecodeTT = 2;                       // token tiles of 16 per pass
-constexpr int kPassRows = 16 * kDecodeTT;
+constexpr int kPassRows = 32;                      // tokens per pass (one 32x32 MFMA tile)
 constexpr int kStreamThreads = 1024;               // 16 wavefronts: one workgroup per CU
 constexpr int kStreamWaves = kStreamThreads / kWave;
 constexpr int kMaskWords = kDecodeMaxTokens / 32;
@@ -64,8 +63,6 @@ __device__ __forceinline__ uint4 buf_ld(Rsrc r, uint32_t voff, uint32_t soff) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-constexpr uint32_t kFragBytes = kFrag * 2;
-
 // A value that is the same in every lane, made known to be so (kept in a
 // scalar register).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -73,20 +70,11 @@ __device__ __forceinline__ uint32_t uniform(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
 }
 
-// Byte offset of the gate fragment (first K step) of 16-column block hb of
-// expert e; the up fragment follows it, and K steps are 8 fragments apart
-// (64-column groups of 4 blocks x gate/up).
-__device__ __forceinline__ uint32_t gateup_frag_bytes(int e, int hb) {
-  return static_cast<uint32_t>(((e * (kFF / 64) + hb / 4) * (kHidden / 32) * 8 + (hb % 4) * 2)) *
-         kFragBytes;
-}
-
-// Byte offset of down-weight row tile rt (first K fragment) of expert e; the
-// K fragments of a tile are 8 fragments apart, and the 8 tiles of a 128-row
-// block are adjacent.
-__device__ __forceinline__ uint32_t down_frag_bytes(int e, int rt) {
-  return static_cast<uint32_t>(((e * (kHidden / 128) + rt / 8) * (kFF / 32) * 8 + rt % 8)) *
-         kFragBytes;
+// Byte offset of the first K-step fragment of row block b of expert e.
+template <bool GATEUP>
+__device__ __forceinline__ uint32_t block_bytes(int e, int b) {
+  return static_cast<uint32_t>(GATEUP ? (e * kGateupBlocks + b) * kGateupSteps
+                                      : (e * kDownBlocks + b) * kDownSteps) * kFragBytes;
 }
 
 // Grouping of the batch's slots by expert, in LDS.
@@ -102,7 +90,7 @@ struct Grouping {
 // Workgroup state: the grouping and the wavefronts' partial tiles.
 struct StreamShared {
   Grouping G;
-  f32x4 red[kStreamWaves][2][kDecodeTT][kWave];
+  float red[kStreamWaves][16][kWave];  // value r of lane l of each wavefront
 };
 
 // Groups the slots t*4 + j of N <= kDecodeMaxTokens tokens by expert.
@@ -151,62 +139,48 @@ __device__ __forceinline__ void my_share(int units, int& begin, int& end) {
   end = static_cast<int>(static_cast<int64_t>(units) * (blockIdx.x + 1) / gridDim.x);
 }
 
-// Once the wavefronts' partial tiles are in LDS, thread (tt, ln, q) of the
-// first 512 adds up accumulator value q of lane ln of token tile tt: token
-// row 16 tt + ln % 16, column 4 (ln / 16) + q of the 16-wide tile.
-struct Owner {
-  bool on;
-  int tt, ln, q, row;
-};
-__device__ __forceinline__ Owner owner() {
-  Owner o;
-  o.on = threadIdx.x < kDecodeTT * kWave * 4;
-  o.tt = (threadIdx.x / 256) % kDecodeTT;
-  o.ln = (threadIdx.x / 4) % kWave;
-  o.q = threadIdx.x % 4;
-  o.row = o.tt * 16 + (o.ln & 15);
-  return o;
-}
-
-// This lane's rows of a pass: slot of row tt*16 + r16 (rows past `rows`
+// This lane's token of a pass: slot of row lane % 32 (rows past `rows`
 // repeat the first row; their results are discarded).
-__device__ __forceinline__ int pass_slot(const int* slots, int rows, int tt, int r16) {
-  const int r = tt * 16 + r16;
+__device__ __forceinline__ int pass_slot(const int* slots, int rows, int lane) {
+  const int r = lane % 32;
   return slots[r < rows ? r : 0];
 }
 
 // Position in a workgroup's sequence of sub-units: unit u, pass `pass` over
-// the expert's rows (kPassRows at a time), half p (gate / up fragments, or
-// the first / second output tile of the unit).  All values are uniform.
+// the expert's rows (kPassRows at a time), half p of the unit's K range.
+// All values are uniform.
 struct Cursor {
   int u, pass, p;
 };
 
 // The per-wavefront pipeline shared by the two kernels.
-//   GATEUP: unit = 16 H columns of one expert; half p streams the gate (0)
-//           or up (1) weights; B operand = rows of X; K = 2048.
-//   down:   unit = 32 output features of one expert; half p streams row
-//           tile 2 (u % 64) + p; B operand = rows of H; K = 1536.
-// Each wavefront covers kF = K / 32 / 16 K fragments of every half.  The
-// weights of a half (kF fragments per wavefront, 64 KB (gate/up) or 48 KB
-// (down) per workgroup) go through a ring of three register buffers, so two
-// halves are in flight while one is multiplied.
+//   GATEUP: unit = row block b of the packed gate/up weights of one expert
+//           (16 H columns: 16 gate rows and 16 up rows); B operand = rows
+//           of X; K = 2048 (128 K steps of 16).
+//   down:   unit = row block b of W_down (32 output features); B operand =
+//           rows of H; K = 1536 (96 K steps).
+// Each wavefront covers kS = K steps / 16 consecutive K steps of every
+// unit, in two halves of kF = kS / 2.  The weights of a half (kF fragments
+// per wavefront, 64 KB (gate/up) or 48 KB (down) per workgroup) go through
+// a ring of three register buffers, so two halves are in flight while one
+// is multiplied.  The 16 partial 32x32 tiles of a unit are added in LDS in
+// wavefront order.
 template <bool GATEUP>
 __device__ __forceinline__ void stream_units(const uint16_t* __restrict__ B,
                                              const uint16_t* __restrict__ Wp,
                                              uint16_t* __restrict__ H, float* __restrict__ Y,
                                              int N, StreamShared& S) {
   constexpr int K = GATEUP ? kHidden : kFF;
-  constexpr int kF = (K / 32) / kStreamWaves;
-  constexpr int kUnitsPerExpert = GATEUP ? kFF / 16 : kHidden / 32;
+  constexpr int kS = (GATEUP ? kGateupSteps : kDownSteps) / kStreamWaves;  // 8 or 6
+  constexpr int kF = kS / 2;
+  constexpr int kUnitsPerExpert = GATEUP ? kGateupBlocks : kDownBlocks;
   int begin, end;
   my_share(uniform(S.G.n_active) * kUnitsPerExpert, begin, end);
   if (begin >= end) return;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int r16 = lane & 15;
   const uint32_t lane_bytes = lane * 16;
-  const uint32_t kcol_bytes = (wave * kF * 32 + (lane >> 4) * 8) * 2;  // this lane's first K column
+  const uint32_t kcol_bytes = (wave * kS * 16 + (lane / 32) * 8) * 2;  // this lane's first K column
   const Rsrc wr = make_rsrc(Wp, static_cast<uint32_t>(kExperts) * 2 * kFF * kHidden * (GATEUP ? 2 : 1));
   const Rsrc br = make_rsrc(B, static_cast<uint32_t>(N) * (GATEUP ? 1 : kTopK) * K * 2);
 
@@ -226,34 +200,27 @@ __device__ __forceinline__ void stream_units(const uint16_t* __restrict__ B,
   auto issue = [&](const Cursor& c, uint4 (&w)[kF]) {
     const bool live = c.u < end;
     const int u = live ? c.u : begin;
-    const int e = expert_of(u);
-    const int j = u % kUnitsPerExpert;
-    const uint32_t base =
-        uniform((GATEUP ? gateup_frag_bytes(e, j) : down_frag_bytes(e, 2 * j)) +
-                (c.p + wave * kF * 8) * kFragBytes);
+    const uint32_t base = uniform(block_bytes<GATEUP>(expert_of(u), u % kUnitsPerExpert) +
+                                  (wave * kS + c.p * kF) * kFragBytes);
     const uint32_t voff = live ? lane_bytes : 0x80000000u + lane_bytes;
 #pragma unroll
-    for (int f = 0; f < kF; ++f) w[f] = buf_ld<true>(wr, voff, base + f * 8 * kFragBytes);
+    for (int f = 0; f < kF; ++f) w[f] = buf_ld<true>(wr, voff, base + f * kFragBytes);
   };
 
-  uint4 w0[kF], w1[kF], w2[kF], xb[kDecodeTT][kF];
-  f32x4 acc[2][kDecodeTT];
+  uint4 w0[kF], w1[kF], w2[kF], xb[kS];
+  f32x16 acc;
   int xe = -1, xpass = -1;  // expert and pass whose rows are in xb
-  // Loads this lane's token rows for the pass of cursor c (unless present).
+  // Loads this lane's token row for the pass of cursor c (unless present).
   auto load_rows = [&](const Cursor& c) {
     if (c.u >= end) return;
     const int e = expert_of(c.u);
     if (e == xe && c.pass == xpass) return;
     const int r0 = c.pass * kPassRows;
     const int rows = min(kPassRows, count_of(e) - r0);
-    const int* slots = S.G.list + S.G.off[e] + r0;
+    const int slot = pass_slot(S.G.list + S.G.off[e] + r0, rows, lane);
+    const uint32_t bo = (GATEUP ? slot / kTopK : slot) * (K * 2) + kcol_bytes;
 #pragma unroll
-    for (int tt = 0; tt < kDecodeTT; ++tt) {
-      const int slot = pass_slot(slots, rows, tt, r16);
-      const uint32_t bo = (GATEUP ? slot / kTopK : slot) * (K * 2) + kcol_bytes;
-#pragma unroll
-      for (int f = 0; f < kF; ++f) xb[tt][f] = buf_ld<false>(br, bo, f * 64);
-    }
+    for (int f = 0; f < kS; ++f) xb[f] = buf_ld<false>(br, bo, f * 32);
     xe = e;
     xpass = c.pass;
   };
@@ -269,25 +236,20 @@ __device__ __forceinline__ void stream_units(const uint16_t* __restrict__ B,
   // to wi.  Order: multiply, then (at the end of a unit) the next unit's
   // token rows, then the weight loads, then the cross-wavefront reduction,
   // so a multiply only ever waits for its own operands.
-  auto step = [&](auto half, uint4 (&wc)[kF], uint4 (&wi)[kF]) {
+  auto step = [&](auto half, uint4 (&wc)[kF], uint4 (&wi)[kF]) -> bool {
     constexpr int P = decltype(half)::value;
+    if (cp.u >= end) return false;
     if (P == 0) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int tt = 0; tt < kDecodeTT; ++tt) acc[h][tt] = f32x4{0, 0, 0, 0};
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
     }
 #pragma unroll
-    for (int f = 0; f < kF; ++f)
-#pragma unroll
-      for (int tt = 0; tt < kDecodeTT; ++tt) acc[P][tt] = mfma16(wc[f], xb[tt][f], acc[P][tt]);
+    for (int f = 0; f < kF; ++f) acc = mfma32(wc[f], xb[P * kF + f], acc);
     const Cursor cur = cp;
     advance(cp);
     if (P == 1) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int tt = 0; tt < kDecodeTT; ++tt) S.red[wave][h][tt][lane] = acc[h][tt];
+      for (int r = 0; r < 16; ++r) S.red[wave][r][lane] = acc[r];
       load_rows(cp);
     }
     issue(ld, wi);
@@ -297,33 +259,39 @@ __device__ __forceinline__ void stream_units(const uint16_t* __restrict__ B,
       const int e = expert_of(cur.u);
       const int r0 = cur.pass * kPassRows;
       const int rows = min(kPassRows, count_of(e) - r0);
-      const Owner own = owner();
-      if (own.on && own.row < rows) {
-        float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-        for (int w = 0; w < kStreamWaves; ++w) {
-          s0 += S.red[w][0][own.tt][own.ln][own.q];
-          s1 += S.red[w][1][own.tt][own.ln][own.q];
-        }
-        const int slot = S.G.list[S.G.off[e] + r0 + own.row];
-        const int col = (cur.u % kUnitsPerExpert) * (GATEUP ? 16 : 32) + 4 * (own.ln >> 4) + own.q;
+      const int* slots = S.G.list + S.G.off[e] + r0;
+      const int b = cur.u % kUnitsPerExpert;
+      // Thread (r, ln) adds value r of lane ln over the wavefronts: token
+      // ln % 32, row mfma32_row(r, ln) of the unit's 32-row tile.
+      const int ln = threadIdx.x % kWave;
+      const int r = threadIdx.x / kWave;
+      if (ln % 32 < rows) {
+        const int slot = slots[ln % 32];
         if (GATEUP) {
-          H[static_cast<size_t>(slot) * kFF + col] = f32_to_bf16(silu(s0) * s1);
+          if (r < 8) {  // rows r (gate) and r + 8 (up) hold H column mfma32_row(r, ln)
+            float gs = 0.f, us = 0.f;
+#pragma unroll
+            for (int w = 0; w < kStreamWaves; ++w) {
+              gs += S.red[w][r][ln];
+              us += S.red[w][r + 8][ln];
+            }
+            H[static_cast<size_t>(slot) * kFF + b * 16 + mfma32_row(r, ln)] = f32_to_bf16(silu(gs) * us);
+          }
         } else {
-          float* dst = Y + static_cast<size_t>(slot) * kHidden + col;
-          dst[0] = s0;
-          dst[16] = s1;
+          float ys = 0.f;
+#pragma unroll
+          for (int w = 0; w < kStreamWaves; ++w) ys += S.red[w][r][ln];
+          Y[static_cast<size_t>(slot) * kHidden + b * 32 + mfma32_row(r, ln)] = ys;
         }
       }
       __syncthreads();
     }
+    return true;
   };
   // Both halves of one pass: a and b hold their weights, c is free.
   auto pass = [&](uint4 (&a)[kF], uint4 (&b)[kF], uint4 (&c)[kF]) -> bool {
-    if (cp.u >= end) return false;
-    step(std::integral_constant<int, 0>{}, a, c);
-    step(std::integral_constant<int, 1>{}, b, a);
-    return true;
+    if (!step(std::integral_constant<int, 0>{}, a, c)) return false;
+    return step(std::integral_constant<int, 1>{}, b, a);
   };
   // Sub-unit s uses buffer s % 3: unrolled by three passes.
   for (;;) {

@@ -4,20 +4,21 @@
 // Caches", section "The router has two different scores") notes that the
 // runtime representation may pack an expert's two input matrices together
 // without changing the function.  This library packs every expert matrix
-// into 16-row x 32-column fragments of 1 KB, each stored in the order in
-// which the 64 lanes of a wavefront hold a 16x16x32 MFMA operand: bytes
-// [16 l, 16 l + 16) of a fragment are row (l % 16), columns
-// 8 (l / 16) .. 8 (l / 16) + 7.  A wavefront then loads one operand with a
+// into fragments of 32 rows x 16 columns (1 KB), each stored in the order in
+// which the 64 lanes of a wavefront hold a 32x32x16 MFMA operand: bytes
+// [16 l, 16 l + 16) of a fragment are row (l % 32), columns
+// 8 (l / 32) .. 8 (l / 32) + 7.  A wavefront then loads one operand with a
 // single contiguous 1 KB read.
 //
-// Fragments are ordered so that, for one 32-wide K step, everything a
-// workgroup of the expert kernels needs is one contiguous 8 KB run:
-//   gate/up: fragment ((e * 24 + nb) * 64 + kf) * 8 + cb * 2 + p holds rows
-//            nb*64 + cb*16 .. +15 of W_gate (p = 0) or W_up (p = 1) of
-//            expert e, columns kf*32 .. kf*32+31   (nb < 24, cb < 4).
-//   down:    fragment ((e * 16 + rb) * 48 + kf) * 8 + rt holds rows
-//            rb*128 + rt*16 .. +15 of W_down of expert e, columns
-//            kf*32 .. kf*32+31                     (rb < 16, rt < 8).
+// Fragments are ordered (expert, 32-row block, 16-column K step), so the K
+// steps of one row block are contiguous:
+//   gate/up: fragment (e * 96 + b) * 128 + ks holds rows 16 b .. 16 b + 15
+//            of W_gate (fragment rows 0..15) and the same rows of W_up
+//            (fragment rows 16..31) of expert e, columns ks*16 .. ks*16+15.
+//            An MFMA on it yields the gate and the up value of an H column
+//            in the same lane.
+//   down:    fragment (e * 64 + b) * 96 + ks holds rows 32 b .. 32 b + 31 of
+//            W_down of expert e, columns ks*16 .. ks*16+15.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -33,16 +34,14 @@ __global__ __launch_bounds__(kPackThreads) void pack_gateup_kernel(
   const size_t piece = static_cast<size_t>(blockIdx.x) * kPackThreads + threadIdx.x;
   const int lane = static_cast<int>(piece % kWave);
   const size_t frag = piece / kWave;
-  const int q = static_cast<int>(frag % 8);  // cb * 2 + p
-  const size_t t = frag / 8;
-  const int kf = static_cast<int>(t % (kHidden / 32));
-  const size_t enb = t / (kHidden / 32);     // e * 24 + nb
-  const size_t e = enb / (kFF / 64);
-  const int nb = static_cast<int>(enb % (kFF / 64));
-  const int cb = q / 2, p = q % 2;
-  const int row = nb * 64 + cb * 16 + (lane % 16);
-  const int col = kf * 32 + (lane / 16) * 8;
-  const uint16_t* src = (p == 0 ? Wg : Wu) + (e * kFF + row) * static_cast<size_t>(kHidden) + col;
+  const int ks = static_cast<int>(frag % kGateupSteps);
+  const size_t eb = frag / kGateupSteps;  // e * 96 + b
+  const size_t e = eb / kGateupBlocks;
+  const int b = static_cast<int>(eb % kGateupBlocks);
+  const int i = lane % 32;
+  const int row = b * 16 + (i % 16);
+  const int col = ks * 16 + (lane / 32) * 8;
+  const uint16_t* src = (i < 16 ? Wg : Wu) + (e * kFF + row) * static_cast<size_t>(kHidden) + col;
   *reinterpret_cast<uint4*>(out + piece * 8) = ld16(src);
 }
 
@@ -51,14 +50,12 @@ __global__ __launch_bounds__(kPackThreads) void pack_down_kernel(const uint16_t*
   const size_t piece = static_cast<size_t>(blockIdx.x) * kPackThreads + threadIdx.x;
   const int lane = static_cast<int>(piece % kWave);
   const size_t frag = piece / kWave;
-  const int rt = static_cast<int>(frag % 8);
-  const size_t t = frag / 8;
-  const int kf = static_cast<int>(t % (kFF / 32));
-  const size_t erb = t / (kFF / 32);         // e * 16 + rb
-  const size_t e = erb / (kHidden / 128);
-  const int rb = static_cast<int>(erb % (kHidden / 128));
-  const int row = rb * 128 + rt * 16 + (lane % 16);
-  const int col = kf * 32 + (lane / 16) * 8;
+  const int ks = static_cast<int>(frag % kDownSteps);
+  const size_t eb = frag / kDownSteps;  // e * 64 + b
+  const size_t e = eb / kDownBlocks;
+  const int b = static_cast<int>(eb % kDownBlocks);
+  const int row = b * 32 + lane % 32;
+  const int col = ks * 16 + (lane / 32) * 8;
   const uint16_t* src = Wd + (e * kHidden + row) * static_cast<size_t>(kFF) + col;
   *reinterpret_cast<uint4*>(out + piece * 8) = ld16(src);
 }

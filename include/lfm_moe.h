@@ -99,23 +99,21 @@ lfm_moe_status lfm_moe_route(const uint16_t* X, const uint16_t* W_r, const float
  * scores": the runtime representation may pack the two input matrices of
  * an expert together; packing does not change the function).
  *
- * The packed layout is made of 1 KB fragments of 16 rows x 32 columns of
- * one matrix; bytes [16 l, 16 l + 16) of a fragment hold row (l % 16),
- * columns 8 (l / 16) .. 8 (l / 16) + 7 -- the order in which the 64 lanes
- * of a wavefront hold a 16x16x32 MFMA operand.
- *
- * Fragments are ordered so that, for one 32-wide K step, the fragments a
- * workgroup of the expert kernels reads are one contiguous 8 KB run.
+ * The packed layout is made of 1 KB fragments of 32 rows x 16 columns;
+ * bytes [16 l, 16 l + 16) of a fragment hold row (l % 32), columns
+ * 8 (l / 32) .. 8 (l / 32) + 7 -- the order in which the 64 lanes of a
+ * wavefront hold a 32x32x16 MFMA operand.  Fragments are ordered (expert,
+ * 32-row block, 16-column step), the steps of one block contiguous.
  *
  * lfm_moe_pack_gateup: W_gate, W_up [64, 1536, 2048] bf16 row-major (read)
  *   -> W_gateup [64 * 3072 * 2048] bf16 (written): fragment
- *   ((e * 24 + nb) * 64 + kf) * 8 + cb * 2 + p holds rows
- *   nb*64 + cb*16 .. +15 of W_gate (p = 0) or W_up (p = 1) of expert e,
- *   columns kf*32 .. kf*32+31 (nb < 24, cb < 4, kf < 64).
+ *   (e * 96 + b) * 128 + ks holds, of expert e and columns ks*16 .. +15,
+ *   rows 16 b .. 16 b + 15 of W_gate as its rows 0..15 and the same rows
+ *   of W_up as its rows 16..31 (b < 96, ks < 128).
  * lfm_moe_pack_down: W_down [64, 2048, 1536] bf16 row-major (read)
  *   -> W_down_packed [64 * 2048 * 1536] bf16 (written): fragment
- *   ((e * 16 + rb) * 48 + kf) * 8 + rt holds rows rb*128 + rt*16 .. +15 of
- *   W_down of expert e, columns kf*32 .. kf*32+31 (rb < 16, rt < 8).
+ *   (e * 64 + b) * 96 + ks holds rows 32 b .. 32 b + 31 of W_down of
+ *   expert e, columns ks*16 .. ks*16+15 (b < 64, ks < 96).
  * Outputs must not overlap the inputs.  A pure permutation: bit exact.
  */
 lfm_moe_status lfm_moe_pack_gateup(const uint16_t* W_gate, const uint16_t* W_up,

@@ -55,20 +55,21 @@ ALL = list(synth.WORKLOADS)
 
 
 def test_weight_packing_is_the_documented_permutation(moe):
-    """Packed fragment layout: gate/up fragment ((e*24 + nb)*64 + kf)*8 +
-    cb*2 + p, lane l = 16 g + r holds row nb*64 + cb*16 + r of W_gate (p = 0)
-    or W_up (p = 1), columns kf*32 + 8 g .. + 7; down fragment
-    ((e*16 + rb)*48 + kf)*8 + rt holds rows rb*128 + rt*16 + r."""
+    """Packed fragment layout: gate/up fragment (e*96 + b)*128 + ks, lane
+    l = 32 h + i holds columns ks*16 + 8 h .. + 7 of row 16 b + i of W_gate
+    (i < 16) or row 16 b + i - 16 of W_up (i >= 16); down fragment
+    (e*64 + b)*96 + ks, lane l = 32 h + i holds row 32 b + i of W_down."""
     w = synth.WORKLOADS["tiny_n32"]
     layer = cached_layer(w["N"], w["seed"], w["skew"])
     Wg, Wu, Wd = layer["W_gate"], layer["W_up"], layer["W_down"]
     _step("pack gate/up and down")
     got_gu = moe.pack_gateup(Wg.cuda(), Wu.cuda()).cpu()
     got_d = moe.pack_down(Wd.cuda()).cpu()
-    # [e, nb, cb, r, kf, g, j] -> [e, nb, kf, cb, (p), g, r, j]
-    gu = lambda W: W.view(64, 24, 4, 16, 64, 4, 8).permute(0, 1, 4, 2, 5, 3, 6)
-    ref_gu = torch.stack([gu(Wg), gu(Wu)], dim=4).reshape(-1)
-    ref_d = Wd.view(64, 16, 8, 16, 48, 4, 8).permute(0, 1, 4, 2, 5, 3, 6).reshape(-1)
+    # [e, b, p, i, ks, h, j] -> [e, b, ks, h, p, i, j]
+    both = torch.stack([Wg.view(64, 96, 16, 128, 2, 8), Wu.view(64, 96, 16, 128, 2, 8)], dim=2)
+    ref_gu = both.permute(0, 1, 4, 5, 2, 3, 6).reshape(-1)
+    # [e, b, i, ks, h, j] -> [e, b, ks, h, i, j]
+    ref_d = Wd.view(64, 64, 32, 96, 2, 8).permute(0, 1, 3, 4, 2, 5).reshape(-1)
     assert torch.equal(got_gu.view(torch.int16), ref_gu.contiguous().view(torch.int16))
     assert torch.equal(got_d.view(torch.int16), ref_d.contiguous().view(torch.int16))
 
