@@ -64,14 +64,17 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def prepare(name, copies):
+def prepare(name, copies, zero_bias=False):
     import torch
     import synth
     import biased_sigmoid_top_amd as moe
     w = synth.WORKLOADS[name]
     N = w["N"]
-    log(f"generating {name}: N={N} seed={w['seed']} skew={w['skew']}")
+    log(f"generating {name}: N={N} seed={w['seed']} skew={w['skew']}"
+        + (" with the bias set to zero" if zero_bias else ""))
     layer = synth.layer_inputs(N, w["seed"], w["skew"])
+    if zero_bias:
+        layer["bias"] = torch.zeros_like(layer["bias"])
     dev = torch.device("cuda")
     X = moe.rmsnorm(layer["z"].to(dev))          # input preparation, not timed
     W_r, bias = layer["W_r"].to(dev), layer["bias"].to(dev)
@@ -168,12 +171,15 @@ def measured_traffic(workload):
 
 
 def roofline(h, workload):
-    """Roofline object of the dominant kernel (gate/up): HBM-bound for the
-    decode-shaped path (N <= 512), bf16-MFMA-bound for the grouped path."""
+    """Roofline object of the dominant kernel (gate/up): HBM-bound while the
+    arithmetic intensity is far below the ridge (N <= 512), bf16-MFMA-bound
+    above."""
+    from biased_sigmoid_top_amd._lib import DECODE_MAX_TOKENS
     N, A = h["N"], h["active_experts"]
     ms = h["kernel_ms"]["gateup"]
     if N <= 512:
-        return dict(bound="hbm", kernel="gateup_decode", achieved=h["gateup_gbs"],
+        kernel = "gateup_decode" if N <= DECODE_MAX_TOKENS else "gateup_tiled"
+        return dict(bound="hbm", kernel=kernel, achieved=h["gateup_gbs"],
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=h["gateup_gbs"] / HBM_PEAK_GBS,
                     traffic=measured_traffic(workload), bytes_per_launch=gateup_bytes(A, N),
                     avg_launch_ms=ms)
@@ -233,6 +239,9 @@ def parse_args(argv=None):
                     help="time budget of the oracle baseline (0 leaves it out)")
     ap.add_argument("--copy-probe", action="store_true", help="only run a plain 1 GiB copy")
     ap.add_argument("--workload", default="decode_n64", help="headline workload")
+    ap.add_argument("--configs", action="store_true",
+                    help="also measure every configuration (C0-C4, the 38-block stack included; "
+                         "several minutes) and add them to the line under 'configs'")
     return ap.parse_args(argv)
 
 
@@ -276,7 +285,12 @@ def main():
         log(f"timing the oracle for ~{args.cpu_seconds:.0f} s on host cores")
         cpu = cpu_baseline(head, args.cpu_seconds)
 
-    print(json.dumps(build_line(args, h, head["seed"], second, cpu)), flush=True)
+    line = build_line(args, h, head["seed"], second, cpu)
+    if args.configs:
+        del head
+        torch.cuda.empty_cache()
+        line["configs"] = measure_configs(args)
+    print(json.dumps(line), flush=True)
 
 
 def build_line(args, h, seed, second=None, cpu=None):
@@ -301,7 +315,110 @@ def build_line(args, h, seed, second=None, cpu=None):
             kernel_ms=second["kernel_ms"],
             roofline=roofline(second, args.secondary))
     return line
-    print(json.dumps(line), flush=True)
+
+
+# Every configuration of the layer contract: (label, workload, zero bias, note).
+CONFIGS = (
+    ("C0", "tiny_n32", False, None),
+    ("C1", "decode_n64", False, None),
+    ("C1u", "decode_n64", True, "supplementary: decode_n64 with the bias set to zero, so that "
+                                "nearly all 64 experts are active"),
+    ("C2", "prefill_n4096", False, None),
+    ("C3", "skewed_n16384", False, None),
+)
+
+
+def config_entry(label, h, note=None):
+    hbm = h["N"] <= 512
+    e = dict(config=label, N=h["N"], active_experts=h["active_experts"],
+             max_tokens_per_expert=h["max_tokens_per_expert"], ms_per_step=h["ms_per_step"],
+             tokens_per_s=h["tokens_per_s"], gbs=h["layer_gbs"], hbm_frac=h["layer_hbm_frac"],
+             tflops=h["layer_tflops"], mfma_frac=h["layer_mfma_frac"],
+             bound="hbm" if hbm else "mfma",
+             roofline_frac=h["layer_hbm_frac"] if hbm else h["layer_mfma_frac"],
+             kernel_ms=h["kernel_ms"])
+    if note:
+        e["note"] = note
+    return e
+
+
+def measure_stack(steps, warmup):
+    """The 38-block stack at N = 512: x <- x + MoE_l(bf16(RMSNorm(x))) for
+    l = 0..37, each block with its own experts (about 46 GB resident)."""
+    from concurrent.futures import ThreadPoolExecutor
+    import torch
+    import synth
+    import biased_sigmoid_top_amd as moe
+    from biased_sigmoid_top_amd import _lib
+    st = synth.STACK
+    N, nb = st["N"], st["blocks"]
+    dev = torch.device("cuda")
+    log(f"generating the stack: {nb} blocks at N={N} seed={st['seed']}")
+    blocks = []
+    with ThreadPoolExecutor(4) as pool:
+        for bp in pool.map(lambda l: synth.stack_block_params(st["seed"], l), range(nb)):
+            blocks.append((bp["W_r"].to(dev), bp["bias"].to(dev),
+                           moe.pack_gateup(bp["W_gate"].to(dev), bp["W_up"].to(dev)),
+                           moe.pack_down(bp["W_down"].contiguous().to(dev))))
+            del bp
+            if len(blocks) % 8 == 0:
+                log(f"  {len(blocks)} blocks on the device")
+    x0 = synth.stack_residual(N, st["seed"]).to(dev)
+    x = x0.clone()
+    ws = moe.alloc_workspace(N)
+    active = []
+    for blk in blocks:  # untimed pass: active experts of every block
+        moe.block_forward(x, *blk, workspace=ws)
+        sel = moe.workspace_view(ws, N, _lib.WS_IDX, torch.int32, (N, 4)).cpu().long()
+        active.append(int((torch.bincount(sel.reshape(-1), minlength=E) > 0).sum()))
+    del ws
+
+    def stack_pass():
+        x.copy_(x0)
+        for blk in blocks:
+            moe.block_forward(x, *blk)
+
+    for _ in range(warmup):
+        stack_pass()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        stack_pass()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    assert torch.isfinite(x).all().item(), "non-finite stack output"
+    bytes_ = sum(a * EXPERT_BYTES + ROUTER_BYTES for a in active) + nb * N * D * 4 * 2
+    flops = nb * N * FLOP_PER_TOKEN
+    s = ms * 1e-3
+    e = dict(config="C4", N=N, blocks=nb, active_experts_per_block_mean=sum(active) / nb,
+             active_experts_per_block_min=min(active), active_experts_per_block_max=max(active),
+             ms_per_step=ms, ms_per_block=ms / nb, tokens_per_s=N / s, gbs=bytes_ / s / 1e9,
+             hbm_frac=bytes_ / s / 1e9 / HBM_PEAK_GBS, tflops=flops / s / 1e12,
+             mfma_frac=flops / s / 1e12 / BF16_PEAK_TFLOPS, bound="hbm",
+             roofline_frac=bytes_ / s / 1e9 / HBM_PEAK_GBS,
+             note="one step = the whole stack (a copy of x0, then 38 block calls)")
+    del blocks
+    torch.cuda.empty_cache()
+    return e
+
+
+def measure_configs(args):
+    import torch
+    out = []
+    for label, name, zero_bias, note in CONFIGS:
+        p = prepare(name, args.copies, zero_bias)
+        steps = args.steps if p["N"] <= 512 else max(5, args.steps // 10)
+        log(f"timing {label} ({name}): {steps} steps")
+        w, k = time_steps(p, steps, max(2, args.warmup // (1 if p["N"] <= 512 else 10)))
+        e = config_entry(label, summarize(p, w, k), note)
+        log(json.dumps(e))
+        out.append(e)
+        del p
+        torch.cuda.empty_cache()
+    e = measure_stack(max(3, args.steps // 40), 1)
+    log(json.dumps(e))
+    out.append(e)
+    return out
 
 
 if __name__ == "__main__":

@@ -13,9 +13,12 @@ constexpr int kFF = 1536;       // expert intermediate width
 constexpr int kWave = 64;       // CDNA wavefront width
 constexpr float kRouterEps = 1e-6f;
 constexpr float kRmsEps = 1e-6f;
-// Largest N taken by the expert-major decode path (its per-expert slot list
-// lives in LDS).
-constexpr int kDecodeMaxTokens = 512;
+// Largest N taken by the decode path (its per-expert slot lists live in
+// LDS).  Measured crossover: the decode kernels win while the experts' token
+// counts fit one 32-token pass (N = 96: 150 us against 190 us for the
+// grouped path); beyond it they stream an expert's weights once per pass
+// (N = 128: 307 us against 192 us).
+constexpr int kDecodeMaxTokens = 96;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

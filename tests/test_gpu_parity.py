@@ -218,7 +218,7 @@ def _layer_case(N, seed_z, bias_override=None):
     return inp, dev
 
 
-@pytest.mark.parametrize("N", [1, 2, 17, 63, 65, 257, 1000, 2049])
+@pytest.mark.parametrize("N", [1, 2, 17, 63, 65, 96, 97, 257, 1000, 2049])
 def test_ragged_token_counts(moe, N):
     inp, dev = _layer_case(N, 100 + N)
     r = oracle.route(inp["X"], inp["W_r"], inp["bias"])
@@ -229,7 +229,7 @@ def test_ragged_token_counts(moe, N):
     check_out(_np(out), expected_outputs(inp, r, np.arange(N), alt))
 
 
-@pytest.mark.parametrize("N", [5, 512, 1000])
+@pytest.mark.parametrize("N", [5, 96, 512, 1000])
 def test_every_token_on_the_same_four_experts(moe, N):
     """Degenerate routing: a large bias puts every token on experts 60..63
     (one group of N rows per expert, 60 empty experts)."""
