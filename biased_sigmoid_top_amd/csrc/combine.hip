@@ -79,10 +79,8 @@ __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const float* __res
   const float inv = 1.0f / sqrtf(tot * (1.0f / kHidden) + kRmsEps);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(v[h].x * inv)) |
-                        (static_cast<uint32_t>(f32_to_bf16(v[h].y * inv)) << 16);
-    const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(v[h].z * inv)) |
-                        (static_cast<uint32_t>(f32_to_bf16(v[h].w * inv)) << 16);
+    const uint32_t lo = pack_bf16x2(v[h].x * inv, v[h].y * inv);
+    const uint32_t hi = pack_bf16x2(v[h].z * inv, v[h].w * inv);
     *reinterpret_cast<uint2*>(X + t * kHidden + (h * kRowThreads + threadIdx.x) * 4) =
         make_uint2(lo, hi);
   }

@@ -42,12 +42,17 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16, round to nearest, ties to even.
+// fp32 -> bf16, round to nearest, ties to even (the gfx950 conversion
+// instruction; NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN stays NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// Two floats to two bf16 in one word, lo in the low half: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 // D = A * B + C on a 16x16 tile with K = 32 (bf16 in, fp32 accumulate).
@@ -85,7 +90,32 @@ constexpr int kDownSteps = kFF / 16;
 constexpr uint32_t kFragBytes = 1024;
 
 __device__ __forceinline__ float silu(float g) {
-  return g / (1.0f + __expf(-g));
+  // The hardware reciprocal (1 ulp) in place of an IEEE divide: the product
+  // is rounded to bf16 right after.
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer loads: a uniform base (SGPRs) plus a 32-bit per-lane byte offset,
+// so that a wavefront's many loads share one address register.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// 16 bytes at byte offset voff + soff.  NT: read once, non-temporal.
+template <bool NT>
+__device__ __forceinline__ uint4 buf_ld(Rsrc r, uint32_t voff, uint32_t soff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, NT ? 2 : 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// A value that is the same in every lane, made known to be so (kept in a
+// scalar register).
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint32_t uniform(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
 }
 
 __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {

@@ -47,29 +47,6 @@ constexpr int kStreamThreads = 1024;               // 16 wavefronts: one workgro
 constexpr int kStreamWaves = kStreamThreads / kWave;
 constexpr int kMaskWords = kDecodeMaxTokens / 32;
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer loads: a uniform base (SGPRs) plus a 32-bit per-lane byte offset,
-// so that a wavefront's many loads share one address register.
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-
-// 16 bytes at byte offset voff + soff.  NT: read once, non-temporal.
-template <bool NT>
-__device__ __forceinline__ uint4 buf_ld(Rsrc r, uint32_t voff, uint32_t soff) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, NT ? 2 : 0);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-// A value that is the same in every lane, made known to be so (kept in a
-// scalar register).
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ __forceinline__ uint32_t uniform(uint32_t v) {
-  return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
-}
-
 // Byte offset of the first K-step fragment of row block b of expert e.
 template <bool GATEUP>
 __device__ __forceinline__ uint32_t block_bytes(int e, int b) {

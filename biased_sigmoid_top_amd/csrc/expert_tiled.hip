@@ -34,150 +34,226 @@ namespace lfm {
 
 namespace {
 
-constexpr int kTileThreads = 256;
+constexpr int kTileThreads = 256;         // four wavefronts
 constexpr int kBM = 128;                  // grouped rows per tile
-constexpr int kBlocksPerTile = 8;         // packed 32-row blocks per tile (256 weight rows)
 constexpr int kKS = 2;                    // 16-wide K steps per stage
 constexpr int kBK = 16 * kKS;             // K per stage
 constexpr int kWSlots = 4;                // weight register ring: three stages ahead
-constexpr int kChunks = kBM * (kBK / 8) / kTileThreads;  // 16-byte token pieces per thread per stage
+constexpr int kPairBytes = 2 * kBK * 2;   // token bytes per row per stage pair: one 128-byte line
+constexpr int kChunks = kBM * (kPairBytes / 16) / kTileThreads;  // 16-byte token pieces per thread per pair
+constexpr int kXcds = 8;
 
+// LDS position of a token piece: 16-byte chunk c (0..7) of row r's line for a
+// stage pair goes to stage c / 4, K step (c / 2) % 2, K half c % 2 of that
+// step's fragment, at fragment lane (c % 2) * 32 + (r % 32 ^ swz(c)).  The XOR
+// keeps both the stores (eight chunks of one row, or of two rows, at once)
+// and the MFMA operand reads (32 rows of one K half) free of bank conflicts.
+__device__ __forceinline__ int swz(int c) { return c + 8 * (c & 1); }
+
+// FB: packed 32-row blocks per wavefront; OCC: workgroups per CU.
 template <bool GATEUP>
 struct TileShape {
+  static constexpr int FB = GATEUP ? 3 : 4;
+  static constexpr int OCC = 1;
   static constexpr int K = GATEUP ? kHidden : kFF;
   static constexpr int kSteps = GATEUP ? kGateupSteps : kDownSteps;
   static constexpr int kBlocks = GATEUP ? kGateupBlocks : kDownBlocks;
-  static constexpr int kColTiles = kBlocks / kBlocksPerTile;  // 12 or 8
-  static constexpr int kColSlots = GATEUP ? 16 : 8;           // multiple of the XCD count
+  static constexpr int kBlocksPerTile = 4 * FB;
+  static constexpr int kColTiles = kBlocks / kBlocksPerTile;
+  // m-tiles per launch group: a group holds a multiple of kXcds tiles.
+  static constexpr int kGroup = kXcds / (kColTiles % kXcds == 0 ? kXcds : kColTiles % 4 == 0 ? 4 : kColTiles % 2 == 0 ? 2 : 1) ;
   static constexpr int kStages = K / kBK;
+  static_assert(kBlocks % kBlocksPerTile == 0, "column tiles cover the weight rows");
+  static_assert(kGroup * kColTiles % kXcds == 0, "a launch group deals evenly over the XCDs");
 };
 
 template <bool GATEUP>
-__global__ __launch_bounds__(kTileThreads, 2) void expert_tiled_kernel(
+__global__ __launch_bounds__(kTileThreads, TileShape<GATEUP>::OCC) void expert_tiled_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Wp,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ row2slot,
     uint16_t* __restrict__ H, float* __restrict__ Y) {
   using T = TileShape<GATEUP>;
+  constexpr int FB = T::FB;
   static_assert(T::kStages % kWSlots == 0, "the stage loop is unrolled by the ring size");
-  __shared__ uint4 tok[2][4 * kKS][kWave];  // 2 stages x (4 token blocks x kKS steps) fragments
+  // Token fragments: 2 pair buffers x (2 stages x 4 token blocks x kKS steps).
+  __shared__ uint4 tok[2][2 * 4 * kKS * kWave];
 
-  const int nb = blockIdx.x % T::kColSlots;
-  if (nb >= T::kColTiles) return;
+  // Launch groups of kGroup m-tiles x kColTiles column tiles; workgroup ids
+  // are dealt to the XCDs round-robin, so id w of a group runs on XCD w % 8.
+  // Tile t = c * kGroup + m of the group (column tile c, m-tile m) goes to
+  // XCD t / (tiles per XCD): each XCD takes a run of consecutive tiles, so a
+  // column tile, read by every m-tile of its expert, stays on one or two
+  // XCDs and is shared through their L2.
+  constexpr int kPerXcd = T::kGroup * T::kColTiles / kXcds;
+  const int w = blockIdx.x % (T::kGroup * T::kColTiles);
+  const int t = (w % kXcds) * kPerXcd + w / kXcds;
+  const int nb = t / T::kGroup;
+  const int mt = blockIdx.x / (T::kGroup * T::kColTiles) * T::kGroup + t % T::kGroup;
   MTile tile;
-  if (!map_mtile(offsets, blockIdx.x / T::kColSlots, kBM, tile)) return;
+  if (!map_mtile(offsets, mt, kBM, tile)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
 
-  // Token pieces of this thread: piece q = tid + 256 i is row q / 4, 16-byte
-  // chunk q % 4 of the stage's 64 bytes; in LDS it is lane (c % 2) * 32 +
-  // row % 32 of fragment (row / 32, c / 2).
+  // Token pieces of this thread: row r0 + 32 i (i < 4) of the tile, 16-byte
+  // chunk c of the row's 128-byte line of a stage pair; eight consecutive
+  // lanes read one whole line.  All four pieces share c and r0 % 32, so their
+  // LDS positions differ by whole token-block fragments.
+  const int r0 = tid / 8, c = tid % 8;
   const uint16_t* arow[kChunks];
-  int lds_f[kChunks], lds_l[kChunks];
 #pragma unroll
   for (int i = 0; i < kChunks; ++i) {
-    const int q = tid + kTileThreads * i, r = q / 4, c = q % 4;
+    const int r = r0 + 32 * i;
     const int slot = row2slot[tile.row_begin + (r < tile.rows ? r : 0)];
     arow[i] = A + static_cast<size_t>(GATEUP ? slot / kTopK : slot) * T::K + c * 8;
-    lds_f[i] = (r / 32) * kKS + c / 2;
-    lds_l[i] = (c % 2) * 32 + r % 32;
   }
-  // This wavefront's two packed row blocks; K steps of a block are contiguous.
-  const uint16_t* wblk = Wp + (static_cast<size_t>(tile.expert) * T::kBlocks + nb * kBlocksPerTile +
-                               wave * 2) * T::kSteps * (kFragBytes / 2) + lane * 8;
-  constexpr size_t kBlockElems = static_cast<size_t>(T::kSteps) * (kFragBytes / 2);
-
-  uint4 wring[kWSlots][2][kKS];
-  // Stages past the end reload the last stage (in bounds, never used).
-  auto load_w = [&](int s, uint4 (&w)[2][kKS]) {
-    const int sc = s < T::kStages ? s : T::kStages - 1;
+  const int st_pos = ((c / 4) * 4 * kKS + (c / 2) % 2) * kWave + (c % 2) * 32 + ((r0 % 32) ^ swz(c));
+  // MFMA operand position of this lane for stage sp of a pair, K step j.
+  int rd_pos[2][kKS];
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+  for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+    for (int j = 0; j < kKS; ++j)
+      rd_pos[sp][j] = (sp * 4 * kKS + j) * kWave + (lane & 32) + ((lane & 31) ^ swz(sp * 4 + j * 2 + lane / 32));
+
+  // This wavefront's FB packed row blocks, K steps of a block contiguous,
+  // read as buffer loads: the expert's packed matrix (12 MB at most) is the
+  // buffer, the wavefront's first block a scalar offset, the lane's 16 bytes
+  // of a fragment the only per-lane offset.
+  constexpr uint32_t kBlockBytes = static_cast<uint32_t>(T::kSteps) * kFragBytes;
+  const Rsrc wr = make_rsrc(Wp + static_cast<size_t>(uniform(tile.expert)) * T::kBlocks * (kBlockBytes / 2),
+                            T::kBlocks * kBlockBytes);
+  const uint32_t wbase = uniform(static_cast<uint32_t>((nb * T::kBlocksPerTile + wave * FB) * kBlockBytes));
+  const uint32_t wlane = lane * 16;
+
+  uint4 wring[kWSlots][FB][kKS];
+  // Stages past the end reload the last stage (in bounds, never used).
+  auto load_w = [&](int s, uint4 (&wv)[FB][kKS]) {
+    const uint32_t sc = s < T::kStages ? s : T::kStages - 1;
+#pragma unroll
+    for (int f = 0; f < FB; ++f)
 #pragma unroll
       for (int j = 0; j < kKS; ++j)
-        w[f][j] = ld16(wblk + f * kBlockElems + static_cast<size_t>(sc * kKS + j) * (kFragBytes / 2));
+        wv[f][j] = buf_ld<false>(wr, wlane, wbase + f * kBlockBytes + (sc * kKS + j) * kFragBytes);
   };
-  uint4 stg[2][kChunks];
-  auto load_x = [&](int s, uint4 (&g)[kChunks]) {
-    const int sc = s < T::kStages ? s : T::kStages - 1;
+  constexpr int kPairs = T::kStages / 2;
+  uint4 stg[kChunks];
+  auto load_x = [&](int pair) {
+    const int pc = pair < kPairs ? pair : kPairs - 1;
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) g[i] = ld16(arow[i] + sc * kBK);
+    for (int i = 0; i < kChunks; ++i) stg[i] = ld16(arow[i] + pc * (kPairBytes / 2));
   };
-  auto store_x = [&](int buf, const uint4 (&g)[kChunks]) {
+  auto store_x = [&](int pb) {
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) tok[buf][lds_f[i]][lds_l[i]] = g[i];
+    for (int i = 0; i < kChunks; ++i) tok[pb][st_pos + i * kKS * kWave] = stg[i];
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[4][FB];
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+    for (int f = 0; f < FB; ++f)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[tb][f][r] = 0.f;
 
 #pragma unroll
   for (int s = 0; s < kWSlots - 1; ++s) load_w(s, wring[s]);
-  {
-    uint4 g0[kChunks];
-    load_x(0, g0);
-    store_x(0, g0);
-  }
-  load_x(1, stg[0]);
-  load_x(2, stg[1]);
+  load_x(0);
+  store_x(0);
+  load_x(1);
   __syncthreads();
 
-  // Stage s: multiplies LDS buffer s % 2 with ring slot s % 4, loads the
-  // weights of stage s + 3 into the free slot, stores the tokens of stage
-  // s + 1 (loaded two stages ago, in g) into the other buffer and loads
-  // those of stage s + 3 into g.
-  auto stage = [&](int s, int buf, uint4 (&wc)[2][kKS], uint4 (&wn)[2][kKS], uint4 (&g)[kChunks]) {
+  // Token operands, double-buffered: tk[x] holds the four token-block
+  // fragments of one K step.
+  uint4 tk[2][4];
+  auto read_tk = [&](int pb, int sp, int j, uint4 (&d)[4]) {
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) d[tb] = tok[pb][rd_pos[sp][j] + tb * kKS * kWave];
+  };
+  auto mma = [&](const uint4 (&wj)[FB][kKS], int j, const uint4 (&d)[4]) {
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int f = 0; f < FB; ++f) acc[tb][f] = mfma32(wj[f][j], d[tb], acc[tb][f]);
+  };
+  // The fences keep the issue order written here, which the wait counts
+  // below rely on: weight loads, then the next LDS operands, then MFMAs.
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  read_tk(0, 0, 0, tk[0]);
+
+  // Stage s of pair p (LDS buffer pb = p % 2) multiplies with ring slot
+  // s % 4 and loads the weights of stage s + 3 into the free slot; the LDS
+  // operands of each K step are read one step ahead.  The first stage of a
+  // pair stores the next pair's tokens (loaded one pair ago) into the other
+  // buffer, whose last readers passed the previous barrier, and loads the
+  // pair after that.  The second stage's barrier comes once its own LDS
+  // reads are done, before its last MFMAs: it publishes the stored tokens
+  // and frees buffer pb for the next store.
+  auto stage = [&](int s, int sp, int pb, uint4 (&wc)[FB][kKS], uint4 (&wn)[FB][kKS]) {
+    static_assert(kKS == 2, "two K steps per stage");
     load_w(s + kWSlots - 1, wn);
-#pragma unroll
-    for (int j = 0; j < kKS; ++j) {
-      uint4 t[4];
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) t[tb] = tok[buf][tb * kKS + j][lane];
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int f = 0; f < 2; ++f) acc[tb][f] = mfma32(wc[f][j], t[tb], acc[tb][f]);
+    read_tk(pb, sp, 1, tk[1]);
+    fence();
+    mma(wc, 0, tk[0]);
+    fence();
+    if (sp == 0) {
+      read_tk(pb, 1, 0, tk[0]);
+      fence();
+      mma(wc, 1, tk[1]);
+      fence();
+      store_x(pb ^ 1);
+      load_x(s / 2 + 2);
+      fence();
+    } else {
+      __syncthreads();
+      read_tk(pb ^ 1, 0, 0, tk[0]);
+      fence();
+      mma(wc, 1, tk[1]);
+      fence();
     }
-    store_x(buf ^ 1, g);
-    load_x(s + 3, g);
-    __syncthreads();
   };
   for (int s = 0; s < T::kStages; s += kWSlots) {
 #pragma unroll
     for (int q = 0; q < kWSlots; ++q)
-      stage(s + q, q % 2, wring[q], wring[(q + kWSlots - 1) % kWSlots], stg[q % 2]);
+      stage(s + q, q % 2, q / 2, wring[q], wring[(q + kWSlots - 1) % kWSlots]);
   }
 
+  // An MFMA result read by a VALU instruction needs wait states after the
+  // MFMA; the accumulator reads below are asm, so give them here: 24 wait
+  // states after the last MFMA of the loop, more than any MFMA needs.
+  if (GATEUP) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+
   // acc[tb][f]: token row tb*32 + lane % 32 of the tile; rows
-  // mfma32_row(r, lane) of packed block nb*8 + wave*2 + f.
+  // mfma32_row(r, lane) of packed block nb * kBlocksPerTile + wave * FB + f.
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
     const int row = tb * 32 + lane % 32;
     if (row >= tile.rows) continue;
     const int slot = row2slot[tile.row_begin + row];
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      const int blk = nb * kBlocksPerTile + wave * 2 + f;
+    for (int f = 0; f < FB; ++f) {
+      const int blk = nb * T::kBlocksPerTile + wave * FB + f;
       if (GATEUP) {
         // Values r < 8 are gate rows, r + 8 the up rows of the same H column.
         uint16_t* dst = H + static_cast<size_t>(slot) * kFF + blk * 16 + 4 * (lane / 32);
+        // Explicit accumulator reads: the tiles stay in AGPRs through the
+        // loop instead of the allocator moving some to arch VGPRs for the
+        // SiLU and spilling there.
+        float v[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[r]) : "a"(acc[tb][f][r]));
 #pragma unroll
         for (int g8 = 0; g8 < 2; ++g8) {
           uint32_t p[2];
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const int r = g8 * 4 + h * 2;
-            p[h] = static_cast<uint32_t>(f32_to_bf16(silu(acc[tb][f][r]) * acc[tb][f][r + 8])) |
-                   (static_cast<uint32_t>(f32_to_bf16(silu(acc[tb][f][r + 1]) * acc[tb][f][r + 9])) << 16);
+            p[h] = pack_bf16x2(silu(v[r]) * v[r + 8], silu(v[r + 1]) * v[r + 9]);
           }
           *reinterpret_cast<uint2*>(dst + g8 * 8) = make_uint2(p[0], p[1]);
         }
+        fence();  // one tile at a time: bounds the registers the SiLU needs
       } else {
         float* dst = Y + static_cast<size_t>(slot) * kHidden + blk * 32 + 4 * (lane / 32);
 #pragma unroll
@@ -190,22 +266,27 @@ __global__ __launch_bounds__(kTileThreads, 2) void expert_tiled_kernel(
   }
 }
 
+template <bool GATEUP>
+int64_t tiled_grid(int64_t N) {
+  using T = TileShape<GATEUP>;
+  const int64_t groups = (max_mtiles(N, kBM) + T::kGroup - 1) / T::kGroup;
+  return groups * T::kGroup * T::kColTiles;
+}
+
 }  // namespace
 
 hipError_t launch_gateup_tiled(const uint16_t* X, const uint16_t* Wgu, const int32_t* offsets,
                                const int32_t* row2slot, uint16_t* H, int64_t N,
                                hipStream_t stream) {
-  const int64_t grid = max_mtiles(N, kBM) * TileShape<true>::kColSlots;
-  hipLaunchKernelGGL(expert_tiled_kernel<true>, dim3(grid), dim3(kTileThreads), 0, stream, X, Wgu,
-                     offsets, row2slot, H, nullptr);
+  hipLaunchKernelGGL(expert_tiled_kernel<true>, dim3(tiled_grid<true>(N)), dim3(kTileThreads), 0,
+                     stream, X, Wgu, offsets, row2slot, H, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_down_tiled(const uint16_t* H, const uint16_t* Wd, const int32_t* offsets,
                              const int32_t* row2slot, float* Y, int64_t N, hipStream_t stream) {
-  const int64_t grid = max_mtiles(N, kBM) * TileShape<false>::kColSlots;
-  hipLaunchKernelGGL(expert_tiled_kernel<false>, dim3(grid), dim3(kTileThreads), 0, stream, H, Wd,
-                     offsets, row2slot, nullptr, Y);
+  hipLaunchKernelGGL(expert_tiled_kernel<false>, dim3(tiled_grid<false>(N)), dim3(kTileThreads), 0,
+                     stream, H, Wd, offsets, row2slot, nullptr, Y);
   return hipGetLastError();
 }
 
