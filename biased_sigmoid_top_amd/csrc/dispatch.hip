@@ -23,6 +23,8 @@ namespace {
 constexpr int kDispatchThreads = 1024;             // one token per thread
 constexpr int kMaskWords = kDispatchThreads / 32;  // token bitmask per expert
 constexpr int kRowGroups = kDispatchThreads / 16;  // 64 groups x 16 lanes of 4 experts
+static_assert(kMaskWords == 32 && kDispatchThreads / kWave * 4 == kExperts,
+              "the word prefix scan gives each wavefront four experts of 32 words");
 
 __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ blockcounts, int route_tokens,
@@ -32,6 +34,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(
   __shared__ int s_excl[kExperts];
   __shared__ int s_base[kExperts];
   __shared__ uint32_t mask[kExperts][kMaskWords];
+  __shared__ int word_base[kExperts][kMaskWords];  // tokens of e in earlier mask words
 
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * kDispatchThreads;
@@ -86,12 +89,31 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(
   }
   __syncthreads();
 
+  // Exclusive prefix of the mask words' popcounts, per expert: wavefront w
+  // scans experts 4w .. 4w + 3, two at a time, one 32-lane half each.
+  {
+    const int lane = tid & (kWave - 1);
+    const int word = lane & 31;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int e = 4 * (tid / kWave) + 2 * it + lane / 32;
+      const int c = __popc(mask[e][word]);
+      int incl = c;
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) {
+        const int o = __shfl_up(incl, off, 32);
+        if (word >= off) incl += o;
+      }
+      word_base[e][word] = incl - c;
+    }
+  }
+  __syncthreads();
+
   if (t < N) {
 #pragma unroll
     for (int j = 0; j < kTopK; ++j) {
       const int e = my_e[j];
-      int rank = __popc(mask[e][tid / 32] & ((1u << (tid % 32)) - 1u));
-      for (int wd = 0; wd < tid / 32; ++wd) rank += __popc(mask[e][wd]);
+      const int rank = word_base[e][tid / 32] + __popc(mask[e][tid / 32] & ((1u << (tid % 32)) - 1u));
       row2slot[s_excl[e] + s_base[e] + rank] = t * kTopK + j;
     }
   }

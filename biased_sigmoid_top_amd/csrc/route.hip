@@ -9,13 +9,23 @@
 // activation takes part in the selection only, weights from the unbiased
 // scores, normalised with an epsilon, routed scale 1.
 //
-// Two kernels.  route_partial: one wavefront per (16-token tile, 128-wide K
-// slice) multiplies the 16 token rows by all 64 router rows over its slice
-// and stores the 16 x 64 fp32 partial tile; with N = 64 that is 64
-// wavefronts on 64 CUs, so the router matrix is pulled through many CUs at
-// once (one CU alone reads it too slowly).  route_select: one wavefront per
-// token adds the 16 partials of each logit in a fixed order, applies the
-// sigmoid and the bias, takes the top 4 and normalises the weights.
+// Two forms, the same arithmetic.  Every 16-token tile is split into 16
+// K slices of 128; a wavefront multiplies the tile's 16 token rows by all 64
+// router rows over one slice (16 MFMAs) into a 16 x 64 fp32 partial.  A
+// wavefront per token then adds the 16 partials of each logit in slice
+// order, applies the sigmoid and the bias, takes the top 4 and normalises
+// the weights.
+//  * Split (up to 2048 tokens): route_partial runs one wavefront per (tile,
+//    slice) and stores the partials to the workspace, route_select reduces
+//    them.  With N = 64 that is 64 wavefronts on 64 CUs, so the router
+//    matrix is pulled through many CUs at once.
+//  * Fused (above 2048 tokens): one 16-wavefront workgroup per tile, the
+//    partials staged in LDS -- one launch, no scratch traffic.  Each tile's
+//    CU then reads the whole 256 KB router matrix, which costs about 12 us
+//    however few tiles run (the rate at which one CU's misses are served),
+//    so it pays only once the split form's partial traffic is larger.
+//    Measured per call: N = 1024 split 9.2 us, fused 11.9; N = 4096 split
+//    18.6, fused 12.3.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -24,8 +34,12 @@ namespace lfm {
 namespace {
 
 constexpr int kRouteTokens = 16;
-constexpr int kSlices = kHidden / 128;              // 16 K slices
+constexpr int kSlices = kHidden / 128;                // 16 K slices
 constexpr int kSelectThreads = kRouteTokens * kWave;  // one wavefront per token
+constexpr int kFusedThreads = kSlices * kWave;        // one wavefront per slice
+constexpr int kPartStride = kExperts + 4;             // LDS row pitch: conflict-free partial stores
+constexpr int64_t kSplitMaxTokens = 2048;
+static_assert(kSlices == kRouteTokens, "the fused kernel's wavefronts serve as slices, then tokens");
 
 // Orders floats like their values as unsigned integers.
 __device__ __forceinline__ uint32_t orderable(float f) {
@@ -42,13 +56,11 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
-// part layout: [token tile][slice][16 tokens][64 experts] fp32.
-__global__ __launch_bounds__(kWave) void route_partial_kernel(const uint16_t* __restrict__ X,
-                                                              const uint16_t* __restrict__ Wr,
-                                                              float* __restrict__ part, int N) {
-  const int lane = threadIdx.x;
-  const int tile = blockIdx.x / kSlices;
-  const int slice = blockIdx.x % kSlices;
+// Partial logits of token tile `tile` over K slice `slice`.  acc[et][r] of
+// a lane is expert et*16 + lane % 16, token 4 * (lane / 16) + r of the tile.
+__device__ __forceinline__ void slice_partial(const uint16_t* __restrict__ X,
+                                              const uint16_t* __restrict__ Wr, int tile, int slice,
+                                              int N, int lane, f32x4 (&acc)[4]) {
   const int r16 = lane & 15;
   const int g = lane >> 4;
   int tok = tile * kRouteTokens + r16;
@@ -66,35 +78,20 @@ __global__ __launch_bounds__(kWave) void route_partial_kernel(const uint16_t* __
   }
   // Keep every load above this point: one memory round trip.
   __builtin_amdgcn_sched_barrier(0);
-  f32x4 acc[4] = {};
+#pragma unroll
+  for (int et = 0; et < 4; ++et) acc[et] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int et = 0; et < 4; ++et) acc[et] = mfma16(a[i], b[et][i], acc[et]);
-  // Accumulator of lane: expert et*16 + r16, tokens 4g + r.
-  float* dst = part + static_cast<size_t>(blockIdx.x) * kRouteTokens * kExperts;
-#pragma unroll
-  for (int et = 0; et < 4; ++et)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) dst[(4 * g + r) * kExperts + et * 16 + r16] = acc[et][r];
 }
 
-__global__ __launch_bounds__(kSelectThreads) void route_select_kernel(
-    const float* __restrict__ part, const float* __restrict__ bias, int32_t* __restrict__ idx_out,
-    float* __restrict__ w_out, int32_t* __restrict__ blockcounts, int N) {
-  __shared__ int wave_counts[kRouteTokens][kExperts];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int t = threadIdx.x / kWave;  // token of this wavefront within the tile
-  const int tg = blockIdx.x * kRouteTokens + t;
-  const float* src = part + static_cast<size_t>(blockIdx.x) * kSlices * kRouteTokens * kExperts +
-                     t * kExperts + lane;
-  const float b_e = bias[lane];
-  float p[kSlices];
-#pragma unroll
-  for (int s = 0; s < kSlices; ++s) p[s] = src[s * kRouteTokens * kExperts];
-  float l = 0.0f;
-#pragma unroll
-  for (int s = 0; s < kSlices; ++s) l += p[s];
+// Selection for one token on one wavefront (lane = expert), from the logit
+// l of the lane's expert.  Writes the token's 4 experts and weights when tg
+// is a real token; returns whether the lane's expert was selected.
+__device__ __forceinline__ bool select_token(float l, float b_e, int lane, int tg, int N,
+                                             int32_t* __restrict__ idx_out,
+                                             float* __restrict__ w_out) {
   const float s_e = 1.0f / (1.0f + expf(-l));
   const float c_e = s_e + b_e;
   const uint32_t key = orderable(c_e);
@@ -113,8 +110,7 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(
     sel_s[j] = __shfl(s_e, win, kWave);
     sum += sel_s[j];
   }
-  const bool valid = tg < N;
-  if (valid && lane < kTopK) {
+  if (tg < N && lane < kTopK) {
     int e_out = sel[0];
     float s_out = sel_s[0];
 #pragma unroll
@@ -123,16 +119,77 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(
     idx_out[static_cast<size_t>(tg) * kTopK + lane] = e_out;
     w_out[static_cast<size_t>(tg) * kTopK + lane] = s_out / (sum + kRouterEps);
   }
-  if (blockcounts != nullptr) {
-    wave_counts[t][lane] = (valid && taken) ? 1 : 0;
-    __syncthreads();
-    if (t == 0) {
-      int c = 0;
+  return tg < N && taken;
+}
+
+// Per-tile expert histogram: counts[t][lane] holds whether token t chose the
+// lane's expert; wavefront 0 adds them up after the barrier.
+__device__ __forceinline__ void store_histogram(int (&counts)[kRouteTokens][kExperts], int t, int lane,
+                                                bool chosen, int32_t* __restrict__ blockcounts) {
+  counts[t][lane] = chosen ? 1 : 0;
+  __syncthreads();
+  if (t == 0) {
+    int c = 0;
 #pragma unroll
-      for (int w = 0; w < kRouteTokens; ++w) c += wave_counts[w][lane];
-      blockcounts[static_cast<size_t>(blockIdx.x) * kExperts + lane] = c;
-    }
+    for (int w = 0; w < kRouteTokens; ++w) c += counts[w][lane];
+    blockcounts[static_cast<size_t>(blockIdx.x) * kExperts + lane] = c;
   }
+}
+
+// part layout: [token tile][slice][16 tokens][64 experts] fp32.
+__global__ __launch_bounds__(kWave) void route_partial_kernel(const uint16_t* __restrict__ X,
+                                                              const uint16_t* __restrict__ Wr,
+                                                              float* __restrict__ part, int N) {
+  const int lane = threadIdx.x;
+  f32x4 acc[4];
+  slice_partial(X, Wr, blockIdx.x / kSlices, blockIdx.x % kSlices, N, lane, acc);
+  float* dst = part + static_cast<size_t>(blockIdx.x) * kRouteTokens * kExperts;
+#pragma unroll
+  for (int et = 0; et < 4; ++et)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[(4 * (lane >> 4) + r) * kExperts + et * 16 + (lane & 15)] = acc[et][r];
+}
+
+__global__ __launch_bounds__(kSelectThreads) void route_select_kernel(
+    const float* __restrict__ part, const float* __restrict__ bias, int32_t* __restrict__ idx_out,
+    float* __restrict__ w_out, int32_t* __restrict__ blockcounts, int N) {
+  __shared__ int counts[kRouteTokens][kExperts];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = threadIdx.x / kWave;  // token of this wavefront within the tile
+  const float* src = part + static_cast<size_t>(blockIdx.x) * kSlices * kRouteTokens * kExperts +
+                     t * kExperts + lane;
+  float p[kSlices];
+#pragma unroll
+  for (int s = 0; s < kSlices; ++s) p[s] = src[s * kRouteTokens * kExperts];
+  float l = 0.0f;
+#pragma unroll
+  for (int s = 0; s < kSlices; ++s) l += p[s];
+  const bool chosen = select_token(l, bias[lane], lane, blockIdx.x * kRouteTokens + t, N, idx_out, w_out);
+  if (blockcounts != nullptr) store_histogram(counts, t, lane, chosen, blockcounts);
+}
+
+__global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wr, const float* __restrict__ bias,
+    int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ blockcounts, int N) {
+  __shared__ float part[kSlices][kRouteTokens][kPartStride];
+  __shared__ int counts[kRouteTokens][kExperts];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  {
+    f32x4 acc[4];
+    slice_partial(X, Wr, blockIdx.x, wave, N, lane, acc);
+#pragma unroll
+    for (int et = 0; et < 4; ++et)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[wave][4 * (lane >> 4) + r][et * 16 + (lane & 15)] = acc[et][r];
+  }
+  __syncthreads();
+  const int t = wave;  // now: the token of this wavefront within the tile
+  float l = 0.0f;
+#pragma unroll
+  for (int s = 0; s < kSlices; ++s) l += part[s][t][lane];
+  const bool chosen = select_token(l, bias[lane], lane, blockIdx.x * kRouteTokens + t, N, idx_out, w_out);
+  if (blockcounts != nullptr) store_histogram(counts, t, lane, chosen, blockcounts);
 }
 
 }  // namespace
@@ -140,6 +197,7 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(
 int route_block_tokens(int64_t) { return kRouteTokens; }
 
 size_t route_partial_bytes(int64_t N) {
+  if (N > kSplitMaxTokens) return 0;  // the fused router keeps its partials in LDS
   const size_t tiles = static_cast<size_t>((N + kRouteTokens - 1) / kRouteTokens);
   return tiles * kSlices * kRouteTokens * kExperts * sizeof(float);
 }
@@ -147,6 +205,11 @@ size_t route_partial_bytes(int64_t N) {
 hipError_t launch_route(const uint16_t* X, const uint16_t* Wr, const float* bias, int32_t* idx,
                         float* w, int32_t* blockcounts, float* part, int N, hipStream_t stream) {
   const int tiles = (N + kRouteTokens - 1) / kRouteTokens;
+  if (N > kSplitMaxTokens) {
+    hipLaunchKernelGGL(route_fused_kernel, dim3(tiles), dim3(kFusedThreads), 0, stream, X, Wr, bias,
+                       idx, w, blockcounts, N);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(route_partial_kernel, dim3(tiles * kSlices), dim3(kWave), 0, stream, X, Wr,
                      part, N);
   hipError_t e = hipGetLastError();

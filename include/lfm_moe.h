@@ -152,7 +152,8 @@ typedef enum {
   LFM_MOE_WS_H = 5,         /* [4N, 1536] bf16 expert hidden rows, slot order (row t*4 + j) */
   LFM_MOE_WS_Y = 6,         /* [4N, 2048] fp32 expert output rows, slot order (row t*4 + j) */
   LFM_MOE_WS_X = 7,         /* [N, 2048] bf16 normalised input (block forward only) */
-  LFM_MOE_WS_ROUTER_PARTIAL = 8, /* [ceil(N/16), 16, 16, 64] fp32 router partial logits per K slice */
+  LFM_MOE_WS_ROUTER_PARTIAL = 8, /* [ceil(N/16), 16, 16, 64] fp32 router partial logits per K slice;
+                                    empty above 2048 tokens, where the router keeps them in LDS */
   LFM_MOE_WS_REGIONS = 9
 } lfm_moe_ws_region;
 

@@ -40,12 +40,16 @@ def test_workspace_layout(lib):
         offs = [lib.lfm_moe_workspace_offset(N, r) for r in range(9)]
         assert offs[0] == 0
         assert all(o % 256 == 0 for o in offs)
-        assert offs == sorted(offs) and offs[-1] < total
+        assert offs == sorted(offs) and offs[-1] <= total
         # H and Y regions hold 4N rows.
         assert offs[_lib.WS_Y] - offs[_lib.WS_H] >= 4 * N * 1536 * 2
         assert offs[_lib.WS_X] - offs[_lib.WS_Y] >= 4 * N * 2048 * 4
         assert offs[_lib.WS_ROUTER_PARTIAL] - offs[_lib.WS_X] >= N * 2048 * 2
-        assert total - offs[_lib.WS_ROUTER_PARTIAL] >= -(-N // 16) * 16 * 16 * 64 * 4
+        part = total - offs[_lib.WS_ROUTER_PARTIAL]
+        if N <= 2048:
+            assert part >= -(-N // 16) * 16 * 16 * 64 * 4
+        else:
+            assert part == 0  # the fused router keeps its partial logits in LDS
     assert lib.lfm_moe_workspace_bytes(-1) == 0
     assert lib.lfm_moe_workspace_offset(10, 99) == ctypes.c_size_t(-1).value
 
