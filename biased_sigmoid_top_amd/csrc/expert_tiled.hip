@@ -10,23 +10,28 @@
 // deployment").
 //
 // Tile: 128 grouped rows (tokens of one expert) x 256 weight rows, 32x32x16
-// bf16 MFMAs (on gfx950 twice the rate of the 16x16x32 form).  Each of the
-// four wavefronts owns 64 weight rows (two packed row blocks) for all 128
-// tokens: 4 x 2 accumulator tiles.  Because no two wavefronts share weight
-// rows, the weights need no LDS: every wavefront streams its own packed
-// fragments (one contiguous 1 KB load each) straight into its MFMA
-// registers, three K stages ahead.  The token rows, which all four
-// wavefronts share, are gathered from their slots (X row t for gate/up, H
-// row t*4 + j for down) two stages ahead into registers and stored into a
-// double-buffered LDS tile in fragment order, so every LDS access is a
-// contiguous, conflict-free 1 KB wavefront access.  Two workgroups share a
-// CU.  For gate/up the 32 rows of a packed block are 16 gate rows and the
-// matching 16 up rows, so the SiLU product is formed in registers.
+// bf16 MFMAs (on gfx950 twice the rate of the 16x16x32 form), two
+// workgroups per CU.  Each of the four wavefronts owns 64 weight rows (two
+// packed row blocks) for all 128 tokens: 4 x 2 accumulator tiles.  Because
+// no two wavefronts share weight rows, the weights need no LDS: every
+// wavefront streams its own packed fragments (one contiguous 1 KB buffer
+// load each) straight into its MFMA registers, three K stages ahead.  The
+// token rows, which all four wavefronts share, are gathered from their
+// slots (X row t for gate/up, H row t*4 + j for down) as whole 128-byte
+// lines, one per row per pair of K stages, so that no L2 request carries
+// half a line.  They are stored into a double-buffered, XOR-swizzled LDS
+// tile (one barrier per stage pair), and the MFMA operands of each K step
+// are read from it one step ahead.  For gate/up the 32 rows of a packed
+// block are 16 gate rows and the matching 16 up rows, so the SiLU product
+// is formed in registers.
 //
-// Grid: m-tile major, 16 (gate/up, 12 used) or 8 (down) column slots per
-// m-tile.  Workgroup ids are dealt to the 8 XCDs round-robin, so the
-// m-tiles of one expert that use the same weight block sit on one XCD and
-// start together, and share the block through that XCD's L2.
+// Grid: workgroup ids are dealt to the 8 XCDs round-robin.  Tiles are
+// launched in groups of m-tiles x column tiles that hold a multiple of 8
+// tiles, each XCD taking a run of consecutive (column-major) tiles of the
+// group: every XCD gets the same share, and a column tile -- read by every
+// m-tile of its expert -- stays on one XCD (down: 8 column tiles) or two
+// (gate/up: 12 column tiles over groups of two m-tiles) and is shared
+// through their L2.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -50,25 +55,26 @@ constexpr int kXcds = 8;
 // and the MFMA operand reads (32 rows of one K half) free of bank conflicts.
 __device__ __forceinline__ int swz(int c) { return c + 8 * (c & 1); }
 
-// FB: packed 32-row blocks per wavefront; OCC: workgroups per CU.
+constexpr int kTilesPerCu = 2;  // occupancy the register budget is set for
+
 template <bool GATEUP>
 struct TileShape {
-  static constexpr int FB = GATEUP ? 3 : 4;
-  static constexpr int OCC = 1;
+  static constexpr int FB = 2;  // packed 32-row blocks per wavefront
   static constexpr int K = GATEUP ? kHidden : kFF;
   static constexpr int kSteps = GATEUP ? kGateupSteps : kDownSteps;
   static constexpr int kBlocks = GATEUP ? kGateupBlocks : kDownBlocks;
   static constexpr int kBlocksPerTile = 4 * FB;
   static constexpr int kColTiles = kBlocks / kBlocksPerTile;
   // m-tiles per launch group: a group holds a multiple of kXcds tiles.
-  static constexpr int kGroup = kXcds / (kColTiles % kXcds == 0 ? kXcds : kColTiles % 4 == 0 ? 4 : kColTiles % 2 == 0 ? 2 : 1) ;
+  static constexpr int kGroup =
+      kXcds / (kColTiles % kXcds == 0 ? kXcds : kColTiles % 4 == 0 ? 4 : kColTiles % 2 == 0 ? 2 : 1);
   static constexpr int kStages = K / kBK;
   static_assert(kBlocks % kBlocksPerTile == 0, "column tiles cover the weight rows");
   static_assert(kGroup * kColTiles % kXcds == 0, "a launch group deals evenly over the XCDs");
 };
 
 template <bool GATEUP>
-__global__ __launch_bounds__(kTileThreads, TileShape<GATEUP>::OCC) void expert_tiled_kernel(
+__global__ __launch_bounds__(kTileThreads, kTilesPerCu) void expert_tiled_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Wp,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ row2slot,
     uint16_t* __restrict__ H, float* __restrict__ Y) {
@@ -219,11 +225,6 @@ __global__ __launch_bounds__(kTileThreads, TileShape<GATEUP>::OCC) void expert_t
       stage(s + q, q % 2, q / 2, wring[q], wring[(q + kWSlots - 1) % kWSlots]);
   }
 
-  // An MFMA result read by a VALU instruction needs wait states after the
-  // MFMA; the accumulator reads below are asm, so give them here: 24 wait
-  // states after the last MFMA of the loop, more than any MFMA needs.
-  if (GATEUP) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
-
   // acc[tb][f]: token row tb*32 + lane % 32 of the tile; rows
   // mfma32_row(r, lane) of packed block nb * kBlocksPerTile + wave * FB + f.
 #pragma unroll
@@ -237,12 +238,7 @@ __global__ __launch_bounds__(kTileThreads, TileShape<GATEUP>::OCC) void expert_t
       if (GATEUP) {
         // Values r < 8 are gate rows, r + 8 the up rows of the same H column.
         uint16_t* dst = H + static_cast<size_t>(slot) * kFF + blk * 16 + 4 * (lane / 32);
-        // Explicit accumulator reads: the tiles stay in AGPRs through the
-        // loop instead of the allocator moving some to arch VGPRs for the
-        // SiLU and spilling there.
-        float v[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[r]) : "a"(acc[tb][f][r]));
+        const f32x16& v = acc[tb][f];
 #pragma unroll
         for (int g8 = 0; g8 < 2; ++g8) {
           uint32_t p[2];
