@@ -39,7 +39,7 @@ void region_sizes(int64_t N, size_t (&sz)[LFM_MOE_WS_REGIONS]) {
   sz[LFM_MOE_WS_OFFSETS] = (kExperts + 1) * sizeof(int32_t);
   sz[LFM_MOE_WS_ROW2SLOT] = rows * sizeof(int32_t);
   sz[LFM_MOE_WS_H] = rows * kFF * sizeof(uint16_t);
-  sz[LFM_MOE_WS_Y] = rows * kHidden * sizeof(uint16_t);
+  sz[LFM_MOE_WS_Y] = rows * kHidden * sizeof(float);
   sz[LFM_MOE_WS_X] = n * kHidden * sizeof(uint16_t);
   sz[LFM_MOE_WS_ROUTER_PARTIAL] = route_partial_bytes(N);
 }
@@ -226,7 +226,7 @@ lfm_moe_status run_layer(const uint16_t* X, const uint16_t* W_r, const float* bi
   int32_t* offsets = region<int32_t>(ws, N, LFM_MOE_WS_OFFSETS);
   int32_t* row2slot = region<int32_t>(ws, N, LFM_MOE_WS_ROW2SLOT);
   uint16_t* H = region<uint16_t>(ws, N, LFM_MOE_WS_H);
-  uint16_t* Y = region<uint16_t>(ws, N, LFM_MOE_WS_Y);
+  float* Y = region<float>(ws, N, LFM_MOE_WS_Y);
   float* part = region<float>(ws, N, LFM_MOE_WS_ROUTER_PARTIAL);
   const int n = static_cast<int>(N);
   const bool decode = use_decode_path(N);

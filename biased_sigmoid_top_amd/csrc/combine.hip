@@ -21,28 +21,23 @@ namespace {
 constexpr int kRowThreads = 256;  // one token row of 2048 values per workgroup
 
 // out[t] = (resid[t] +) sum_j w[t, j] * Y[t*4 + j]; resid may alias out.
-// Y rows (bf16) are in slot order, so a token's four rows are contiguous.
-__device__ __forceinline__ float4 bf16x4_to_f32(uint2 v) {
-  return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
-                     __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
-}
-
-__global__ __launch_bounds__(kRowThreads) void combine_kernel(const uint16_t* __restrict__ Y,
+// Y rows are in slot order, so a token's four rows are contiguous.
+__global__ __launch_bounds__(kRowThreads) void combine_kernel(const float* __restrict__ Y,
                                                               const float* __restrict__ w,
                                                               const float* resid, float* out) {
   const size_t t = blockIdx.x;
   const float4 wt = *reinterpret_cast<const float4*>(w + t * kTopK);
-  const uint16_t* y0 = Y + t * kTopK * kHidden;
-  const uint16_t* y1 = y0 + kHidden;
-  const uint16_t* y2 = y1 + kHidden;
-  const uint16_t* y3 = y2 + kHidden;
+  const float* y0 = Y + t * kTopK * kHidden;
+  const float* y1 = y0 + kHidden;
+  const float* y2 = y1 + kHidden;
+  const float* y3 = y2 + kHidden;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int col = (h * kRowThreads + threadIdx.x) * 4;
-    const float4 a = bf16x4_to_f32(*reinterpret_cast<const uint2*>(y0 + col));
-    const float4 b = bf16x4_to_f32(*reinterpret_cast<const uint2*>(y1 + col));
-    const float4 c = bf16x4_to_f32(*reinterpret_cast<const uint2*>(y2 + col));
-    const float4 d = bf16x4_to_f32(*reinterpret_cast<const uint2*>(y3 + col));
+    const float4 a = *reinterpret_cast<const float4*>(y0 + col);
+    const float4 b = *reinterpret_cast<const float4*>(y1 + col);
+    const float4 c = *reinterpret_cast<const float4*>(y2 + col);
+    const float4 d = *reinterpret_cast<const float4*>(y3 + col);
     float4 acc;
     acc.x = fmaf(wt.w, d.x, fmaf(wt.z, c.x, fmaf(wt.y, b.x, wt.x * a.x)));
     acc.y = fmaf(wt.w, d.y, fmaf(wt.z, c.y, fmaf(wt.y, b.y, wt.x * a.y)));
@@ -93,7 +88,7 @@ __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const float* __res
 
 }  // namespace
 
-hipError_t launch_combine(const uint16_t* Y, const float* w, const float* resid, float* out,
+hipError_t launch_combine(const float* Y, const float* w, const float* resid, float* out,
                           int64_t N, hipStream_t stream) {
   hipLaunchKernelGGL(combine_kernel, dim3(N), dim3(kRowThreads), 0, stream, Y, w, resid, out);
   return hipGetLastError();

@@ -5,7 +5,7 @@
 // (flozi.net guide "LFM2.5-24B-A2B: Biased Routing, Short Convolutions and
 // Ten KV Caches", section "The router has two different scores"):
 //   H = silu(X_e W_gate_e^T) * (X_e W_up_e^T)    (bf16 out, fp32 accumulate)
-//   Y = H_e W_down_e^T                           (bf16 out, fp32 accumulate)
+//   Y = H_e W_down_e^T                           (fp32 out)
 // and the expert path groups tokens by expert (section "What to verify in a
 // deployment").
 //
@@ -145,7 +145,7 @@ struct Cursor {
 template <bool GATEUP>
 __device__ __forceinline__ void stream_units(const uint16_t* __restrict__ B,
                                              const uint16_t* __restrict__ Wp,
-                                             uint16_t* __restrict__ H, uint16_t* __restrict__ Y,
+                                             uint16_t* __restrict__ H, float* __restrict__ Y,
                                              int N, StreamShared& S) {
   constexpr int K = GATEUP ? kHidden : kFF;
   constexpr int kS = (GATEUP ? kGateupSteps : kDownSteps) / kStreamWaves;  // 8 or 6
@@ -258,7 +258,7 @@ __device__ __forceinline__ void stream_units(const uint16_t* __restrict__ B,
           float ys = 0.f;
 #pragma unroll
           for (int w = 0; w < kStreamWaves; ++w) ys += S.red[w][r][ln];
-          Y[static_cast<size_t>(slot) * kHidden + b * 32 + mfma32_row(r, ln)] = f32_to_bf16(ys);
+          Y[static_cast<size_t>(slot) * kHidden + b * 32 + mfma32_row(r, ln)] = ys;
         }
       }
       __syncthreads();
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(kStreamThreads) void gateup_decode_kernel(
 
 __global__ __launch_bounds__(kStreamThreads) void down_decode_kernel(
     const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wd,
-    const int32_t* __restrict__ idx, uint16_t* __restrict__ Y, int N) {
+    const int32_t* __restrict__ idx, float* __restrict__ Y, int N) {
   __shared__ StreamShared S;
   group_slots(idx, N, S.G);
   stream_units<false>(H, Wd, nullptr, Y, N, S);
@@ -324,7 +324,7 @@ hipError_t launch_gateup_decode(const uint16_t* X, const uint16_t* Wgu, const in
 }
 
 hipError_t launch_down_decode(const uint16_t* H, const uint16_t* Wd, const int32_t* idx,
-                              uint16_t* Y, int N, hipStream_t stream) {
+                              float* Y, int N, hipStream_t stream) {
   hipLaunchKernelGGL(down_decode_kernel, dim3(cu_count()), dim3(kStreamThreads), 0, stream, H, Wd,
                      idx, Y, N);
   return hipGetLastError();

@@ -5,7 +5,7 @@
 // (flozi.net guide "LFM2.5-24B-A2B: Biased Routing, Short Convolutions and
 // Ten KV Caches", section "The router has two different scores"):
 //   H = silu(X_e W_gate_e^T) * (X_e W_up_e^T)    (bf16 out, fp32 accumulate)
-//   Y = H_e W_down_e^T                           (bf16 out, fp32 accumulate)
+//   Y = H_e W_down_e^T                           (fp32 out)
 // over the tokens grouped by expert (section "What to verify in a
 // deployment").
 //
@@ -77,7 +77,7 @@ template <bool GATEUP>
 __global__ __launch_bounds__(kTileThreads, kTilesPerCu) void expert_tiled_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Wp,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ row2slot,
-    uint16_t* __restrict__ H, uint16_t* __restrict__ Y) {
+    uint16_t* __restrict__ H, float* __restrict__ Y) {
   using T = TileShape<GATEUP>;
   constexpr int FB = T::FB;
   static_assert(T::kStages % kWSlots == 0, "the stage loop is unrolled by the ring size");
@@ -251,12 +251,12 @@ __global__ __launch_bounds__(kTileThreads, kTilesPerCu) void expert_tiled_kernel
         }
         fence();  // one tile at a time: bounds the registers the SiLU needs
       } else {
-        uint16_t* dst = Y + static_cast<size_t>(slot) * kHidden + blk * 32 + 4 * (lane / 32);
+        float* dst = Y + static_cast<size_t>(slot) * kHidden + blk * 32 + 4 * (lane / 32);
 #pragma unroll
         for (int g8 = 0; g8 < 4; ++g8)
-          *reinterpret_cast<uint2*>(dst + g8 * 8) =
-              make_uint2(pack_bf16x2(acc[tb][f][g8 * 4], acc[tb][f][g8 * 4 + 1]),
-                         pack_bf16x2(acc[tb][f][g8 * 4 + 2], acc[tb][f][g8 * 4 + 3]));
+          *reinterpret_cast<float4*>(dst + g8 * 8) =
+              make_float4(acc[tb][f][g8 * 4], acc[tb][f][g8 * 4 + 1], acc[tb][f][g8 * 4 + 2],
+                          acc[tb][f][g8 * 4 + 3]);
       }
     }
   }
@@ -280,7 +280,7 @@ hipError_t launch_gateup_tiled(const uint16_t* X, const uint16_t* Wgu, const int
 }
 
 hipError_t launch_down_tiled(const uint16_t* H, const uint16_t* Wd, const int32_t* offsets,
-                             const int32_t* row2slot, uint16_t* Y, int64_t N, hipStream_t stream) {
+                             const int32_t* row2slot, float* Y, int64_t N, hipStream_t stream) {
   hipLaunchKernelGGL(expert_tiled_kernel<false>, dim3(tiled_grid<false>(N)), dim3(kTileThreads), 0,
                      stream, H, Wd, offsets, row2slot, nullptr, Y);
   return hipGetLastError();

@@ -32,16 +32,16 @@ hipError_t launch_dispatch(const int32_t* idx, const int32_t* blockcounts, int32
 hipError_t launch_gateup_decode(const uint16_t* X, const uint16_t* Wgu, const int32_t* idx,
                                 uint16_t* H, int N, hipStream_t stream);
 hipError_t launch_down_decode(const uint16_t* H, const uint16_t* Wd, const int32_t* idx,
-                              uint16_t* Y, int N, hipStream_t stream);
+                              float* Y, int N, hipStream_t stream);
 
 // Grouped path, LDS-tiled MFMA kernels (prefill-shaped batches).
 hipError_t launch_gateup_tiled(const uint16_t* X, const uint16_t* Wgu, const int32_t* offsets,
                                const int32_t* row2slot, uint16_t* H, int64_t N,
                                hipStream_t stream);
 hipError_t launch_down_tiled(const uint16_t* H, const uint16_t* Wd, const int32_t* offsets,
-                             const int32_t* row2slot, uint16_t* Y, int64_t N, hipStream_t stream);
+                             const int32_t* row2slot, float* Y, int64_t N, hipStream_t stream);
 
-hipError_t launch_combine(const uint16_t* Y, const float* w, const float* resid, float* out,
+hipError_t launch_combine(const float* Y, const float* w, const float* resid, float* out,
                           int64_t N, hipStream_t stream);
 
 }  // namespace lfm

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define LFM_MOE_ABI_VERSION 2
+#define LFM_MOE_ABI_VERSION 1
 #define LFM_MOE_HIDDEN 2048
 #define LFM_MOE_EXPERTS 64
 #define LFM_MOE_TOPK 4
@@ -130,9 +130,7 @@ lfm_moe_status lfm_moe_pack_down(const uint16_t* W_down, uint16_t* W_down_packed
  *   W_down:   packed down weights, as written by lfm_moe_pack_down (read)
  *   out:      [N, 2048] fp32 (written; must not overlap any input)
  * Expert hidden activations are rounded to bf16 before the down
- * projection and expert outputs to bf16 before the weighted combine (the
- * activation precision of a bf16 model); every accumulation, the combine's
- * included, is fp32.  Uses a workspace that the
+ * projection; every accumulation is fp32.  Uses a workspace that the
  * library owns (one per device, grown on demand with hipMalloc and kept
  * until lfm_moe_release()); calls that overlap in time on one device must
  * use lfm_moe_forward_ws with separate workspaces instead.
@@ -152,7 +150,7 @@ typedef enum {
   LFM_MOE_WS_OFFSETS = 3,   /* [65] int32: offsets[e] = first grouped row of expert e, offsets[64] = 4N */
   LFM_MOE_WS_ROW2SLOT = 4,  /* [4N] int32 grouped row -> slot t*4 + j (stable: token order inside an expert) */
   LFM_MOE_WS_H = 5,         /* [4N, 1536] bf16 expert hidden rows, slot order (row t*4 + j) */
-  LFM_MOE_WS_Y = 6,         /* [4N, 2048] bf16 expert output rows, slot order (row t*4 + j) */
+  LFM_MOE_WS_Y = 6,         /* [4N, 2048] fp32 expert output rows, slot order (row t*4 + j) */
   LFM_MOE_WS_X = 7,         /* [N, 2048] bf16 normalised input (block forward only) */
   LFM_MOE_WS_ROUTER_PARTIAL = 8, /* [ceil(N/16), 16, 16, 64] fp32 router partial logits per K slice;
                                     empty above 2048 tokens, where the router keeps them in LDS */

@@ -43,7 +43,7 @@ def test_workspace_layout(lib):
         assert offs == sorted(offs) and offs[-1] <= total
         # H and Y regions hold 4N rows.
         assert offs[_lib.WS_Y] - offs[_lib.WS_H] >= 4 * N * 1536 * 2
-        assert offs[_lib.WS_X] - offs[_lib.WS_Y] >= 4 * N * 2048 * 2
+        assert offs[_lib.WS_X] - offs[_lib.WS_Y] >= 4 * N * 2048 * 4
         assert offs[_lib.WS_ROUTER_PARTIAL] - offs[_lib.WS_X] >= N * 2048 * 2
         part = total - offs[_lib.WS_ROUTER_PARTIAL]
         if N <= 2048:

@@ -143,7 +143,7 @@ def test_intermediates_with_poisoned_workspace(moe, name):
     idx = view(_lib.WS_IDX, torch.int32, (N, 4))
     w = view(_lib.WS_W, torch.float32, (N, 4))
     H = _np(moe.workspace_view(ws, N, _lib.WS_H, torch.bfloat16, (4 * N, 1536)).float())
-    Y = _np(moe.workspace_view(ws, N, _lib.WS_Y, torch.bfloat16, (4 * N, 2048)).float())
+    Y = view(_lib.WS_Y, torch.float32, (4 * N, 2048))
     assert np.array_equal(_np(out), _np(out_internal)), "workspace forms disagree"
     alt = check_route(idx, w, r)
     check_out(_np(out), expected_outputs(inp, r, np.arange(N), alt))
@@ -173,10 +173,9 @@ def test_intermediates_with_poisoned_workspace(moe, name):
         h_rms = np.sqrt(np.mean(H_ref ** 2))
         assert np.all(np.abs(H - H_ref) <= np.ldexp(1.0, ex - 9) * (1 + 2 ** -6) + 1e-4 * h_rms)
         assert np.mean(H == Hq) > 0.98
-        # Y (stored in bf16 too) from the bf16 H: against the oracle taking the
-        # same rounding point, up to half a bf16 ulp plus the fp32
-        # accumulation error and the rare one-ulp H difference, and against
-        # the unrounded oracle within the output gate.
+        # Y from the bf16 H: against the oracle taking the same rounding point
+        # (fp32 accumulation error and the rare one-ulp H difference), and
+        # against the unrounded oracle within the output gate.
         Yq = np.zeros_like(Y_ref)
         slot_expert = r.idx.reshape(-1)
         for e in range(64):
@@ -184,8 +183,7 @@ def test_intermediates_with_poisoned_workspace(moe, name):
             if len(rows):
                 Yq[rows] = Hq[rows] @ inp["W_down"][e].astype(np.float64).T
         y_rms = np.sqrt(np.mean(Y_ref ** 2))
-        _, ey = np.frexp(Yq)
-        assert np.all(np.abs(Y - Yq) <= np.ldexp(1.0, ey - 9) * (1 + 2 ** -6) + 5e-3 * y_rms)
+        assert np.max(np.abs(Y - Yq)) <= 5e-3 * y_rms
         assert np.max(np.abs(Y - Y_ref)) <= 2e-2 * y_rms
 
 
