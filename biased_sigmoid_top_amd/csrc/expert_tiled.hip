@@ -9,19 +9,22 @@
 // over the tokens grouped by expert (section "What to verify in a
 // deployment").
 //
-// Tile: 128 grouped rows (tokens of one expert) x 256 weight rows, 32x32x16
-// bf16 MFMAs (on gfx950 twice the rate of the 16x16x32 form), two
-// workgroups per CU.  Each of the four wavefronts owns 64 weight rows (two
-// packed row blocks) for all 128 tokens: 4 x 2 accumulator tiles.  Because
-// no two wavefronts share weight rows, the weights need no LDS: every
-// wavefront streams its own packed fragments (one contiguous 1 KB buffer
-// load each) straight into its MFMA registers, three K stages ahead.  The
-// token rows, which all four wavefronts share, are gathered from their
-// slots (X row t for gate/up, H row t*4 + j for down) as whole 128-byte
-// lines, one per row per pair of K stages, so that no L2 request carries
-// half a line.  They are stored into a double-buffered, XOR-swizzled LDS
-// tile (one barrier per stage pair), and the MFMA operands of each K step
-// are read from it one step ahead.  For gate/up the 32 rows of a packed
+// Tile: 128 grouped rows (tokens of one expert) x 64 weight rows per
+// wavefront, 32x32x16 bf16 MFMAs (on gfx950 twice the rate of the 16x16x32
+// form).  Gate/up runs 8 wavefronts per workgroup (512 weight rows), one
+// workgroup per CU; down runs 4 (256 rows), two per CU.  Each wavefront
+// owns 64 weight rows (two packed row blocks) for all 128 tokens: 4 x 2
+// accumulator tiles.  Because no two wavefronts share weight rows, the
+// weights need no LDS: every wavefront streams its own packed fragments
+// (one contiguous 1 KB buffer load each) straight into its MFMA registers,
+// three K stages ahead.  The token rows, which all wavefronts share, are
+// gathered from their slots (X row t for gate/up, H row t*4 + j for down)
+// as whole 128-byte lines, one per row per pair of K stages, so that no L2
+// request carries half a line.  They are stored into a double-buffered,
+// XOR-swizzled LDS tile (one barrier per stage pair), and the MFMA operands
+// of each K step are read from it one step ahead.  The more wavefronts
+// share a token tile, the fewer bytes a CU pulls through its L1 per MFMA,
+// which is what bounds these kernels.  For gate/up the 32 rows of a packed
 // block are 16 gate rows and the matching 16 up rows, so the SiLU product
 // is formed in registers.
 //
@@ -30,7 +33,7 @@
 // tiles, each XCD taking a run of consecutive (column-major) tiles of the
 // group: every XCD gets the same share, and a column tile -- read by every
 // m-tile of its expert -- stays on one XCD (down: 8 column tiles) or two
-// (gate/up: 12 column tiles over groups of two m-tiles) and is shared
+// (gate/up: 6 column tiles over groups of four m-tiles) and is shared
 // through their L2.
 #include "common.hpp"
 #include "launch.hpp"
@@ -39,13 +42,11 @@ namespace lfm {
 
 namespace {
 
-constexpr int kTileThreads = 256;         // four wavefronts
 constexpr int kBM = 128;                  // grouped rows per tile
 constexpr int kKS = 2;                    // 16-wide K steps per stage
 constexpr int kBK = 16 * kKS;             // K per stage
 constexpr int kWSlots = 4;                // weight register ring: three stages ahead
 constexpr int kPairBytes = 2 * kBK * 2;   // token bytes per row per stage pair: one 128-byte line
-constexpr int kChunks = kBM * (kPairBytes / 16) / kTileThreads;  // 16-byte token pieces per thread per pair
 constexpr int kXcds = 8;
 
 // LDS position of a token piece: 16-byte chunk c (0..7) of row r's line for a
@@ -55,15 +56,22 @@ constexpr int kXcds = 8;
 // and the MFMA operand reads (32 rows of one K half) free of bank conflicts.
 __device__ __forceinline__ int swz(int c) { return c + 8 * (c & 1); }
 
-constexpr int kTilesPerCu = 2;  // occupancy the register budget is set for
-
+// Gate/up: 8 wavefronts (128 x 512 tiles), one workgroup per CU.  Down:
+// 4 wavefronts (128 x 256), two per CU -- its 8 column tiles then deal
+// evenly over the CUs where 4 wide ones would leave a half-empty last round
+// (N = 4096: down 159 us against 164; gate/up 256 against 267 with 4).
 template <bool GATEUP>
 struct TileShape {
   static constexpr int FB = 2;  // packed 32-row blocks per wavefront
+  static constexpr int kWaves = GATEUP ? 8 : 4;
+  static constexpr int kThreads = kWaves * kWave;
+  static constexpr int kPerCu = GATEUP ? 1 : 2;  // workgroups per CU the register budget is set for
+  static constexpr int kChunks = kBM * (kPairBytes / 16) / kThreads;  // 16-byte token pieces per thread per pair
+  static constexpr int kRowStep = kThreads / 8;  // tile rows one pass of the workgroup loads
   static constexpr int K = GATEUP ? kHidden : kFF;
   static constexpr int kSteps = GATEUP ? kGateupSteps : kDownSteps;
   static constexpr int kBlocks = GATEUP ? kGateupBlocks : kDownBlocks;
-  static constexpr int kBlocksPerTile = 4 * FB;
+  static constexpr int kBlocksPerTile = kWaves * FB;
   static constexpr int kColTiles = kBlocks / kBlocksPerTile;
   // m-tiles per launch group: a group holds a multiple of kXcds tiles.
   static constexpr int kGroup =
@@ -74,7 +82,8 @@ struct TileShape {
 };
 
 template <bool GATEUP>
-__global__ __launch_bounds__(kTileThreads, kTilesPerCu) void expert_tiled_kernel(
+__global__ __launch_bounds__(TileShape<GATEUP>::kThreads, TileShape<GATEUP>::kPerCu)
+void expert_tiled_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Wp,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ row2slot,
     uint16_t* __restrict__ H, float* __restrict__ Y) {
@@ -102,19 +111,21 @@ __global__ __launch_bounds__(kTileThreads, kTilesPerCu) void expert_tiled_kernel
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
 
-  // Token pieces of this thread: row r0 + 32 i (i < 4) of the tile, 16-byte
+  // Token pieces of this thread: row r0 + kRowStep * i of the tile, 16-byte
   // chunk c of the row's 128-byte line of a stage pair; eight consecutive
-  // lanes read one whole line.  All four pieces share c and r0 % 32, so their
+  // lanes read one whole line.  All the pieces share c and r0 % 32, so their
   // LDS positions differ by whole token-block fragments.
   const int r0 = tid / 8, c = tid % 8;
-  const uint16_t* arow[kChunks];
+  const uint16_t* arow[T::kChunks];
 #pragma unroll
-  for (int i = 0; i < kChunks; ++i) {
-    const int r = r0 + 32 * i;
+  for (int i = 0; i < T::kChunks; ++i) {
+    const int r = r0 + T::kRowStep * i;
     const int slot = row2slot[tile.row_begin + (r < tile.rows ? r : 0)];
     arow[i] = A + static_cast<size_t>(GATEUP ? slot / kTopK : slot) * T::K + c * 8;
   }
-  const int st_pos = ((c / 4) * 4 * kKS + (c / 2) % 2) * kWave + (c % 2) * 32 + ((r0 % 32) ^ swz(c));
+  const int st_pos = ((c / 4) * 4 * kKS + (c / 2) % 2) * kWave + (c % 2) * 32 + ((r0 % 32) ^ swz(c)) +
+                     (r0 / 32) * kKS * kWave;
+  static_assert(T::kRowStep % 32 == 0, "a thread's pieces share their row within a token block");
   // MFMA operand position of this lane for stage sp of a pair, K step j.
   int rd_pos[2][kKS];
 #pragma unroll
@@ -144,15 +155,15 @@ __global__ __launch_bounds__(kTileThreads, kTilesPerCu) void expert_tiled_kernel
         wv[f][j] = buf_ld<false>(wr, wlane, wbase + f * kBlockBytes + (sc * kKS + j) * kFragBytes);
   };
   constexpr int kPairs = T::kStages / 2;
-  uint4 stg[kChunks];
+  uint4 stg[T::kChunks];
   auto load_x = [&](int pair) {
     const int pc = pair < kPairs ? pair : kPairs - 1;
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) stg[i] = ld16(arow[i] + pc * (kPairBytes / 2));
+    for (int i = 0; i < T::kChunks; ++i) stg[i] = ld16(arow[i] + pc * (kPairBytes / 2));
   };
   auto store_x = [&](int pb) {
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) tok[pb][st_pos + i * kKS * kWave] = stg[i];
+    for (int i = 0; i < T::kChunks; ++i) tok[pb][st_pos + i * (T::kRowStep / 32) * kKS * kWave] = stg[i];
   };
 
   f32x16 acc[4][FB];
@@ -274,15 +285,15 @@ int64_t tiled_grid(int64_t N) {
 hipError_t launch_gateup_tiled(const uint16_t* X, const uint16_t* Wgu, const int32_t* offsets,
                                const int32_t* row2slot, uint16_t* H, int64_t N,
                                hipStream_t stream) {
-  hipLaunchKernelGGL(expert_tiled_kernel<true>, dim3(tiled_grid<true>(N)), dim3(kTileThreads), 0,
-                     stream, X, Wgu, offsets, row2slot, H, nullptr);
+  hipLaunchKernelGGL(expert_tiled_kernel<true>, dim3(tiled_grid<true>(N)),
+                     dim3(TileShape<true>::kThreads), 0, stream, X, Wgu, offsets, row2slot, H, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_down_tiled(const uint16_t* H, const uint16_t* Wd, const int32_t* offsets,
                              const int32_t* row2slot, float* Y, int64_t N, hipStream_t stream) {
-  hipLaunchKernelGGL(expert_tiled_kernel<false>, dim3(tiled_grid<false>(N)), dim3(kTileThreads), 0,
-                     stream, H, Wd, offsets, row2slot, nullptr, Y);
+  hipLaunchKernelGGL(expert_tiled_kernel<false>, dim3(tiled_grid<false>(N)),
+                     dim3(TileShape<false>::kThreads), 0, stream, H, Wd, offsets, row2slot, nullptr, Y);
   return hipGetLastError();
 }
 
