@@ -137,16 +137,6 @@ struct MTile {
   int rows;       // valid rows in the tile (<= tile_rows)
 };
 
-// Number of m-tiles of tile_rows grouped rows over all experts (every lane
-// of the calling wavefront gets it).
-__device__ __forceinline__ int mtile_count(const int* __restrict__ offsets, int tile_rows) {
-  const int lane = threadIdx.x & (kWave - 1);
-  int nt = (offsets[lane + 1] - offsets[lane] + tile_rows - 1) / tile_rows;
-#pragma unroll
-  for (int off = kWave / 2; off >= 1; off >>= 1) nt += __shfl_xor(nt, off, kWave);
-  return nt;
-}
-
 __device__ __forceinline__ bool map_mtile(const int* __restrict__ offsets, int mt, int tile_rows,
                                           MTile& t) {
   const int lane = threadIdx.x & (kWave - 1);

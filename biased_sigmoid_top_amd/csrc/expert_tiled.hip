@@ -106,6 +106,7 @@ void expert_tiled_kernel(
   const int mt = blockIdx.x / (T::kGroup * T::kColTiles) * T::kGroup + t % T::kGroup;
   MTile tile;
   if (!map_mtile(offsets, mt, kBM, tile)) return;
+  const int live_rows = uniform(tile.rows);
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -188,11 +189,15 @@ void expert_tiled_kernel(
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) d[tb] = tok[pb][rd_pos[sp][j] + tb * kKS * kWave];
   };
+  // Gate/up skips the MFMAs of 32-row token blocks that are all padding
+  // (the last m-tile of an expert); in the down kernel the branches cost
+  // more registers than it has.
   auto mma = [&](const uint4 (&wj)[FB][kKS], int j, const uint4 (&d)[4]) {
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
+      if (!GATEUP || tb == 0 || tb * 32 < live_rows)
 #pragma unroll
-      for (int f = 0; f < FB; ++f) acc[tb][f] = mfma32(wj[f][j], d[tb], acc[tb][f]);
+        for (int f = 0; f < FB; ++f) acc[tb][f] = mfma32(wj[f][j], d[tb], acc[tb][f]);
   };
   // The fences keep the issue order written here, which the wait counts
   // below rely on: weight loads, then the next LDS operands, then MFMAs.
