@@ -67,7 +67,6 @@ def log(msg):
 def prepare(name, copies, zero_bias=False):
     import torch
     import synth
-    import biased_sigmoid_top_amd as moe
     w = synth.WORKLOADS[name]
     N = w["N"]
     log(f"generating {name}: N={N} seed={w['seed']} skew={w['skew']}"
@@ -75,6 +74,25 @@ def prepare(name, copies, zero_bias=False):
     layer = synth.layer_inputs(N, w["seed"], w["skew"])
     if zero_bias:
         layer["bias"] = torch.zeros_like(layer["bias"])
+    return prepare_layer(name, N, w["seed"], layer, copies)
+
+
+def expert_counts(p, N):
+    """Slots per expert of the first N tokens (one untimed call through the _ws form)."""
+    import torch
+    import biased_sigmoid_top_amd as moe
+    from biased_sigmoid_top_amd import _lib
+    ws = moe.alloc_workspace(N)
+    moe.forward(p["X"][:N], p["W_r"], p["bias"], p["Wgu"][0], p["Wd"][0], p["out"][:N], workspace=ws)
+    sel = moe.workspace_view(ws, N, _lib.WS_IDX, torch.int32, (N, 4)).cpu().long()
+    del ws
+    torch.cuda.synchronize()
+    return torch.bincount(sel.reshape(-1), minlength=E).tolist()
+
+
+def prepare_layer(name, N, seed, layer, copies):
+    import torch
+    import biased_sigmoid_top_amd as moe
     dev = torch.device("cuda")
     X = moe.rmsnorm(layer["z"].to(dev))          # input preparation, not timed
     W_r, bias = layer["W_r"].to(dev), layer["bias"].to(dev)
@@ -83,16 +101,10 @@ def prepare(name, copies, zero_bias=False):
     Wgu = [Wgu0] + [Wgu0.clone() for _ in range(copies - 1)]
     Wd = [Wd0] + [Wd0.clone() for _ in range(copies - 1)]
     out = torch.empty(N, D, dtype=torch.float32, device=dev)
-    # Routing structure of this input (one untimed call through the _ws form).
-    from biased_sigmoid_top_amd import _lib
-    ws = moe.alloc_workspace(N)
-    moe.forward(X, W_r, bias, Wgu0, Wd0, out, workspace=ws)
-    sel = moe.workspace_view(ws, N, _lib.WS_IDX, torch.int32, (N, 4)).cpu().long()
-    counts = torch.bincount(sel.reshape(-1), minlength=E).tolist()
-    del ws
-    torch.cuda.synchronize()
-    return dict(name=name, N=N, seed=w["seed"], layer=layer, X=X, W_r=W_r, bias=bias,
-                Wgu=Wgu, Wd=Wd, out=out, counts=counts)
+    p = dict(name=name, N=N, seed=seed, layer=layer, X=X, W_r=W_r, bias=bias,
+             Wgu=Wgu, Wd=Wd, out=out)
+    p["counts"] = expert_counts(p, N)
+    return p
 
 
 def time_steps(p, steps, warmup):
@@ -241,7 +253,7 @@ def parse_args(argv=None):
     ap.add_argument("--workload", default="decode_n64", help="headline workload")
     ap.add_argument("--configs", action="store_true",
                     help="also measure every configuration (C0-C4, the 38-block stack included; "
-                         "several minutes) and add them to the line under 'configs'")
+                         "several minutes) and add them, with the verification-batch series V1-V64, to the line under 'configs'")
     return ap.parse_args(argv)
 
 
@@ -418,6 +430,30 @@ def measure_configs(args):
     e = measure_stack(max(3, args.steps // 40), 1)
     log(json.dumps(e))
     out.append(e)
+    out += measure_verify(args)
+    return out
+
+
+def measure_verify(args):
+    """Verification-shaped batches of speculative decoding: c requests x 10
+    tokens per step, the first 10c tokens of one layer (seed 5)."""
+    import torch
+    import synth
+    log("generating the verification-batch layer (seed 5)")
+    Nmax = max(synth.verify_batch_sizes())
+    full = prepare_layer("verify", Nmax, synth.VERIFY["seed"], synth.verify_inputs(), args.copies)
+    out = []
+    for c, N in zip(synth.VERIFY["concurrency"], synth.verify_batch_sizes()):
+        p = dict(full, N=N, X=full["X"][:N], out=full["out"][:N])
+        p["counts"] = expert_counts(p, N)
+        log(f"timing V{c}: {N} tokens, {args.steps} steps")
+        w, k = time_steps(p, args.steps, args.warmup)
+        e = config_entry(f"V{c}", summarize(p, w, k),
+                         f"verification batch: {c} requests x 10 tokens (supplementary)")
+        log(json.dumps(e))
+        out.append(e)
+    del full
+    torch.cuda.empty_cache()
     return out
 
 

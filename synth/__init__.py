@@ -106,6 +106,26 @@ def stack_block_params(seed: int, block: int, d: int = HIDDEN, E: int = EXPERTS,
     return layer_params(block_seed(seed, block), 0, False, d, E, ff)
 
 
+# Verification-shaped batches of speculative decoding (orcarouter.ai page
+# "LFM2.5-24B-A2B-DSpark ist live auf Hugging Face", sections "Was ist
+# eigentlich im Repository?" and "Es ausführen": the drafter proposes blocks
+# of 9 and the target verifies ten tokens per request per step; verifying k
+# tokens activates more experts than decoding one).  c concurrent requests
+# make a batch of 10c tokens.  One layer, drawn with seed 5 for the largest
+# batch, serves the whole series: the batch of c requests is the first 10c
+# rows of its z, so the growth of the active-expert set is seen on one model.
+VERIFY = dict(seed=5, tokens_per_request=10, concurrency=(1, 2, 4, 8, 16, 32, 64))
+
+
+def verify_batch_sizes() -> list:
+    return [VERIFY["tokens_per_request"] * c for c in VERIFY["concurrency"]]
+
+
+def verify_inputs() -> dict:
+    """z for the largest verification batch plus the layer's parameters."""
+    return layer_inputs(max(verify_batch_sizes()), VERIFY["seed"])
+
+
 # The single-layer workloads: (name, N, seed, skew).
 WORKLOADS = {
     "tiny_n32": dict(N=32, seed=0, skew=False),

@@ -18,6 +18,15 @@ def pytest_configure(config):
 _LAYER_CACHE = {}
 
 
+def cached_verify_layer():
+    """The verification-batch series' layer (CPU tensors), generated once per session."""
+    import synth
+    key = ("verify",)
+    if key not in _LAYER_CACHE:
+        _LAYER_CACHE[key] = synth.verify_inputs()
+    return _LAYER_CACHE[key]
+
+
 def cached_layer(N, seed, skew=False):
     """Seeded single-layer workload (CPU tensors), generated once per session."""
     import synth

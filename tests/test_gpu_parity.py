@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import synth
-from conftest import cached_layer
+from conftest import cached_layer, cached_verify_layer
 from parity import (check_grouping_valid, check_out, check_route, device_inputs,
                     device_weights, expected_outputs, oracle_inputs)
 
@@ -241,6 +241,27 @@ def test_every_token_on_the_same_four_experts(moe, N):
     _step(f"same-four-experts N={N}")
     out = moe.forward(dev["X"], dev["W_r"], dev["bias"], dev["W_gateup"], dev["W_down"])
     idx, w = moe.route(dev["X"], dev["W_r"], dev["bias"])
+    alt = check_route(_np(idx), _np(w), r)
+    check_out(_np(out), expected_outputs(inp, r, np.arange(N), alt))
+
+
+@pytest.mark.parametrize("c", [1, 8, 16, 64])
+def test_verification_batches(moe, c):
+    """Speculative-decoding verification batches: c requests x 10 tokens, the
+    first 10c tokens of one layer's inputs (decode path up to 96 tokens, the
+    grouped path above)."""
+    if "verify" not in _CASES:
+        layer = cached_verify_layer()
+        inp = oracle_inputs(layer)
+        _CASES["verify"] = (inp, device_inputs(layer, inp["X"]))
+    full, dev = _CASES["verify"]
+    N = synth.VERIFY["tokens_per_request"] * c
+    inp = dict(full, X=full["X"][:N])
+    r = oracle.route(inp["X"], inp["W_r"], inp["bias"])
+    _step(f"verification batch c={c} N={N}")
+    X = dev["X"][:N]
+    out = moe.forward(X, dev["W_r"], dev["bias"], dev["W_gateup"], dev["W_down"])
+    idx, w = moe.route(X, dev["W_r"], dev["bias"])
     alt = check_route(_np(idx), _np(w), r)
     check_out(_np(out), expected_outputs(inp, r, np.arange(N), alt))
 
