@@ -60,9 +60,9 @@ __device__ __forceinline__ int swz(int c) { return c + 8 * (c & 1); }
 // 4 wavefronts (128 x 256), two per CU -- its 8 column tiles then deal
 // evenly over the CUs where 4 wide ones would leave a half-empty last round
 // (N = 4096: down 159 us against 164; gate/up 256 against 267 with 4).
-template <bool GATEUP>
+template <bool GATEUP, int FB_>
 struct TileShape {
-  static constexpr int FB = 2;  // packed 32-row blocks per wavefront
+  static constexpr int FB = FB_;  // packed 32-row blocks per wavefront
   static constexpr int kWaves = GATEUP ? 8 : 4;
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kPerCu = GATEUP ? 1 : 2;  // workgroups per CU the register budget is set for
@@ -81,13 +81,13 @@ struct TileShape {
   static_assert(kGroup * kColTiles % kXcds == 0, "a launch group deals evenly over the XCDs");
 };
 
-template <bool GATEUP>
-__global__ __launch_bounds__(TileShape<GATEUP>::kThreads, TileShape<GATEUP>::kPerCu)
+template <bool GATEUP, int FB_>
+__global__ __launch_bounds__((TileShape<GATEUP, FB_>::kThreads), (TileShape<GATEUP, FB_>::kPerCu))
 void expert_tiled_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Wp,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ row2slot,
     uint16_t* __restrict__ H, float* __restrict__ Y) {
-  using T = TileShape<GATEUP>;
+  using T = TileShape<GATEUP, FB_>;
   constexpr int FB = T::FB;
   static_assert(T::kStages % kWSlots == 0, "the stage loop is unrolled by the ring size");
   // Token fragments: 2 pair buffers x (2 stages x 4 token blocks x kKS steps).
@@ -278,11 +278,31 @@ void expert_tiled_kernel(
   }
 }
 
-template <bool GATEUP>
+template <bool GATEUP, int FB>
 int64_t tiled_grid(int64_t N) {
-  using T = TileShape<GATEUP>;
+  using T = TileShape<GATEUP, FB>;
   const int64_t groups = (max_mtiles(N, kBM) + T::kGroup - 1) / T::kGroup;
   return groups * T::kGroup * T::kColTiles;
+}
+
+// Gate/up column tiles: 512 weight rows (two blocks per wavefront), or 256
+// (one) for batches of 257 to 2048 tokens.  There the experts have few
+// m-tiles each, and 512-row tiles make barely more workgroups than the
+// device holds, so a second, nearly empty round follows the first; half as
+// wide, twice as many tiles finish in about one round and a fifth.
+// Measured gate/up, 512-row against 256-row tiles: N = 256: 95 vs 99 us;
+// 384: 139 vs 105; 1024: 146 vs 133; 2048: 188 vs 177; 4096: 245 vs 261.
+bool narrow_gateup_tiles(int64_t N) { return N > 256 && N <= 2048; }
+
+template <bool GATEUP, int FB, typename Out>
+hipError_t launch_tiled(const uint16_t* A, const uint16_t* W, const int32_t* offsets,
+                        const int32_t* row2slot, Out* out, int64_t N, hipStream_t stream) {
+  uint16_t* H = nullptr;
+  float* Y = nullptr;
+  if constexpr (GATEUP) H = out; else Y = out;
+  hipLaunchKernelGGL((expert_tiled_kernel<GATEUP, FB>), dim3(tiled_grid<GATEUP, FB>(N)),
+                     dim3(TileShape<GATEUP, FB>::kThreads), 0, stream, A, W, offsets, row2slot, H, Y);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -290,16 +310,13 @@ int64_t tiled_grid(int64_t N) {
 hipError_t launch_gateup_tiled(const uint16_t* X, const uint16_t* Wgu, const int32_t* offsets,
                                const int32_t* row2slot, uint16_t* H, int64_t N,
                                hipStream_t stream) {
-  hipLaunchKernelGGL(expert_tiled_kernel<true>, dim3(tiled_grid<true>(N)),
-                     dim3(TileShape<true>::kThreads), 0, stream, X, Wgu, offsets, row2slot, H, nullptr);
-  return hipGetLastError();
+  return narrow_gateup_tiles(N) ? launch_tiled<true, 1>(X, Wgu, offsets, row2slot, H, N, stream)
+                                : launch_tiled<true, 2>(X, Wgu, offsets, row2slot, H, N, stream);
 }
 
 hipError_t launch_down_tiled(const uint16_t* H, const uint16_t* Wd, const int32_t* offsets,
                              const int32_t* row2slot, float* Y, int64_t N, hipStream_t stream) {
-  hipLaunchKernelGGL(expert_tiled_kernel<false>, dim3(tiled_grid<false>(N)),
-                     dim3(TileShape<false>::kThreads), 0, stream, H, Wd, offsets, row2slot, nullptr, Y);
-  return hipGetLastError();
+  return launch_tiled<false, 2>(H, Wd, offsets, row2slot, Y, N, stream);
 }
 
 }  // namespace lfm
