@@ -6,7 +6,8 @@ Importing the package loads liblfm_moe.so and fails if it has not been built.
 
 from . import _lib
 from .api import (EXPERTS, FF, HIDDEN, TOP_K, abi_version, alloc_workspace,  # noqa: F401
-                  block_forward, forward, pack_down, pack_gateup, release, rmsnorm,
+                  block_forward, forward, forward_fp8, pack_down, pack_fp8_down,
+                  pack_fp8_gateup, pack_gateup, release, rmsnorm,
                   route, timing_enable,
                   timing_read, workspace_bytes, workspace_offset, workspace_view)
 

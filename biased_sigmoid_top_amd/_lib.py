@@ -22,6 +22,7 @@ ERR_HIP = 4
 
 WS_IDX, WS_W, WS_BLOCKCOUNTS, WS_OFFSETS, WS_ROW2SLOT, WS_H, WS_Y, WS_X, WS_ROUTER_PARTIAL = range(9)
 DECODE_MAX_TOKENS = 96
+FP8_MAX_TOKENS = 96
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -41,6 +42,10 @@ SIGNATURES = {
     "lfm_moe_forward_ws": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _P, _SZ, _P]),
     "lfm_moe_block_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _P]),
     "lfm_moe_block_forward_ws": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _P, _SZ, _P]),
+    "lfm_moe_pack_fp8_gateup": (ctypes.c_int, [_P, _P, _P, _P, _P]),
+    "lfm_moe_pack_fp8_down": (ctypes.c_int, [_P, _P, _P, _P]),
+    "lfm_moe_forward_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _P]),
+    "lfm_moe_forward_fp8_ws": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _P, _SZ, _P]),
     "lfm_moe_release": (None, []),
     "lfm_moe_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "lfm_moe_timing_read": (ctypes.c_int, [_P, _P]),

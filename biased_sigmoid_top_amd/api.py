@@ -113,6 +113,54 @@ def route(X, W_r, bias, idx=None, w=None, stream=None):
     return idx, w
 
 
+FP8_GATEUP_SCALES = (EXPERTS, 2, FF // 128, HIDDEN // 128)
+FP8_DOWN_SCALES = (EXPERTS, HIDDEN // 128, FF // 128)
+
+
+def pack_fp8_gateup(W_gate, W_up, stream=None):
+    """FP8 block quantisation of the gate and up matrices: (codes [64*3072*2048]
+    uint8 in the FP8 fragment layout, scales [64, 2, 12, 16] fp32)."""
+    pg = _req(W_gate, "W_gate", torch.bfloat16, (EXPERTS, FF, HIDDEN))
+    pu = _req(W_up, "W_up", torch.bfloat16, (EXPERTS, FF, HIDDEN))
+    codes = torch.empty(EXPERTS * 2 * FF * HIDDEN, dtype=torch.uint8, device=W_gate.device)
+    scales = torch.empty(FP8_GATEUP_SCALES, dtype=torch.float32, device=W_gate.device)
+    _lib.call("lfm_moe_pack_fp8_gateup", pg, pu, codes.data_ptr(), scales.data_ptr(), _stream(stream))
+    return codes, scales
+
+
+def pack_fp8_down(W_down, stream=None):
+    """FP8 block quantisation of the down matrices: (codes [64*2048*1536] uint8,
+    scales [64, 16, 12] fp32)."""
+    pd = _req(W_down, "W_down", torch.bfloat16, (EXPERTS, HIDDEN, FF))
+    codes = torch.empty(EXPERTS * HIDDEN * FF, dtype=torch.uint8, device=W_down.device)
+    scales = torch.empty(FP8_DOWN_SCALES, dtype=torch.float32, device=W_down.device)
+    _lib.call("lfm_moe_pack_fp8_down", pd, codes.data_ptr(), scales.data_ptr(), _stream(stream))
+    return codes, scales
+
+
+def forward_fp8(X, W_r, bias, gateup_fp8, down_fp8, out=None, workspace=None, stream=None):
+    """The layer with FP8 experts (N <= 96): gateup_fp8 and down_fp8 are the
+    (codes, scales) pairs of pack_fp8_gateup / pack_fp8_down.  With
+    ``workspace`` the _ws entry point is used."""
+    N = X.shape[0]
+    pX = _req(X, "X", torch.bfloat16, (N, HIDDEN))
+    pr = _req(W_r, "W_r", torch.bfloat16, (EXPERTS, HIDDEN))
+    pb = _req(bias, "bias", torch.float32, (EXPERTS,))
+    gc = _req(gateup_fp8[0], "W_gateup_fp8", torch.uint8, (EXPERTS * 2 * FF * HIDDEN,))
+    gs = _req(gateup_fp8[1], "scales_gateup", torch.float32, FP8_GATEUP_SCALES)
+    dc = _req(down_fp8[0], "W_down_fp8", torch.uint8, (EXPERTS * HIDDEN * FF,))
+    ds = _req(down_fp8[1], "scales_down", torch.float32, FP8_DOWN_SCALES)
+    if out is None:
+        out = torch.empty(N, HIDDEN, dtype=torch.float32, device=X.device)
+    po = _req(out, "out", torch.float32, (N, HIDDEN))
+    if workspace is None:
+        _lib.call("lfm_moe_forward_fp8", pX, pr, pb, gc, gs, dc, ds, po, N, _stream(stream))
+    else:
+        _lib.call("lfm_moe_forward_fp8_ws", pX, pr, pb, gc, gs, dc, ds, po, N, workspace.data_ptr(),
+                  workspace.numel() * workspace.element_size(), _stream(stream))
+    return out
+
+
 def forward(X, W_r, bias, W_gateup, W_down, out=None, workspace=None, stream=None):
     """out [N, 2048] fp32.  With ``workspace`` the _ws entry point is used."""
     N = X.shape[0]

@@ -262,6 +262,68 @@ size_t act_bytes(int64_t N, size_t elem) {
   return static_cast<size_t>(N < 0 ? 0 : N) * kHidden * elem;
 }
 
+// FP8 experts: one byte per weight, a fp32 scale per 128 x 128 block.
+constexpr size_t kFp8GateupBytes = static_cast<size_t>(kExperts) * 2 * kFF * kHidden;
+constexpr size_t kFp8DownBytes = static_cast<size_t>(kExperts) * kHidden * kFF;
+constexpr size_t kFp8GateupScaleBytes = sizeof(float) * kExperts * 2 * (kFF / 128) * (kHidden / 128);
+constexpr size_t kFp8DownScaleBytes = sizeof(float) * kExperts * (kHidden / 128) * (kFF / 128);
+
+// Checks of the FP8 layer entry points.
+lfm_moe_status check_fp8_args(const uint16_t* X, const uint16_t* W_r, const float* bias,
+                              const uint8_t* W_gateup_fp8, const float* scales_gateup,
+                              const uint8_t* W_down_fp8, const float* scales_down, const float* out,
+                              int64_t N) {
+  if (N < 0) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "N must be >= 0");
+  if (N > LFM_MOE_FP8_MAX_TOKENS)
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "N exceeds LFM_MOE_FP8_MAX_TOKENS (FP8 experts: decode batches)");
+  if (N == 0) return LFM_MOE_OK;
+  if (!X || !W_r || !bias || !W_gateup_fp8 || !scales_gateup || !W_down_fp8 || !scales_down || !out)
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if (misaligned(X) || misaligned(W_r) || misaligned(bias) || misaligned(W_gateup_fp8) ||
+      misaligned(scales_gateup) || misaligned(W_down_fp8) || misaligned(scales_down) || misaligned(out))
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  const Span o{out, act_bytes(N, 4)};
+  const Span ins[] = {{X, act_bytes(N, 2)},
+                      {W_r, sizeof(uint16_t) * kExperts * kHidden},
+                      {bias, sizeof(float) * kExperts},
+                      {W_gateup_fp8, kFp8GateupBytes},
+                      {scales_gateup, kFp8GateupScaleBytes},
+                      {W_down_fp8, kFp8DownBytes},
+                      {scales_down, kFp8DownScaleBytes}};
+  for (const Span& s : ins)
+    if (overlap(o, s)) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "output overlaps an input");
+  return LFM_MOE_OK;
+}
+
+// The FP8 layer on checked arguments: route, FP8 gate/up and down (weight
+// streaming, each workgroup groups the slots itself), combine.
+lfm_moe_status run_fp8(const uint16_t* X, const uint16_t* W_r, const float* bias,
+                       const uint8_t* W_gateup_fp8, const float* scales_gateup,
+                       const uint8_t* W_down_fp8, const float* scales_down, float* out, int64_t N,
+                       void* ws, hipStream_t stream) {
+  StageTimer timer(stream);
+  int32_t* idx = region<int32_t>(ws, N, LFM_MOE_WS_IDX);
+  float* w = region<float>(ws, N, LFM_MOE_WS_W);
+  uint16_t* H = region<uint16_t>(ws, N, LFM_MOE_WS_H);
+  float* Y = region<float>(ws, N, LFM_MOE_WS_Y);
+  float* part = region<float>(ws, N, LFM_MOE_WS_ROUTER_PARTIAL);
+  const int n = static_cast<int>(N);
+  hipError_t e;
+  if ((e = launch_route(X, W_r, bias, idx, w, nullptr, part, n, stream)) != hipSuccess)
+    return hip_fail(e, "route kernel launch");
+  timer.after(1);
+  if ((e = launch_gateup_decode_fp8(X, W_gateup_fp8, scales_gateup, idx, H, n, stream)) != hipSuccess)
+    return hip_fail(e, "fp8 gate/up kernel launch");
+  timer.after(3);
+  if ((e = launch_down_decode_fp8(H, W_down_fp8, scales_down, idx, Y, n, stream)) != hipSuccess)
+    return hip_fail(e, "fp8 down kernel launch");
+  timer.after(4);
+  if ((e = launch_combine(Y, w, nullptr, out, N, stream)) != hipSuccess)
+    return hip_fail(e, "combine kernel launch");
+  timer.after(5);
+  return LFM_MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -318,6 +380,68 @@ lfm_moe_status lfm_moe_pack_down(const uint16_t* W_down, uint16_t* W_down_packed
     return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "output overlaps the input");
   hipError_t e = launch_pack_down(W_down, W_down_packed, stream);
   return e == hipSuccess ? LFM_MOE_OK : hip_fail(e, "pack kernel launch");
+}
+
+lfm_moe_status lfm_moe_pack_fp8_gateup(const uint16_t* W_gate, const uint16_t* W_up,
+                                       uint8_t* W_gateup_fp8, float* scales_gateup,
+                                       hipStream_t stream) {
+  g_last_error.clear();
+  if (!W_gate || !W_up || !W_gateup_fp8 || !scales_gateup)
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if (misaligned(W_gate) || misaligned(W_up) || misaligned(W_gateup_fp8) || misaligned(scales_gateup))
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  const size_t half = sizeof(uint16_t) * kExperts * kFF * kHidden;
+  const Span outs[] = {{W_gateup_fp8, kFp8GateupBytes}, {scales_gateup, kFp8GateupScaleBytes}};
+  for (const Span& o : outs)
+    if (overlap(o, Span{W_gate, half}) || overlap(o, Span{W_up, half}))
+      return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "output overlaps an input");
+  if (overlap(outs[0], outs[1])) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "codes overlap scales");
+  hipError_t e = launch_pack_fp8_gateup(W_gate, W_up, W_gateup_fp8, scales_gateup, stream);
+  return e == hipSuccess ? LFM_MOE_OK : hip_fail(e, "fp8 pack kernel launch");
+}
+
+lfm_moe_status lfm_moe_pack_fp8_down(const uint16_t* W_down, uint8_t* W_down_fp8,
+                                     float* scales_down, hipStream_t stream) {
+  g_last_error.clear();
+  if (!W_down || !W_down_fp8 || !scales_down)
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if (misaligned(W_down) || misaligned(W_down_fp8) || misaligned(scales_down))
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  const Span in{W_down, sizeof(uint16_t) * kExperts * kHidden * kFF};
+  const Span outs[] = {{W_down_fp8, kFp8DownBytes}, {scales_down, kFp8DownScaleBytes}};
+  for (const Span& o : outs)
+    if (overlap(o, in)) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "output overlaps the input");
+  if (overlap(outs[0], outs[1])) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "codes overlap scales");
+  hipError_t e = launch_pack_fp8_down(W_down, W_down_fp8, scales_down, stream);
+  return e == hipSuccess ? LFM_MOE_OK : hip_fail(e, "fp8 pack kernel launch");
+}
+
+lfm_moe_status lfm_moe_forward_fp8_ws(const uint16_t* X, const uint16_t* W_r, const float* bias,
+                                      const uint8_t* W_gateup_fp8, const float* scales_gateup,
+                                      const uint8_t* W_down_fp8, const float* scales_down, float* out,
+                                      int64_t N, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  lfm_moe_status st = check_fp8_args(X, W_r, bias, W_gateup_fp8, scales_gateup, W_down_fp8,
+                                     scales_down, out, N);
+  if (st != LFM_MOE_OK || N == 0) return st;
+  if ((st = check_ws(ws, ws_bytes, N, Span{out, act_bytes(N, 4)})) != LFM_MOE_OK) return st;
+  return run_fp8(X, W_r, bias, W_gateup_fp8, scales_gateup, W_down_fp8, scales_down, out, N, ws,
+                 stream);
+}
+
+lfm_moe_status lfm_moe_forward_fp8(const uint16_t* X, const uint16_t* W_r, const float* bias,
+                                   const uint8_t* W_gateup_fp8, const float* scales_gateup,
+                                   const uint8_t* W_down_fp8, const float* scales_down, float* out,
+                                   int64_t N, hipStream_t stream) {
+  g_last_error.clear();
+  lfm_moe_status st = check_fp8_args(X, W_r, bias, W_gateup_fp8, scales_gateup, W_down_fp8,
+                                     scales_down, out, N);
+  if (st != LFM_MOE_OK || N == 0) return st;
+  void* ws = nullptr;
+  size_t bytes = 0;
+  if ((st = internal_ws(N, &ws, &bytes)) != LFM_MOE_OK) return st;
+  return run_fp8(X, W_r, bias, W_gateup_fp8, scales_gateup, W_down_fp8, scales_down, out, N, ws,
+                 stream);
 }
 
 lfm_moe_status lfm_moe_route(const uint16_t* X, const uint16_t* W_r, const float* bias,

@@ -73,10 +73,11 @@ struct StreamShared {
 // Groups the slots t*4 + j of N <= kDecodeMaxTokens tokens by expert.
 __device__ void group_slots(const int32_t* __restrict__ idx, int N, Grouping& G) {
   const int tid = threadIdx.x;
-  for (int i = tid; i < kExperts * kMaskWords; i += kStreamThreads) (&G.mask[0][0])[i] = 0u;
+  const int nthreads = blockDim.x;
+  for (int i = tid; i < kExperts * kMaskWords; i += nthreads) (&G.mask[0][0])[i] = 0u;
   if (tid < kExperts) G.cnt[tid] = 0;
   __syncthreads();
-  for (int t = tid; t < N; t += kStreamThreads) {
+  for (int t = tid; t < N; t += nthreads) {
     const int4 v = *reinterpret_cast<const int4*>(idx + static_cast<size_t>(t) * kTopK);
     const int es[kTopK] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -96,7 +97,7 @@ __device__ void group_slots(const int32_t* __restrict__ idx, int N, Grouping& G)
     if (tid == 0) G.n_active = __popcll(act);
   }
   __syncthreads();
-  for (int t = tid; t < N; t += kStreamThreads) {
+  for (int t = tid; t < N; t += nthreads) {
     const int4 v = *reinterpret_cast<const int4*>(idx + static_cast<size_t>(t) * kTopK);
     const int es[kTopK] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -163,7 +164,10 @@ __device__ __forceinline__ void stream_units(const uint16_t* __restrict__ B,
 
   auto expert_of = [&](int u) { return uniform(S.G.active[u / kUnitsPerExpert]); };
   auto count_of = [&](int e) { return uniform(S.G.off[e + 1] - S.G.off[e]); };
+  // Past the end of the share a cursor stays put (its loads are dummies),
+  // so no expert past the last active one is looked up.
   auto advance = [&](Cursor& c) {
+    if (c.u >= end) return;
     c.p ^= 1;
     if (c.p == 0 && ++c.pass * kPassRows >= count_of(expert_of(c.u))) {
       c.pass = 0;
@@ -278,6 +282,233 @@ __device__ __forceinline__ void stream_units(const uint16_t* __restrict__ B,
   }
 }
 
+// FP8 experts (pack_fp8.hip): 1 KB fragments of 32 rows x 32 K, one
+// 16-byte load per lane holding its operands of two 16-wide K steps; a fp32
+// scale per 128 x 128 weight block.  Each wavefront covers one 128-wide K
+// group of a unit (gate/up: 16 wavefronts, down: 12), which is both a weight
+// block's columns and an activation group: the wavefront loads its slice of
+// the bf16 token rows, quantises it per token (largest magnitude of the
+// token's 128 values, codes E4M3(x * (448 / amax)), scale amax / 448 -- the
+// activation quantisation of the inferencekey.com page's FP8_BLOCK entry),
+// multiplies, and scales its partial tile once by weight scale x token scale
+// before the cross-wavefront sum.  One unit per step (4 fragments, 4 KB per
+// wavefront), three units in the register ring.
+//
+// The products run on the bf16 MFMA: both operands' codes are widened to
+// bf16 in registers (E4M3 values are bf16 values, and their products are
+// exact in fp32), so the sums are fp32 sums of exact products.  The FP8
+// MFMA is not used: measured on gfx950, it adds each group of 8 products
+// after aligning them to the group's largest exponent and truncating to 13
+// fraction bits, an error of up to 2^-10 of the largest product, where the
+// bf16 MFMA returns the correctly rounded fp32 sum.  The loop is bound by
+// the weight stream, so the widening costs no time.
+constexpr uint32_t kFp8FragBytes = 1024;
+
+template <bool GATEUP>
+__device__ __forceinline__ uint32_t fp8_block_bytes(int e, int b) {
+  constexpr int kPairs = (GATEUP ? kHidden : kFF) / 32;
+  constexpr int kBlocks = GATEUP ? kGateupBlocks : kDownBlocks;
+  return static_cast<uint32_t>((e * kBlocks + b) * kPairs) * kFp8FragBytes;
+}
+
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
+}
+
+// Eight E4M3 codes (bytes of lo, then hi) as eight bf16 values (exact).
+__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  using bf16x2 = __bf16 __attribute__((ext_vector_type(2)));
+  const bf16x2 v[4] = {__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, false),
+                       __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, true),
+                       __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, false),
+                       __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, true)};
+  uint4 r;
+  __builtin_memcpy(&r, v, sizeof(r));
+  return r;
+}
+
+template <bool GATEUP>
+__device__ __forceinline__ void stream_units_fp8(const uint16_t* __restrict__ B,
+                                                 const uint8_t* __restrict__ Wq,
+                                                 const float* __restrict__ Ws,
+                                                 uint16_t* __restrict__ H, float* __restrict__ Y,
+                                                 int N, StreamShared& S) {
+  constexpr int K = GATEUP ? kHidden : kFF;
+  constexpr int kWaves = K / 128;  // one 128-wide group per wavefront
+  constexpr int kFrags = 4;        // 128 K = 4 fragments of 32 K
+  constexpr int kUnitsPerExpert = GATEUP ? kGateupBlocks : kDownBlocks;
+  int begin, end;
+  my_share(uniform(S.G.n_active) * kUnitsPerExpert, begin, end);
+  if (begin >= end) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const uint32_t lane_bytes = lane * 16;
+  const uint32_t kcol_bytes = (wave * 128 + (lane / 32) * 8) * 2;  // this lane's first bf16 K column
+  const Rsrc wr = make_rsrc(Wq, static_cast<uint32_t>(kExperts) * kHidden * kFF * (GATEUP ? 2 : 1));
+  const Rsrc br = make_rsrc(B, static_cast<uint32_t>(N) * (GATEUP ? 1 : kTopK) * K * 2);
+
+  auto expert_of = [&](int u) { return uniform(S.G.active[u / kUnitsPerExpert]); };
+  auto count_of = [&](int e) { return uniform(S.G.off[e + 1] - S.G.off[e]); };
+  auto advance = [&](Cursor& c) {
+    if (c.u >= end) return;
+    if (++c.pass * kPassRows >= count_of(expert_of(c.u))) {
+      c.pass = 0;
+      ++c.u;
+    }
+  };
+  // Weight loads of unit c (past the end of the share: an offset outside the
+  // buffer, which returns zeros, so every path keeps the same loads in flight).
+  auto issue = [&](const Cursor& c, uint4 (&w)[kFrags]) {
+    const bool live = c.u < end;
+    const int u = live ? c.u : begin;
+    const uint32_t base = uniform(fp8_block_bytes<GATEUP>(expert_of(u), u % kUnitsPerExpert) +
+                                  wave * kFrags * kFp8FragBytes);
+    const uint32_t voff = live ? lane_bytes : 0x80000000u + lane_bytes;
+#pragma unroll
+    for (int f = 0; f < kFrags; ++f) w[f] = buf_ld<true>(wr, voff, base + f * kFp8FragBytes);
+  };
+
+  // Token rows: 8 bf16 K steps per lane as loaded; quantised in place to
+  // the bf16 values of their E4M3 codes (K step k stays in xb[k]).
+  uint4 w0[kFrags], w1[kFrags], w2[kFrags], xb[8];
+  float xscale = 0.f;
+  bool fresh = false;
+  int xe = -1, xpass = -1;
+  auto load_rows = [&](const Cursor& c) {
+    if (c.u >= end) return;
+    const int e = expert_of(c.u);
+    if (e == xe && c.pass == xpass) return;
+    const int r0 = c.pass * kPassRows;
+    const int rows = min(kPassRows, count_of(e) - r0);
+    const int slot = pass_slot(S.G.list + S.G.off[e] + r0, rows, lane);
+    const uint32_t bo = (GATEUP ? slot / kTopK : slot) * (K * 2) + kcol_bytes;
+#pragma unroll
+    for (int f = 0; f < 8; ++f) xb[f] = buf_ld<false>(br, bo, f * 32);
+    xe = e;
+    xpass = c.pass;
+    fresh = true;
+  };
+  auto quantize_rows = [&] {
+    // Largest magnitude: on the bf16 bit patterns (the order of finite
+    // non-negative floats is that of their bits).
+    uint32_t m = 0;
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      const uint32_t w4[4] = {xb[f].x, xb[f].y, xb[f].z, xb[f].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m = max(m, max(w4[k] & 0x7fffu, (w4[k] >> 16) & 0x7fffu));
+    }
+    float amax = __uint_as_float(m << 16);
+    // Lanes l and l ^ 32 hold the two halves of the same token's group.
+    amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+    const float inv = amax > 0.f ? 448.f / amax : 0.f;
+    xscale = amax / 448.f;
+    auto q4 = [&](uint32_t lo, uint32_t hi) {
+      return e4m3x4(__uint_as_float(lo << 16) * inv, __uint_as_float(lo & 0xffff0000u) * inv,
+                    __uint_as_float(hi << 16) * inv, __uint_as_float(hi & 0xffff0000u) * inv);
+    };
+#pragma unroll
+    for (int k = 0; k < 8; ++k) xb[k] = e4m3x8_to_bf16(q4(xb[k].x, xb[k].y), q4(xb[k].z, xb[k].w));
+  };
+
+  Cursor cp{begin, 0, 0}, ld{begin, 0, 0};
+  load_rows(cp);
+  issue(ld, w0);
+  advance(ld);
+  issue(ld, w1);
+  advance(ld);
+
+  auto step = [&](uint4 (&wc)[kFrags], uint4 (&wi)[kFrags]) -> bool {
+    if (cp.u >= end) return false;
+    if (fresh) {
+      quantize_rows();
+      fresh = false;
+    }
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int f = 0; f < kFrags; ++f) {
+      acc = mfma32(e4m3x8_to_bf16(wc[f].x, wc[f].y), xb[2 * f], acc);
+      acc = mfma32(e4m3x8_to_bf16(wc[f].z, wc[f].w), xb[2 * f + 1], acc);
+    }
+    const Cursor cur = cp;
+    const int e = expert_of(cur.u);
+    const int b = cur.u % kUnitsPerExpert;
+    // Weight scales of this unit's rows and this wavefront's K group.
+    if (GATEUP) {
+      const float sg = Ws[((e * 2 + 0) * (kFF / 128) + b / 8) * (kHidden / 128) + wave] * xscale;
+      const float su = Ws[((e * 2 + 1) * (kFF / 128) + b / 8) * (kHidden / 128) + wave] * xscale;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S.red[wave][r][lane] = acc[r] * (r < 8 ? sg : su);
+    } else {
+      const float sd = Ws[(e * (kHidden / 128) + b / 4) * (kFF / 128) + wave] * xscale;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S.red[wave][r][lane] = acc[r] * sd;
+    }
+    advance(cp);
+    load_rows(cp);
+    issue(ld, wi);
+    advance(ld);
+    __syncthreads();
+    const int r0 = cur.pass * kPassRows;
+    const int rows = min(kPassRows, count_of(e) - r0);
+    const int* slots = S.G.list + S.G.off[e] + r0;
+    // Thread (r, ln) adds value r of lane ln over the wavefronts (token
+    // ln % 32, row mfma32_row(r, ln) of the unit's 32-row tile), for r =
+    // its wavefront index and, with fewer than 16 wavefronts, r + kWaves.
+    const int ln = threadIdx.x % kWave;
+    if (ln % 32 < rows) {
+      const int slot = slots[ln % 32];
+      for (int r = threadIdx.x / kWave; r < 16; r += kWaves) {
+        if (GATEUP) {
+          if (r < 8) {  // rows r (gate) and r + 8 (up) hold H column mfma32_row(r, ln)
+            float gs = 0.f, us = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+              gs += S.red[w][r][ln];
+              us += S.red[w][r + 8][ln];
+            }
+            H[static_cast<size_t>(slot) * kFF + b * 16 + mfma32_row(r, ln)] = f32_to_bf16(silu(gs) * us);
+          }
+        } else {
+          float ys = 0.f;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) ys += S.red[w][r][ln];
+          Y[static_cast<size_t>(slot) * kHidden + b * 32 + mfma32_row(r, ln)] = ys;
+        }
+      }
+    }
+    __syncthreads();
+    return true;
+  };
+  for (;;) {
+    if (!step(w0, w2)) break;
+    if (!step(w1, w0)) break;
+    if (!step(w2, w1)) break;
+  }
+}
+
+constexpr int kFp8GateupThreads = kHidden / 128 * kWave;  // 16 wavefronts
+constexpr int kFp8DownThreads = kFF / 128 * kWave;        // 12 wavefronts
+
+__global__ __launch_bounds__(kFp8GateupThreads) void gateup_decode_fp8_kernel(
+    const uint16_t* __restrict__ X, const uint8_t* __restrict__ Wq, const float* __restrict__ Ws,
+    const int32_t* __restrict__ idx, uint16_t* __restrict__ H, int N) {
+  __shared__ StreamShared S;
+  group_slots(idx, N, S.G);
+  stream_units_fp8<true>(X, Wq, Ws, H, nullptr, N, S);
+}
+
+__global__ __launch_bounds__(kFp8DownThreads) void down_decode_fp8_kernel(
+    const uint16_t* __restrict__ H, const uint8_t* __restrict__ Wq, const float* __restrict__ Ws,
+    const int32_t* __restrict__ idx, float* __restrict__ Y, int N) {
+  __shared__ StreamShared S;
+  group_slots(idx, N, S.G);
+  stream_units_fp8<false>(H, Wq, Ws, nullptr, Y, N, S);
+}
+
 __global__ __launch_bounds__(kStreamThreads) void gateup_decode_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wgu,
     const int32_t* __restrict__ idx, uint16_t* __restrict__ H, int N) {
@@ -327,6 +558,20 @@ hipError_t launch_down_decode(const uint16_t* H, const uint16_t* Wd, const int32
                               float* Y, int N, hipStream_t stream) {
   hipLaunchKernelGGL(down_decode_kernel, dim3(cu_count()), dim3(kStreamThreads), 0, stream, H, Wd,
                      idx, Y, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_gateup_decode_fp8(const uint16_t* X, const uint8_t* Wq, const float* scales,
+                                    const int32_t* idx, uint16_t* H, int N, hipStream_t stream) {
+  hipLaunchKernelGGL(gateup_decode_fp8_kernel, dim3(cu_count()), dim3(kFp8GateupThreads), 0, stream,
+                     X, Wq, scales, idx, H, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_decode_fp8(const uint16_t* H, const uint8_t* Wq, const float* scales,
+                                  const int32_t* idx, float* Y, int N, hipStream_t stream) {
+  hipLaunchKernelGGL(down_decode_fp8_kernel, dim3(cu_count()), dim3(kFp8DownThreads), 0, stream, H,
+                     Wq, scales, idx, Y, N);
   return hipGetLastError();
 }
 

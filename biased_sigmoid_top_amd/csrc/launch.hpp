@@ -17,6 +17,12 @@ hipError_t launch_pack_gateup(const uint16_t* Wg, const uint16_t* Wu, uint16_t* 
                               hipStream_t stream);
 hipError_t launch_pack_down(const uint16_t* Wd, uint16_t* out, hipStream_t stream);
 
+// FP8 (E4M3) block quantisation + packing of the expert weights.
+hipError_t launch_pack_fp8_gateup(const uint16_t* Wg, const uint16_t* Wu, uint8_t* out,
+                                  float* scales, hipStream_t stream);
+hipError_t launch_pack_fp8_down(const uint16_t* Wd, uint8_t* out, float* scales,
+                                hipStream_t stream);
+
 hipError_t launch_rmsnorm(const float* x, uint16_t* X, int64_t N, hipStream_t stream);
 
 // Scratch bytes of the router's partial logits for N tokens.
@@ -33,6 +39,12 @@ hipError_t launch_gateup_decode(const uint16_t* X, const uint16_t* Wgu, const in
                                 uint16_t* H, int N, hipStream_t stream);
 hipError_t launch_down_decode(const uint16_t* H, const uint16_t* Wd, const int32_t* idx,
                               float* Y, int N, hipStream_t stream);
+// The same with FP8 expert weights; the bf16 token rows are quantised per
+// group of 128 as they are loaded.
+hipError_t launch_gateup_decode_fp8(const uint16_t* X, const uint8_t* Wq, const float* scales,
+                                    const int32_t* idx, uint16_t* H, int N, hipStream_t stream);
+hipError_t launch_down_decode_fp8(const uint16_t* H, const uint8_t* Wq, const float* scales,
+                                  const int32_t* idx, float* Y, int N, hipStream_t stream);
 
 // Grouped path, LDS-tiled MFMA kernels (prefill-shaped batches).
 hipError_t launch_gateup_tiled(const uint16_t* X, const uint16_t* Wgu, const int32_t* offsets,

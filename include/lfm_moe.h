@@ -45,13 +45,15 @@
 extern "C" {
 #endif
 
-#define LFM_MOE_ABI_VERSION 1
+#define LFM_MOE_ABI_VERSION 2
 #define LFM_MOE_HIDDEN 2048
 #define LFM_MOE_EXPERTS 64
 #define LFM_MOE_TOPK 4
 #define LFM_MOE_FF 1536
 /* Largest N accepted: grouped rows (4N) and their element offsets stay in range. */
 #define LFM_MOE_MAX_TOKENS (1LL << 24)
+/* Largest N of lfm_moe_forward_fp8 (decode-shaped batches). */
+#define LFM_MOE_FP8_MAX_TOKENS 96
 
 typedef enum {
   LFM_MOE_OK = 0,
@@ -188,6 +190,59 @@ lfm_moe_status lfm_moe_block_forward(float* x_inout, const uint16_t* W_r, const 
 lfm_moe_status lfm_moe_block_forward_ws(float* x_inout, const uint16_t* W_r, const float* bias,
                                         const uint16_t* W_gateup, const uint16_t* W_down,
                                         int64_t N, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * FP8 experts (inferencekey.com page on the 24B reasoning MoE, German
+ * edition, "Für Engineers" part, the quantisation entry: the FP8 checkpoint
+ * is compressed-tensors FP8_BLOCK -- weights FP8 (E4M3) statically in
+ * 128 x 128 blocks, activations FP8 dynamically per group of 128, router
+ * not quantised).
+ *
+ * Quantisation of a block or group with largest magnitude amax > 0: codes
+ * E4M3(x * (448 / amax)) (OCP E4M3FN; fp32 arithmetic; round to nearest
+ * even; a value rounding to zero keeps its sign), dequantisation scale
+ * amax / 448 (fp32); amax = 0 gives zero codes and scale 0.
+ *
+ * lfm_moe_pack_fp8_gateup: W_gate, W_up [64, 1536, 2048] bf16 (read) ->
+ *   W_gateup_fp8 [64 * 3072 * 2048] bytes and scales_gateup
+ *   [64][2][12][16] fp32 (written): scale (e, m, rb, kb) of the 128 x 128
+ *   block rows 128 rb.., columns 128 kb.. of W_gate (m = 0) or W_up (m = 1).
+ *   Codes in 1 KB fragments of 32 rows x 32 columns: bytes [16 l, 16 l + 16)
+ *   of a fragment are row l % 32, bytes 0..7 its columns 8 h .. 8 h + 7 and
+ *   bytes 8..15 columns 16 + 8 h .. 16 + 8 h + 7 (h = l / 32); fragment
+ *   (e * 96 + b) * 64 + kp holds rows 16 b .. 16 b + 15 of W_gate as its
+ *   rows 0..15 and the same rows of W_up as its rows 16..31, columns
+ *   32 kp .. 32 kp + 31.
+ * lfm_moe_pack_fp8_down: W_down [64, 2048, 1536] bf16 (read) ->
+ *   W_down_fp8 [64 * 2048 * 1536] bytes, scales_down [64][16][12] fp32
+ *   (written); fragment (e * 64 + b) * 48 + kp holds rows 32 b .. 32 b + 31,
+ *   columns 32 kp .. 32 kp + 31, in the same lane order.
+ * lfm_moe_forward_fp8: the layer with these experts, for N <= 96 tokens
+ *   (the weight-streaming decode regime; larger N returns
+ *   LFM_MOE_ERR_INVALID_ARGUMENT).  Router and mixture weights as in
+ *   lfm_moe_forward; each expert's input rows (X, then the bf16 hidden rows)
+ *   are quantised per group of 128 features as above; accumulation fp32;
+ *   out [N, 2048] fp32.  Library-owned workspace, as lfm_moe_forward.
+ * lfm_moe_forward_fp8_ws: the same with a caller workspace, as
+ *   lfm_moe_forward_ws (same size and regions: the routing, the bf16 hidden
+ *   rows H and the fp32 expert rows Y, both in slot order t * 4 + j; the
+ *   regions of the grouped path are not written).
+ * Pointers 16-byte aligned; outputs must not overlap inputs; asynchronous on
+ * `stream`.
+ */
+lfm_moe_status lfm_moe_pack_fp8_gateup(const uint16_t* W_gate, const uint16_t* W_up,
+                                       uint8_t* W_gateup_fp8, float* scales_gateup,
+                                       hipStream_t stream);
+lfm_moe_status lfm_moe_pack_fp8_down(const uint16_t* W_down, uint8_t* W_down_fp8,
+                                     float* scales_down, hipStream_t stream);
+lfm_moe_status lfm_moe_forward_fp8(const uint16_t* X, const uint16_t* W_r, const float* bias,
+                                   const uint8_t* W_gateup_fp8, const float* scales_gateup,
+                                   const uint8_t* W_down_fp8, const float* scales_down, float* out,
+                                   int64_t N, hipStream_t stream);
+lfm_moe_status lfm_moe_forward_fp8_ws(const uint16_t* X, const uint16_t* W_r, const float* bias,
+                                      const uint8_t* W_gateup_fp8, const float* scales_gateup,
+                                      const uint8_t* W_down_fp8, const float* scales_down, float* out,
+                                      int64_t N, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Frees the library-owned workspaces (call with no work of this library in flight). */
 void lfm_moe_release(void);

@@ -164,6 +164,24 @@ def quantize_experts(W_gate, W_up, W_down) -> dict:
     return out
 
 
+def expert_hidden_fp8(Xq, q: dict, e: int, rounded: bool = True) -> np.ndarray:
+    """Hidden rows of expert e for dequantised input rows Xq:
+    silu(Xq W_gate^T) * (Xq W_up^T) with the dequantised weights, rounded to
+    bf16 (the rounding point of the bf16 layer) unless ``rounded`` is False."""
+    Wg = dequantize_blocks(q["gate_codes"][e], q["gate_scales"][e])
+    Wu = dequantize_blocks(q["up_codes"][e], q["up_scales"][e])
+    H = silu(Xq @ Wg.T) * (Xq @ Wu.T)
+    return round_bf16(H) if rounded else H
+
+
+def expert_down_fp8(H, q: dict, e: int) -> np.ndarray:
+    """Output rows of expert e for bf16 hidden rows H: H quantised per group
+    of 128, dequantised, times the dequantised W_down^T."""
+    hc, hs = quantize_groups(H)
+    Wd = dequantize_blocks(q["down_codes"][e], q["down_scales"][e])
+    return dequantize_groups(hc, hs) @ Wd.T
+
+
 def moe_apply_fp8(X, idx, w, q: dict) -> LayerResult:
     """The layer with FP8 experts, for given routing decisions.
 
@@ -188,14 +206,8 @@ def moe_apply_fp8(X, idx, w, q: dict) -> LayerResult:
         a, b = int(g.offsets[e]), int(g.offsets[e + 1])
         if a == b:
             continue
-        Xe = Xq[g.row2tok[a:b]]
-        Wg = dequantize_blocks(q["gate_codes"][e], q["gate_scales"][e])
-        Wu = dequantize_blocks(q["up_codes"][e], q["up_scales"][e])
-        Wd = dequantize_blocks(q["down_codes"][e], q["down_scales"][e])
-        He = round_bf16(silu(Xe @ Wg.T) * (Xe @ Wu.T))
-        H[a:b] = He
-        hc, hs = quantize_groups(He)
-        Y[a:b] = dequantize_groups(hc, hs) @ Wd.T
+        H[a:b] = expert_hidden_fp8(Xq[g.row2tok[a:b]], q, e)
+        Y[a:b] = expert_down_fp8(H[a:b], q, e)
     out = np.zeros((N, d))
     for j in range(k):
         out += w[:, j:j + 1] * Y[g.slot2row.reshape(N, k)[:, j]]
@@ -211,12 +223,7 @@ def dense_masked_forward_fp8(X, idx, w, q: dict) -> np.ndarray:
     Xq = dequantize_groups(xc, xs)
     out = np.zeros((N, X.shape[1]))
     for e in range(E):
-        Wg = dequantize_blocks(q["gate_codes"][e], q["gate_scales"][e])
-        Wu = dequantize_blocks(q["up_codes"][e], q["up_scales"][e])
-        Wd = dequantize_blocks(q["down_codes"][e], q["down_scales"][e])
-        He = round_bf16(silu(Xq @ Wg.T) * (Xq @ Wu.T))
-        hc, hs = quantize_groups(He)
-        Ye = dequantize_groups(hc, hs) @ Wd.T
+        Ye = expert_down_fp8(expert_hidden_fp8(Xq, q, e), q, e)
         m = (np.asarray(idx) == e).astype(np.float64)
         out += ((m * w).sum(axis=1))[:, None] * Ye
     return out

@@ -115,3 +115,23 @@ def check_grouping_valid(idx: np.ndarray, offsets: np.ndarray, row2slot: np.ndar
         a, b = offsets[e], offsets[e + 1]
         assert np.all(flat[r2s[a:b]] == e)
         assert np.all(np.diff(r2s[a:b] // 4) > 0), f"expert {e} rows not in token order"
+
+
+def oracle_fp8_experts(inp: dict, workers: int = 8) -> dict:
+    """oracle.fp8.quantize_experts of a workload's expert weights, one
+    (matrix, expert) block quantisation per task on a thread pool (numpy
+    releases the GIL in the element-wise work)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import fp8
+    jobs = [(name, e) for name in ("gate", "up", "down") for e in range(inp["W_gate"].shape[0])]
+    src = {"gate": inp["W_gate"], "up": inp["W_up"], "down": inp["W_down"]}
+    with ThreadPoolExecutor(workers) as pool:
+        res = list(pool.map(lambda j: fp8.quantize_blocks(src[j[0]][j[1]]), jobs))
+    q = {}
+    for name in ("gate", "up", "down"):
+        qs = [r for (n, _), r in zip(jobs, res) if n == name]
+        q[name + "_codes"] = np.stack([c for c, _ in qs])
+        q[name + "_scales"] = np.stack([s for _, s in qs])
+    return q
+

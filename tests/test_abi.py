@@ -116,5 +116,39 @@ def test_pack_checks(lib):
     assert lib.lfm_moe_pack_down(None, a[1], None) == _lib.ERR_INVALID_ARGUMENT
 
 
+def test_fp8_argument_checks(lib):
+    a = [_addr(i) for i in range(8)]
+    f = lib.lfm_moe_forward_fp8
+    assert f(*a, 0, None) == _lib.OK                      # N == 0: nothing launched
+    assert f(*a, -1, None) == _lib.ERR_INVALID_ARGUMENT
+    assert f(*a, _lib.FP8_MAX_TOKENS + 1, None) == _lib.ERR_INVALID_ARGUMENT
+    assert b"FP8_MAX_TOKENS" in lib.lfm_moe_last_error()
+    for i in range(8):
+        b = list(a)
+        b[i] = None
+        assert f(*b, 8, None) == _lib.ERR_INVALID_ARGUMENT
+        b = list(a)
+        b[i] = a[i] + 4
+        assert f(*b, 8, None) == _lib.ERR_INVALID_ARGUMENT
+    b = list(a)
+    b[7] = a[3] + 1024                                      # out inside the gate/up codes
+    assert f(*b, 8, None) == _lib.ERR_INVALID_ARGUMENT
+    fw = lib.lfm_moe_forward_fp8_ws
+    need = lib.lfm_moe_workspace_bytes(8)
+    ws = _addr(9)
+    assert fw(*a, 0, None, 0, None) == _lib.OK
+    assert fw(*a, 8, None, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert fw(*a, 8, ws + 16, need, None) == _lib.ERR_INVALID_ARGUMENT      # not 256-aligned
+    assert fw(*a, 8, ws, need - 1, None) == _lib.ERR_WORKSPACE_TOO_SMALL
+    assert fw(*a, 8, a[7] - 256, need, None) == _lib.ERR_INVALID_ARGUMENT   # overlaps out
+    assert fw(*a, _lib.FP8_MAX_TOKENS + 1, ws, 1 << 40, None) == _lib.ERR_INVALID_ARGUMENT
+    g, d = lib.lfm_moe_pack_fp8_gateup, lib.lfm_moe_pack_fp8_down
+    assert g(a[0], a[1], a[2], None, None) == _lib.ERR_INVALID_ARGUMENT
+    assert g(a[0], a[1], a[0] + 512, a[3], None) == _lib.ERR_INVALID_ARGUMENT   # codes over W_gate
+    assert g(a[0], a[1], a[2], a[2] + 256, None) == _lib.ERR_INVALID_ARGUMENT   # scales over codes
+    assert d(a[0], a[1], a[1] + 4, None) == _lib.ERR_INVALID_ARGUMENT
+    assert d(a[0], a[0] + 64, a[2], None) == _lib.ERR_INVALID_ARGUMENT
+
+
 def test_release_without_allocation_is_a_no_op(lib):
     lib.lfm_moe_release()
