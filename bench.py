@@ -4,8 +4,9 @@
 One step = one lfm_moe_forward (router, dispatch, gate/up, down, combine)
 over one batch of synthetic tokens whose inputs and weights are already
 resident in HBM.  The headline workload is the decode-shaped layer (N = 64
-tokens, seed 1); the prefill-shaped layer (N = 4096, seed 2) is measured in
-the same run and reported beside it.  Expert weights are cycled over
+tokens, seed 1); the prefill-shaped layer (N = 4096, seed 2) and the same
+decode layer with FP8 block-scaled experts are measured in the same run and
+reported beside it.  Expert weights are cycled over
 `--copies` identical device copies so that the 256 MB Infinity Cache does
 not serve repeated steps.
 
@@ -50,6 +51,23 @@ def gateup_bytes(A, N):
 
 def gateup_flops(N):
     return K * N * 2 * (2 * FF) * D
+
+
+# FP8 experts: one byte per weight plus a fp32 scale per 128 x 128 block.
+FP8_GATEUP_W_BYTES = 2 * FF * D + 2 * (FF // 128) * (D // 128) * 4   # 6,292,992 per active expert
+FP8_DOWN_W_BYTES = D * FF + (D // 128) * (FF // 128) * 4             # 3,146,496 per active expert
+
+
+def fp8_layer_bytes(A, N):
+    return A * (FP8_GATEUP_W_BYTES + FP8_DOWN_W_BYTES) + ROUTER_BYTES + N * (D * 2 + D * 4)
+
+
+def fp8_gateup_bytes(A, N):
+    return A * FP8_GATEUP_W_BYTES + N * D * 2 + K * N * FF * 2
+
+
+def fp8_down_bytes(A, N):
+    return A * FP8_DOWN_W_BYTES + K * N * FF * 2 + K * N * D * 4
 
 
 def down_bytes(A, N):
@@ -107,13 +125,32 @@ def prepare_layer(name, N, seed, layer, copies):
     return p
 
 
+def prepare_fp8(p):
+    """FP8 codes and scales of a prepared workload's experts (packed on the
+    device), one set per weight copy."""
+    import biased_sigmoid_top_amd as moe
+    import torch
+    layer = p["layer"]
+    dev = torch.device("cuda")
+    gu = moe.pack_fp8_gateup(layer["W_gate"].to(dev), layer["W_up"].to(dev))
+    dn = moe.pack_fp8_down(layer["W_down"].contiguous().to(dev))
+    c = len(p["Wgu"])
+    q = dict(p, fp8=True,
+             Gq=[gu] + [tuple(t.clone() for t in gu) for _ in range(c - 1)],
+             Dq=[dn] + [tuple(t.clone() for t in dn) for _ in range(c - 1)])
+    return q
+
+
 def time_steps(p, steps, warmup):
     import torch
     import biased_sigmoid_top_amd as moe
     c = len(p["Wgu"])
 
     def step(i):
-        moe.forward(p["X"], p["W_r"], p["bias"], p["Wgu"][i % c], p["Wd"][i % c], p["out"])
+        if p.get("fp8"):
+            moe.forward_fp8(p["X"], p["W_r"], p["bias"], p["Gq"][i % c], p["Dq"][i % c], p["out"])
+        else:
+            moe.forward(p["X"], p["W_r"], p["bias"], p["Wgu"][i % c], p["Wd"][i % c], p["out"])
 
     for i in range(warmup):
         step(i)
@@ -157,6 +194,36 @@ def summarize(p, wall_ms, per_kernel):
         down_gbs=down_bytes(A, N) / (dn_ms * 1e-3) / 1e9 if dn_ms else None,
         down_tflops=down_flops(N) / (dn_ms * 1e-3) / 1e12 if dn_ms else None,
     )
+
+
+def summarize_fp8(p, wall_ms, per_kernel, label, note):
+    """Summary of FP8-expert steps: bytes are the FP8 codes and scales of the
+    active experts, the router, x in and out."""
+    N = p["N"]
+    A = sum(1 for c in p["counts"] if c > 0)
+    s = wall_ms * 1e-3
+    gu_ms, dn_ms = per_kernel["gateup"], per_kernel["down"]
+    gu_gbs = fp8_gateup_bytes(A, N) / (gu_ms * 1e-3) / 1e9
+    gbs = fp8_layer_bytes(A, N) / s / 1e9
+    return dict(config=label, N=N, dtype="fp8-e4m3 experts (bf16 router, fp32 accumulation)",
+                active_experts=A, max_tokens_per_expert=max(p["counts"]), ms_per_step=wall_ms,
+                tokens_per_s=N / s, gbs=gbs, hbm_frac=gbs / HBM_PEAK_GBS, bound="hbm",
+                roofline_frac=gbs / HBM_PEAK_GBS, kernel_ms=per_kernel,
+                roofline=dict(bound="hbm", kernel="gateup_decode_fp8", achieved=gu_gbs,
+                              peak=HBM_PEAK_GBS, unit="GB/s", frac=gu_gbs / HBM_PEAK_GBS,
+                              bytes_per_launch=fp8_gateup_bytes(A, N), avg_launch_ms=gu_ms,
+                              down_gbs=fp8_down_bytes(A, N) / (dn_ms * 1e-3) / 1e9),
+                note=note)
+
+
+def measure_fp8(p, steps, warmup, label, note):
+    q = prepare_fp8(p)
+    log(f"timing {label} (FP8 experts, {p['name']}): {steps} steps")
+    w, k = time_steps(q, steps, warmup)
+    e = summarize_fp8(q, w, k, label, note)
+    log(json.dumps(e))
+    del q
+    return e
 
 
 def kernel_source_digest(path):
@@ -281,6 +348,9 @@ def main():
     h = summarize(head, wall_ms, per_kernel)
     log(json.dumps(h))
 
+    fp8 = measure_fp8(head, args.steps, args.warmup, "F1",
+                      f"supplementary: {args.workload} with FP8 block-scaled experts")
+
     second = None
     if args.secondary != "none":
         p2 = prepare(args.secondary, args.copies)
@@ -298,6 +368,7 @@ def main():
         cpu = cpu_baseline(head, args.cpu_seconds)
 
     line = build_line(args, h, head["seed"], second, cpu)
+    line["fp8_decode"] = fp8
     if args.configs:
         del head
         torch.cuda.empty_cache()
@@ -425,6 +496,9 @@ def measure_configs(args):
         e = config_entry(label, summarize(p, w, k), note)
         log(json.dumps(e))
         out.append(e)
+        if label == "C1u":
+            out.append(measure_fp8(p, steps, args.warmup, "F1u",
+                                   "supplementary: C1u with FP8 block-scaled experts"))
         del p
         torch.cuda.empty_cache()
     e = measure_stack(max(3, args.steps // 40), 1)

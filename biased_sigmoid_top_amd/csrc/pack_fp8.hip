@@ -1,5 +1,6 @@
 // FP8 (E4M3) block quantisation of the expert weights, packed into the
-// operand-fragment layout of the 32x32x16 FP8 MFMA.
+// operand-fragment layout of the 32x32x16 MFMAs (each lane's 8 codes of a
+// 16-wide K step are its operand, widened to bf16 in registers).
 //
 // Method: the inferencekey.com page on the 24B reasoning MoE (German
 // edition, "Für Engineers" part, the quantisation entry) describes the

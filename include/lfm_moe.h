@@ -221,8 +221,10 @@ lfm_moe_status lfm_moe_block_forward_ws(float* x_inout, const uint16_t* W_r, con
  *   (the weight-streaming decode regime; larger N returns
  *   LFM_MOE_ERR_INVALID_ARGUMENT).  Router and mixture weights as in
  *   lfm_moe_forward; each expert's input rows (X, then the bf16 hidden rows)
- *   are quantised per group of 128 features as above; accumulation fp32;
- *   out [N, 2048] fp32.  Library-owned workspace, as lfm_moe_forward.
+ *   are quantised per group of 128 features as above; the products of
+ *   codes are exact and summed in fp32, then scaled by weight scale x
+ *   activation scale per 128-wide K group; out [N, 2048] fp32.
+ *   Library-owned workspace, as lfm_moe_forward.
  * lfm_moe_forward_fp8_ws: the same with a caller workspace, as
  *   lfm_moe_forward_ws (same size and regions: the routing, the bf16 hidden
  *   rows H and the fp32 expert rows Y, both in slot order t * 4 + j; the

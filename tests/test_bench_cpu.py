@@ -25,6 +25,10 @@ def test_algorithmic_counts():
     assert bench.FLOP_PER_TOKEN == 262_144 + 75_497_472
     assert bench.layer_bytes(40, 64) == 40 * 18_874_368 + 262_144 + 256 + 64 * 12_288
     assert bench.gateup_flops(4096) == 4 * 4096 * 2 * 3072 * 2048
+    # FP8 experts: one byte per weight and a fp32 scale per 128 x 128 block
+    # (gate and up: 2 x 12 x 16 blocks, down: 16 x 12).
+    assert bench.FP8_GATEUP_W_BYTES + bench.FP8_DOWN_W_BYTES == 9_437_184 + (384 + 192) * 4
+    assert bench.fp8_gateup_bytes(40, 64) == 40 * 6_292_992 + 64 * 4096 + 256 * 3072
 
 
 def _summary(N, A, ms, gu_ms):
