@@ -211,6 +211,7 @@ def summarize_fp8(p, wall_ms, per_kernel, label, note):
                 roofline_frac=gbs / HBM_PEAK_GBS, kernel_ms=per_kernel,
                 roofline=dict(bound="hbm", kernel="gateup_decode_fp8", achieved=gu_gbs,
                               peak=HBM_PEAK_GBS, unit="GB/s", frac=gu_gbs / HBM_PEAK_GBS,
+                              traffic=measured_traffic(p["name"], "gateup_fp8"),
                               bytes_per_launch=fp8_gateup_bytes(A, N), avg_launch_ms=gu_ms,
                               down_gbs=fp8_down_bytes(A, N) / (dn_ms * 1e-3) / 1e9),
                 note=note)
@@ -232,11 +233,11 @@ def kernel_source_digest(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, kernel="gateup"):
     """HBM bytes per gate/up launch from the committed rocprofv3 counter
     summary of this workload, or None when it is missing or was taken on a
     different version of the kernel source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_gateup_{workload}.md")
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -348,8 +349,11 @@ def main():
     h = summarize(head, wall_ms, per_kernel)
     log(json.dumps(h))
 
-    fp8 = measure_fp8(head, args.steps, args.warmup, "F1",
-                      f"supplementary: {args.workload} with FP8 block-scaled experts")
+    from biased_sigmoid_top_amd._lib import FP8_MAX_TOKENS
+    fp8 = None
+    if head["N"] <= FP8_MAX_TOKENS:
+        fp8 = measure_fp8(head, args.steps, args.warmup, "F1",
+                          f"supplementary: {args.workload} with FP8 block-scaled experts")
 
     second = None
     if args.secondary != "none":
