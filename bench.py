@@ -171,7 +171,24 @@ def time_steps(p, steps, warmup):
     moe.timing_enable(False)
     per_kernel = {s: (ms / n if n else 0.0) for s, (ms, n) in stages.items()}
     assert torch.isfinite(p["out"]).all().item(), "non-finite layer output"
+
+    # Third pass: per-step device times from event pairs around each step.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        step(i)
+        b.record()
+    torch.cuda.synchronize()
+    per_kernel["step_percentiles_ms"] = percentiles([a.elapsed_time(b) for a, b in evs])
     return wall_ms, per_kernel
+
+
+def percentiles(xs):
+    """p10 / median / p90 of per-step times (ms)."""
+    import numpy as np
+    q = np.percentile(np.asarray(xs, dtype=np.float64), [10, 50, 90])
+    return dict(p10=float(q[0]), p50=float(q[1]), p90=float(q[2]))
 
 
 def summarize(p, wall_ms, per_kernel):
@@ -252,12 +269,12 @@ def measured_traffic(workload, kernel="gateup"):
 
 def roofline(h, workload):
     """Roofline object of the dominant kernel (gate/up): HBM-bound while the
-    arithmetic intensity is far below the ridge (N <= 512), bf16-MFMA-bound
-    above."""
+    arithmetic intensity is far below the ridge (hbm_bound), bf16-MFMA-bound
+    otherwise."""
     from biased_sigmoid_top_amd._lib import DECODE_MAX_TOKENS
     N, A = h["N"], h["active_experts"]
     ms = h["kernel_ms"]["gateup"]
-    if N <= 512:
+    if hbm_bound(h):
         kernel = "gateup_decode" if N <= DECODE_MAX_TOKENS else "gateup_tiled"
         return dict(bound="hbm", kernel=kernel, achieved=h["gateup_gbs"],
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=h["gateup_gbs"] / HBM_PEAK_GBS,
@@ -415,8 +432,16 @@ CONFIGS = (
 )
 
 
+def hbm_bound(h):
+    """HBM-bound while the layer's algorithmic intensity (FLOP per byte) is
+    below half the ridge point of the two peaks (2.5 PFLOP/s / 8 TB/s = 312
+    FLOP/B): decode and verification batches up to a few hundred tokens per
+    expert; the N = 4096 and N = 16384 workloads sit at or above the ridge."""
+    return h["layer_tflops"] * 1e3 / h["layer_gbs"] < 0.5 * BF16_PEAK_TFLOPS * 1e3 / HBM_PEAK_GBS
+
+
 def config_entry(label, h, note=None):
-    hbm = h["N"] <= 512
+    hbm = hbm_bound(h)
     e = dict(config=label, N=h["N"], active_experts=h["active_experts"],
              max_tokens_per_expert=h["max_tokens_per_expert"], ms_per_step=h["ms_per_step"],
              tokens_per_s=h["tokens_per_s"], gbs=h["layer_gbs"], hbm_frac=h["layer_hbm_frac"],
@@ -460,10 +485,12 @@ def measure_stack(steps, warmup):
         active.append(int((torch.bincount(sel.reshape(-1), minlength=E) > 0).sum()))
     del ws
 
+    ws = moe.alloc_workspace(N)
+
     def stack_pass():
         x.copy_(x0)
         for blk in blocks:
-            moe.block_forward(x, *blk)
+            moe.block_forward(x, *blk, workspace=ws)
 
     for _ in range(warmup):
         stack_pass()
@@ -474,6 +501,29 @@ def measure_stack(steps, warmup):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
     assert torch.isfinite(x).all().item(), "non-finite stack output"
+    eager_x = x.clone()
+
+    # The same stack captured once in a HIP graph (the library records no
+    # allocation, memset or host synchronisation) and replayed.
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        stack_pass()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        stack_pass()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(x, eager_x), "graph replay differs from the eager stack"
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms_graph = (time.perf_counter() - t0) * 1e3 / steps
+    assert torch.equal(x, eager_x), "graph replay differs from the eager stack"
+    del graph
     bytes_ = sum(a * EXPERT_BYTES + ROUTER_BYTES for a in active) + nb * N * D * 4 * 2
     flops = nb * N * FLOP_PER_TOKEN
     s = ms * 1e-3
@@ -483,7 +533,9 @@ def measure_stack(steps, warmup):
              hbm_frac=bytes_ / s / 1e9 / HBM_PEAK_GBS, tflops=flops / s / 1e12,
              mfma_frac=flops / s / 1e12 / BF16_PEAK_TFLOPS, bound="hbm",
              roofline_frac=bytes_ / s / 1e9 / HBM_PEAK_GBS,
-             note="one step = the whole stack (a copy of x0, then 38 block calls)")
+             ms_per_step_graph=ms_graph, tokens_per_s_graph=N / (ms_graph * 1e-3),
+             note="one step = the whole stack (a copy of x0, then 38 block calls); "
+                  "the _graph figures replay the same step captured in one HIP graph")
     del blocks
     torch.cuda.empty_cache()
     return e

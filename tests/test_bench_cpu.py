@@ -33,7 +33,8 @@ def test_algorithmic_counts():
 
 def _summary(N, A, ms, gu_ms):
     h = dict(N=N, active_experts=A, max_tokens_per_expert=17, ms_per_step=ms,
-             tokens_per_s=N / (ms * 1e-3), layer_gbs=1.0, layer_hbm_frac=0.1, layer_tflops=1.0,
+             tokens_per_s=N / (ms * 1e-3), layer_gbs=bench.layer_bytes(A, N) / (ms * 1e-3) / 1e9,
+             layer_hbm_frac=0.1, layer_tflops=N * bench.FLOP_PER_TOKEN / (ms * 1e-3) / 1e12,
              layer_mfma_frac=0.1, kernel_ms=dict(gateup=gu_ms, down=0.05, route=0.01),
              gateup_gbs=bench.gateup_bytes(A, N) / (gu_ms * 1e-3) / 1e9,
              gateup_tflops=bench.gateup_flops(N) / (gu_ms * 1e-3) / 1e12)
@@ -54,3 +55,7 @@ def test_json_line_and_roofline_selection():
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-12
     q = line["prefill"]["roofline"]
     assert q["bound"] == "mfma" and q["unit"] == "TFLOP/s" and q["peak"] == 2500.0
+    # The bound follows the algorithmic intensity: 640 tokens on 48 experts
+    # (about 53 FLOP/B) is HBM-bound although N > 512.
+    assert bench.hbm_bound(_summary(640, 48, 0.22, 0.12))
+    assert not bench.hbm_bound(_summary(16384, 44, 1.5, 0.8))

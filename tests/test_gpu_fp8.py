@@ -192,3 +192,16 @@ def test_fp8_zero_tokens_and_limit(moe):
     big = torch.zeros(97, 2048, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(RuntimeError):
         moe.forward_fp8(big, dev["W_r"], dev["bias"], dev["gateup_fp8"], dev["down_fp8"])
+
+
+def test_fp8_graph_capture_replays_match_eager(moe):
+    """The FP8 layer's _ws form captured in a HIP graph replays to the eager
+    result, bit for bit, with eager work between the replays."""
+    from test_gpu_parity import _graph_replays_match
+    inp, dev, q = _decode_case(moe)
+    N = inp["X"].shape[0]
+    ws = moe.alloc_workspace(N)
+    args = (dev["X"], dev["W_r"], dev["bias"], dev["gateup_fp8"], dev["down_fp8"])
+    _step(f"graph capture forward_fp8 N={N}")
+    eager = moe.forward_fp8(*args, workspace=ws).clone()
+    _graph_replays_match(moe, lambda out: moe.forward_fp8(*args, out=out, workspace=ws), eager)

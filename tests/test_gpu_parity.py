@@ -187,6 +187,40 @@ def test_intermediates_with_poisoned_workspace(moe, name):
         assert np.max(np.abs(Y - Y_ref)) <= 2e-2 * y_rms
 
 
+def _graph_replays_match(moe, run, eager):
+    """Captures run(out) in a HIP graph and checks three replays against
+    `eager`, bit for bit, with eager work and synchronisations between them."""
+    out = torch.empty_like(eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(out)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(out)
+    for i in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i} differs from the eager call"
+        run(torch.empty_like(eager))
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["decode_n64", "prefill_n4096"])
+def test_graph_capture_replays_match_eager(moe, name):
+    """The _ws form records no allocation, memset or host synchronisation, so
+    the layer can be captured in a HIP graph and replayed."""
+    inp, dev, r = case(name)
+    N = inp["X"].shape[0]
+    ws = moe.alloc_workspace(N)
+    args = (dev["X"], dev["W_r"], dev["bias"], dev["W_gateup"], dev["W_down"])
+    _step(f"graph capture {name} N={N}")
+    eager = moe.forward(*args, workspace=ws).clone()
+    _graph_replays_match(moe, lambda out: moe.forward(*args, out=out, workspace=ws), eager)
+
+
 def test_bitwise_determinism(moe):
     inp, dev, r = case("prefill_n4096")
     _step("determinism prefill_n4096")
