@@ -60,12 +60,12 @@ __device__ __forceinline__ int swz(int c) { return c + 8 * (c & 1); }
 // 4 wavefronts (128 x 256), two per CU -- its 8 column tiles then deal
 // evenly over the CUs where 4 wide ones would leave a half-empty last round
 // (N = 4096: down 159 us against 164; gate/up 256 against 267 with 4).
-template <bool GATEUP, int FB_>
+template <bool GATEUP, int FB_, int WAVES_ = (GATEUP ? 8 : 4)>
 struct TileShape {
   static constexpr int FB = FB_;  // packed 32-row blocks per wavefront
-  static constexpr int kWaves = GATEUP ? 8 : 4;
+  static constexpr int kWaves = WAVES_;
   static constexpr int kThreads = kWaves * kWave;
-  static constexpr int kPerCu = GATEUP ? 1 : 2;  // workgroups per CU the register budget is set for
+  static constexpr int kPerCu = kWaves == 8 ? 1 : 2;  // workgroups per CU the register budget is set for
   static constexpr int kChunks = kBM * (kPairBytes / 16) / kThreads;  // 16-byte token pieces per thread per pair
   static constexpr int kRowStep = kThreads / 8;  // tile rows one pass of the workgroup loads
   static constexpr int K = GATEUP ? kHidden : kFF;
@@ -81,13 +81,14 @@ struct TileShape {
   static_assert(kGroup * kColTiles % kXcds == 0, "a launch group deals evenly over the XCDs");
 };
 
-template <bool GATEUP, int FB_>
-__global__ __launch_bounds__((TileShape<GATEUP, FB_>::kThreads), (TileShape<GATEUP, FB_>::kPerCu))
+template <bool GATEUP, int FB_, int WAVES_>
+__global__ __launch_bounds__((TileShape<GATEUP, FB_, WAVES_>::kThreads),
+                             (TileShape<GATEUP, FB_, WAVES_>::kPerCu))
 void expert_tiled_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Wp,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ row2slot,
     uint16_t* __restrict__ H, float* __restrict__ Y) {
-  using T = TileShape<GATEUP, FB_>;
+  using T = TileShape<GATEUP, FB_, WAVES_>;
   constexpr int FB = T::FB;
   static_assert(T::kStages % kWSlots == 0, "the stage loop is unrolled by the ring size");
   // Token fragments: 2 pair buffers x (2 stages x 4 token blocks x kKS steps).
@@ -278,30 +279,43 @@ void expert_tiled_kernel(
   }
 }
 
-template <bool GATEUP, int FB>
+template <bool GATEUP, int FB, int WAVES>
 int64_t tiled_grid(int64_t N) {
-  using T = TileShape<GATEUP, FB>;
+  using T = TileShape<GATEUP, FB, WAVES>;
   const int64_t groups = (max_mtiles(N, kBM) + T::kGroup - 1) / T::kGroup;
   return groups * T::kGroup * T::kColTiles;
 }
 
-// Gate/up column tiles: 512 weight rows (two blocks per wavefront), or 256
-// (one) for batches of 257 to 2048 tokens.  There the experts have few
-// m-tiles each, and 512-row tiles make barely more workgroups than the
-// device holds, so a second, nearly empty round follows the first; half as
-// wide, twice as many tiles finish in about one round and a fifth.
-// Measured gate/up, 512-row against 256-row tiles: N = 256: 95 vs 99 us;
-// 384: 139 vs 105; 1024: 146 vs 133; 2048: 188 vs 177; 4096: 245 vs 261.
-bool narrow_gateup_tiles(int64_t N) { return N > 256 && N <= 2048; }
+// Column tiles by batch size.  With few tokens per expert the kernels are
+// bound by the weight stream, each expert has one or two m-tiles, and the
+// tile count barely exceeds what the device holds, so the last round of
+// tiles runs on a fraction of the CUs; narrower tiles make that tail
+// shorter.  Gate/up: 512 weight rows (8 wavefronts x two blocks) by
+// default, 128 rows (4 wavefronts x one block, two workgroups per CU) for
+// 193-512 tokens, 256 rows (8 x one) for 513-2048.  Down: 256 rows (4 x two)
+// by default, 128 rows (4 x one) up to 512 tokens.  Measured (layer of seed
+// 4, first N tokens; gate/up 512 / 128 / 256 rows, us): N = 160: 92 / 97 /
+// -; 256: 132 / 112 / -; 320: - / 112 / 117; 512: - / 119 / 121; 640: - /
+// 130 / 126; 1024: - / 140 / 133; earlier, 4096: 245 / - / 261.  Down 256 /
+// 128 rows: N = 128: 61 / 52; 320: 71 / 61; 512: 77 / 69; 640: 74 / 75;
+// 2048: 104 / 108.
+enum class GateupTiles { kWide, kNarrow4, kNarrow8 };
+GateupTiles gateup_tiles(int64_t N) {
+  if (N > 192 && N <= 512) return GateupTiles::kNarrow4;
+  if (N > 512 && N <= 2048) return GateupTiles::kNarrow8;
+  return GateupTiles::kWide;
+}
+bool narrow_down_tiles(int64_t N) { return N <= 512; }
 
-template <bool GATEUP, int FB, typename Out>
+template <bool GATEUP, int FB, int WAVES = (GATEUP ? 8 : 4), typename Out>
 hipError_t launch_tiled(const uint16_t* A, const uint16_t* W, const int32_t* offsets,
                         const int32_t* row2slot, Out* out, int64_t N, hipStream_t stream) {
   uint16_t* H = nullptr;
   float* Y = nullptr;
   if constexpr (GATEUP) H = out; else Y = out;
-  hipLaunchKernelGGL((expert_tiled_kernel<GATEUP, FB>), dim3(tiled_grid<GATEUP, FB>(N)),
-                     dim3(TileShape<GATEUP, FB>::kThreads), 0, stream, A, W, offsets, row2slot, H, Y);
+  hipLaunchKernelGGL((expert_tiled_kernel<GATEUP, FB, WAVES>), dim3(tiled_grid<GATEUP, FB, WAVES>(N)),
+                     dim3(TileShape<GATEUP, FB, WAVES>::kThreads), 0, stream, A, W, offsets, row2slot,
+                     H, Y);
   return hipGetLastError();
 }
 
@@ -310,13 +324,20 @@ hipError_t launch_tiled(const uint16_t* A, const uint16_t* W, const int32_t* off
 hipError_t launch_gateup_tiled(const uint16_t* X, const uint16_t* Wgu, const int32_t* offsets,
                                const int32_t* row2slot, uint16_t* H, int64_t N,
                                hipStream_t stream) {
-  return narrow_gateup_tiles(N) ? launch_tiled<true, 1>(X, Wgu, offsets, row2slot, H, N, stream)
-                                : launch_tiled<true, 2>(X, Wgu, offsets, row2slot, H, N, stream);
+  switch (gateup_tiles(N)) {
+    case GateupTiles::kNarrow4:
+      return launch_tiled<true, 1, 4>(X, Wgu, offsets, row2slot, H, N, stream);
+    case GateupTiles::kNarrow8:
+      return launch_tiled<true, 1>(X, Wgu, offsets, row2slot, H, N, stream);
+    default:
+      return launch_tiled<true, 2>(X, Wgu, offsets, row2slot, H, N, stream);
+  }
 }
 
 hipError_t launch_down_tiled(const uint16_t* H, const uint16_t* Wd, const int32_t* offsets,
                              const int32_t* row2slot, float* Y, int64_t N, hipStream_t stream) {
-  return launch_tiled<false, 2>(H, Wd, offsets, row2slot, Y, N, stream);
+  return narrow_down_tiles(N) ? launch_tiled<false, 1, 4>(H, Wd, offsets, row2slot, Y, N, stream)
+                              : launch_tiled<false, 2>(H, Wd, offsets, row2slot, Y, N, stream);
 }
 
 }  // namespace lfm

@@ -252,7 +252,7 @@ def _layer_case(N, seed_z, bias_override=None):
     return inp, dev
 
 
-@pytest.mark.parametrize("N", [1, 2, 17, 63, 65, 96, 97, 257, 1000, 2049])
+@pytest.mark.parametrize("N", [1, 2, 17, 63, 65, 96, 97, 193, 257, 511, 513, 1000, 2049])
 def test_ragged_token_counts(moe, N):
     inp, dev = _layer_case(N, 100 + N)
     r = oracle.route(inp["X"], inp["W_r"], inp["bias"])
@@ -279,7 +279,7 @@ def test_every_token_on_the_same_four_experts(moe, N):
     check_out(_np(out), expected_outputs(inp, r, np.arange(N), alt))
 
 
-@pytest.mark.parametrize("c", [1, 8, 16, 64])
+@pytest.mark.parametrize("c", [1, 8, 16, 32, 64])
 def test_verification_batches(moe, c):
     """Speculative-decoding verification batches: c requests x 10 tokens, the
     first 10c tokens of one layer's inputs (decode path up to 96 tokens, the
