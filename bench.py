@@ -234,8 +234,10 @@ def summarize_fp8(p, wall_ms, per_kernel, label, note):
                 note=note)
 
 
-def measure_fp8(p, steps, warmup, label, note):
-    q = prepare_fp8(p)
+def measure_fp8(p, steps, warmup, label, note, q=None):
+    """FP8 steps on workload p (packing its experts unless q, a prepare_fp8
+    result of the same layer, is given)."""
+    q = prepare_fp8(p) if q is None else dict(q, N=p["N"], X=p["X"], out=p["out"], counts=p["counts"])
     log(f"timing {label} (FP8 experts, {p['name']}): {steps} steps")
     w, k = time_steps(q, steps, warmup)
     e = summarize_fp8(q, w, k, label, note)
@@ -571,7 +573,9 @@ def measure_verify(args):
     import synth
     log("generating the verification-batch layer (seed 5)")
     Nmax = max(synth.verify_batch_sizes())
+    from biased_sigmoid_top_amd._lib import FP8_MAX_TOKENS
     full = prepare_layer("verify", Nmax, synth.VERIFY["seed"], synth.verify_inputs(), args.copies)
+    q = prepare_fp8(full)
     out = []
     for c, N in zip(synth.VERIFY["concurrency"], synth.verify_batch_sizes()):
         p = dict(full, N=N, X=full["X"][:N], out=full["out"][:N])
@@ -582,7 +586,11 @@ def measure_verify(args):
                          f"verification batch: {c} requests x 10 tokens (supplementary)")
         log(json.dumps(e))
         out.append(e)
-    del full
+        if N <= FP8_MAX_TOKENS:
+            out.append(measure_fp8(p, args.steps, args.warmup, f"FV{c}",
+                                   f"verification batch: {c} requests x 10 tokens, FP8 experts "
+                                   "(supplementary)", q))
+    del full, q
     torch.cuda.empty_cache()
     return out
 

@@ -22,7 +22,7 @@ ERR_HIP = 4
 
 WS_IDX, WS_W, WS_BLOCKCOUNTS, WS_OFFSETS, WS_ROW2SLOT, WS_H, WS_Y, WS_X, WS_ROUTER_PARTIAL = range(9)
 DECODE_MAX_TOKENS = 96
-FP8_MAX_TOKENS = 96
+FP8_MAX_TOKENS = 256
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64

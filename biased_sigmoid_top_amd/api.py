@@ -139,7 +139,7 @@ def pack_fp8_down(W_down, stream=None):
 
 
 def forward_fp8(X, W_r, bias, gateup_fp8, down_fp8, out=None, workspace=None, stream=None):
-    """The layer with FP8 experts (N <= 96): gateup_fp8 and down_fp8 are the
+    """The layer with FP8 experts (N <= 256): gateup_fp8 and down_fp8 are the
     (codes, scales) pairs of pack_fp8_gateup / pack_fp8_down.  With
     ``workspace`` the _ws entry point is used."""
     N = X.shape[0]

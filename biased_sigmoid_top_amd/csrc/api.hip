@@ -275,7 +275,7 @@ lfm_moe_status check_fp8_args(const uint16_t* X, const uint16_t* W_r, const floa
                               int64_t N) {
   if (N < 0) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "N must be >= 0");
   if (N > LFM_MOE_FP8_MAX_TOKENS)
-    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "N exceeds LFM_MOE_FP8_MAX_TOKENS (FP8 experts: decode batches)");
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "N exceeds LFM_MOE_FP8_MAX_TOKENS (FP8 experts: batches of up to 256 tokens)");
   if (N == 0) return LFM_MOE_OK;
   if (!X || !W_r || !bias || !W_gateup_fp8 || !scales_gateup || !W_down_fp8 || !scales_down || !out)
     return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "null tensor pointer");

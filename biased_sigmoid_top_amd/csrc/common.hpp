@@ -18,7 +18,8 @@ constexpr float kRmsEps = 1e-6f;
 // counts fit one 32-token pass (N = 96: 150 us against 190 us for the
 // grouped path); beyond it they stream an expert's weights once per pass
 // (N = 128: 307 us against 192 us).
-constexpr int kDecodeMaxTokens = 96;
+constexpr int kDecodeMaxTokens = 96;   // bf16 layer: weight-streaming path up to here
+constexpr int kStreamMaxTokens = 256;  // tokens the weight-streaming kernels can group (FP8 layer limit)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

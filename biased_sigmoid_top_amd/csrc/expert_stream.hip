@@ -45,7 +45,7 @@ namespace {
 constexpr int kPassRows = 32;                      // tokens per pass (one 32x32 MFMA tile)
 constexpr int kStreamThreads = 1024;               // 16 wavefronts: one workgroup per CU
 constexpr int kStreamWaves = kStreamThreads / kWave;
-constexpr int kMaskWords = kDecodeMaxTokens / 32;
+constexpr int kMaskWords = kStreamMaxTokens / 32;
 
 // Byte offset of the first K-step fragment of row block b of expert e.
 template <bool GATEUP>
@@ -61,7 +61,7 @@ struct Grouping {
   int active[kExperts];
   int n_active;
   uint32_t mask[kExperts][kMaskWords];  // bit t: token t chose the expert
-  int list[kDecodeMaxTokens * kTopK];   // slots grouped by expert, token order
+  int list[kStreamMaxTokens * kTopK];   // slots grouped by expert, token order
 };
 
 // Workgroup state: the grouping and the wavefronts' partial tiles.
@@ -70,7 +70,7 @@ struct StreamShared {
   float red[kStreamWaves][16][kWave];  // value r of lane l of each wavefront
 };
 
-// Groups the slots t*4 + j of N <= kDecodeMaxTokens tokens by expert.
+// Groups the slots t*4 + j of N <= kStreamMaxTokens tokens by expert.
 __device__ void group_slots(const int32_t* __restrict__ idx, int N, Grouping& G) {
   const int tid = threadIdx.x;
   const int nthreads = blockDim.x;
@@ -111,10 +111,30 @@ __device__ void group_slots(const int32_t* __restrict__ idx, int N, Grouping& G)
   __syncthreads();
 }
 
-// Contiguous share [begin, end) of `units` work units for this workgroup.
-__device__ __forceinline__ void my_share(int units, int& begin, int& end) {
-  begin = static_cast<int>(static_cast<int64_t>(units) * blockIdx.x / gridDim.x);
-  end = static_cast<int>(static_cast<int64_t>(units) * (blockIdx.x + 1) / gridDim.x);
+// Contiguous share [begin, end) of the units of all active experts (in
+// active-expert order, kUnitsPerExpert per expert) for this workgroup.  A
+// unit is streamed once per pass of 32 tokens of its expert, so the shares
+// are cut at equal numbers of (unit, pass) sub-units; with one pass per
+// expert this is an equal split of the units.
+template <int kUnitsPerExpert>
+__device__ __forceinline__ void my_share(const Grouping& G, int& begin, int& end) {
+  const int n = uniform(G.n_active);
+  auto passes = [&](int i) { return (G.cnt[G.active[i]] + kPassRows - 1) / kPassRows; };
+  int64_t total = 0;
+  for (int i = 0; i < n; ++i) total += static_cast<int64_t>(kUnitsPerExpert) * passes(i);
+  // First unit whose first sub-unit is at or after sub-unit t.
+  auto unit_at = [&](int64_t t) {
+    int64_t P = 0;
+    for (int i = 0; i < n; ++i) {
+      const int w = passes(i);
+      const int64_t next = P + static_cast<int64_t>(kUnitsPerExpert) * w;
+      if (t < next) return i * kUnitsPerExpert + static_cast<int>((t - P + w - 1) / w);
+      P = next;
+    }
+    return n * kUnitsPerExpert;
+  };
+  begin = uniform(unit_at(total * blockIdx.x / gridDim.x));
+  end = uniform(unit_at(total * (blockIdx.x + 1) / gridDim.x));
 }
 
 // This lane's token of a pass: slot of row lane % 32 (rows past `rows`
@@ -153,7 +173,7 @@ __device__ __forceinline__ void stream_units(const uint16_t* __restrict__ B,
   constexpr int kF = kS / 2;
   constexpr int kUnitsPerExpert = GATEUP ? kGateupBlocks : kDownBlocks;
   int begin, end;
-  my_share(uniform(S.G.n_active) * kUnitsPerExpert, begin, end);
+  my_share<kUnitsPerExpert>(S.G, begin, end);
   if (begin >= end) return;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -164,15 +184,28 @@ __device__ __forceinline__ void stream_units(const uint16_t* __restrict__ B,
 
   auto expert_of = [&](int u) { return uniform(S.G.active[u / kUnitsPerExpert]); };
   auto count_of = [&](int e) { return uniform(S.G.off[e + 1] - S.G.off[e]); };
-  // Past the end of the share a cursor stays put (its loads are dummies),
-  // so no expert past the last active one is looked up.
+  // Next (unit, pass) after c: the next unit of the expert's run in the
+  // share, else the run's first unit for the next pass, else the next
+  // expert's first unit.
+  auto next_unit = [&](Cursor& c) {
+    const int run = c.u / kUnitsPerExpert;
+    if (++c.u < min(end, (run + 1) * kUnitsPerExpert)) return;
+    if (++c.pass * kPassRows < count_of(expert_of(c.u - 1))) {
+      c.u = max(begin, run * kUnitsPerExpert);
+      return;
+    }
+    c.pass = 0;
+  };
+  // Order of the sub-units: within the share's units of one expert, all
+  // units for one pass of 32 tokens, then all again for the next pass, so
+  // the token rows change once per pass (an expert's weights are streamed
+  // once per pass either way).  Past the end of the share a cursor stays
+  // put (its loads are dummies), so no expert past the last active one is
+  // looked up.
   auto advance = [&](Cursor& c) {
     if (c.u >= end) return;
     c.p ^= 1;
-    if (c.p == 0 && ++c.pass * kPassRows >= count_of(expert_of(c.u))) {
-      c.pass = 0;
-      ++c.u;
-    }
+    if (c.p == 0) next_unit(c);
   };
   // Issues the weight loads of sub-unit c.  Past the end of the share the
   // loads are still issued, with an offset outside the buffer (they return
@@ -339,7 +372,7 @@ __device__ __forceinline__ void stream_units_fp8(const uint16_t* __restrict__ B,
   constexpr int kFrags = 4;        // 128 K = 4 fragments of 32 K
   constexpr int kUnitsPerExpert = GATEUP ? kGateupBlocks : kDownBlocks;
   int begin, end;
-  my_share(uniform(S.G.n_active) * kUnitsPerExpert, begin, end);
+  my_share<kUnitsPerExpert>(S.G, begin, end);
   if (begin >= end) return;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -350,12 +383,23 @@ __device__ __forceinline__ void stream_units_fp8(const uint16_t* __restrict__ B,
 
   auto expert_of = [&](int u) { return uniform(S.G.active[u / kUnitsPerExpert]); };
   auto count_of = [&](int e) { return uniform(S.G.off[e + 1] - S.G.off[e]); };
+  // Next (unit, pass) after c: the next unit of the expert's run in the
+  // share, else the run's first unit for the next pass, else the next
+  // expert's first unit.
+  auto next_unit = [&](Cursor& c) {
+    const int run = c.u / kUnitsPerExpert;
+    if (++c.u < min(end, (run + 1) * kUnitsPerExpert)) return;
+    if (++c.pass * kPassRows < count_of(expert_of(c.u - 1))) {
+      c.u = max(begin, run * kUnitsPerExpert);
+      return;
+    }
+    c.pass = 0;
+  };
+  // Sub-unit order as in stream_units: pass-major within the share's units
+  // of one expert.
   auto advance = [&](Cursor& c) {
     if (c.u >= end) return;
-    if (++c.pass * kPassRows >= count_of(expert_of(c.u))) {
-      c.pass = 0;
-      ++c.u;
-    }
+    next_unit(c);
   };
   // Weight loads of unit c (past the end of the share: an offset outside the
   // buffer, which returns zeros, so every path keeps the same loads in flight).

@@ -52,8 +52,8 @@ extern "C" {
 #define LFM_MOE_FF 1536
 /* Largest N accepted: grouped rows (4N) and their element offsets stay in range. */
 #define LFM_MOE_MAX_TOKENS (1LL << 24)
-/* Largest N of lfm_moe_forward_fp8 (decode-shaped batches). */
-#define LFM_MOE_FP8_MAX_TOKENS 96
+/* Largest N of lfm_moe_forward_fp8 (decode and verification-shaped batches). */
+#define LFM_MOE_FP8_MAX_TOKENS 256
 
 typedef enum {
   LFM_MOE_OK = 0,
@@ -217,8 +217,9 @@ lfm_moe_status lfm_moe_block_forward_ws(float* x_inout, const uint16_t* W_r, con
  *   W_down_fp8 [64 * 2048 * 1536] bytes, scales_down [64][16][12] fp32
  *   (written); fragment (e * 64 + b) * 48 + kp holds rows 32 b .. 32 b + 31,
  *   columns 32 kp .. 32 kp + 31, in the same lane order.
- * lfm_moe_forward_fp8: the layer with these experts, for N <= 96 tokens
- *   (the weight-streaming decode regime; larger N returns
+ * lfm_moe_forward_fp8: the layer with these experts, for N <= 256 tokens
+ *   (LFM_MOE_FP8_MAX_TOKENS: decode and verification-shaped batches, where
+ *   the layer streams its weights; larger N returns
  *   LFM_MOE_ERR_INVALID_ARGUMENT).  Router and mixture weights as in
  *   lfm_moe_forward; each expert's input rows (X, then the bf16 hidden rows)
  *   are quantised per group of 128 features as above; the products of

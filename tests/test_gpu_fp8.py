@@ -5,7 +5,7 @@ Weights: the N = 64 decode workload's.  The packed codes and scales are
 compared bit-exactly with oracle.fp8's block quantisation of every expert
 (after undoing the documented fragment permutation); the layer output with
 the oracle's FP8 layer at N = 64 (the workload itself) and at ragged token
-counts up to the entry point's limit of 96.
+counts up to the entry point's limit of 256.
 """
 
 import numpy as np
@@ -175,7 +175,7 @@ def test_fp8_forward_parity_decode_n64(moe):
     _check_fp8_forward(moe, inp, dev, q, inp["X"].shape[0])
 
 
-@pytest.mark.parametrize("N", [1, 17, 33, 95, 96])
+@pytest.mark.parametrize("N", [1, 17, 33, 95, 96, 97, 160, 255, 256])
 def test_fp8_forward_ragged(moe, N):
     inp0, dev0, q = _decode_case(moe)
     X = oracle.block_input(synth.hidden_states(N, 500 + N).numpy())
@@ -189,7 +189,8 @@ def test_fp8_zero_tokens_and_limit(moe):
     X = dev["X"][:0]
     out = torch.empty(0, 2048, dtype=torch.float32, device="cuda")
     moe.forward_fp8(X, dev["W_r"], dev["bias"], dev["gateup_fp8"], dev["down_fp8"], out=out)
-    big = torch.zeros(97, 2048, dtype=torch.bfloat16, device="cuda")
+    from biased_sigmoid_top_amd import _lib
+    big = torch.zeros(_lib.FP8_MAX_TOKENS + 1, 2048, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(RuntimeError):
         moe.forward_fp8(big, dev["W_r"], dev["bias"], dev["gateup_fp8"], dev["down_fp8"])
 
