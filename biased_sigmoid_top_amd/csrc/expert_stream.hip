@@ -317,15 +317,19 @@ __device__ __forceinline__ void stream_units(const uint16_t* __restrict__ B,
 
 // FP8 experts (pack_fp8.hip): 1 KB fragments of 32 rows x 32 K, one
 // 16-byte load per lane holding its operands of two 16-wide K steps; a fp32
-// scale per 128 x 128 weight block.  Each wavefront covers one 128-wide K
-// group of a unit (gate/up: 16 wavefronts, down: 12), which is both a weight
-// block's columns and an activation group: the wavefront loads its slice of
-// the bf16 token rows, quantises it per token (largest magnitude of the
-// token's 128 values, codes E4M3(x * (448 / amax)), scale amax / 448 -- the
-// activation quantisation of the inferencekey.com page's FP8_BLOCK entry),
-// multiplies, and scales its partial tile once by weight scale x token scale
-// before the cross-wavefront sum.  One unit per step (4 fragments, 4 KB per
-// wavefront), three units in the register ring.
+// scale per 128 x 128 weight block.  Each wavefront covers GPW 128-wide K
+// groups of a unit (gate/up: 2 groups, 8 wavefronts; down: 1 group, 12
+// wavefronts).  A group is both a weight block's columns and an activation
+// group: the wavefront loads its slice of the bf16 token rows, quantises it
+// per token and group (largest magnitude of the token's 128 values, codes
+// E4M3(x * (448 / amax)), scale amax / 448 -- the activation quantisation
+// of the inferencekey.com page's FP8_BLOCK entry), multiplies each group
+// into its own accumulator, and adds the groups' products times weight scale
+// x token scale into its partial tile before the cross-wavefront sum.  Two
+// groups per wavefront halve the partial tiles a unit reduces through LDS
+// (measured gate/up: 62.1 -> 58.9 us at N = 64, 40 experts; no gain for
+// down).  One unit per step (4 GPW fragments per wavefront), three units in
+// the register ring.
 //
 // The products run on the bf16 MFMA: both operands' codes are widened to
 // bf16 in registers (E4M3 values are bf16 values, and their products are
@@ -361,15 +365,16 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
   return r;
 }
 
-template <bool GATEUP>
+template <bool GATEUP, int GPW>
 __device__ __forceinline__ void stream_units_fp8(const uint16_t* __restrict__ B,
                                                  const uint8_t* __restrict__ Wq,
                                                  const float* __restrict__ Ws,
                                                  uint16_t* __restrict__ H, float* __restrict__ Y,
                                                  int N, StreamShared& S) {
   constexpr int K = GATEUP ? kHidden : kFF;
-  constexpr int kWaves = K / 128;  // one 128-wide group per wavefront
-  constexpr int kFrags = 4;        // 128 K = 4 fragments of 32 K
+  constexpr int kWaves = K / (128 * GPW);  // GPW 128-wide groups per wavefront
+  constexpr int kFrags = 4 * GPW;          // 128 K = 4 fragments of 32 K
+  constexpr int kSteps = 8 * GPW;          // 16-wide K steps per wavefront
   constexpr int kUnitsPerExpert = GATEUP ? kGateupBlocks : kDownBlocks;
   int begin, end;
   my_share<kUnitsPerExpert>(S.G, begin, end);
@@ -377,7 +382,7 @@ __device__ __forceinline__ void stream_units_fp8(const uint16_t* __restrict__ B,
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const uint32_t lane_bytes = lane * 16;
-  const uint32_t kcol_bytes = (wave * 128 + (lane / 32) * 8) * 2;  // this lane's first bf16 K column
+  const uint32_t kcol_bytes = (wave * 128 * GPW + (lane / 32) * 8) * 2;  // this lane's first bf16 K column
   const Rsrc wr = make_rsrc(Wq, static_cast<uint32_t>(kExperts) * kHidden * kFF * (GATEUP ? 2 : 1));
   const Rsrc br = make_rsrc(B, static_cast<uint32_t>(N) * (GATEUP ? 1 : kTopK) * K * 2);
 
@@ -413,10 +418,10 @@ __device__ __forceinline__ void stream_units_fp8(const uint16_t* __restrict__ B,
     for (int f = 0; f < kFrags; ++f) w[f] = buf_ld<true>(wr, voff, base + f * kFp8FragBytes);
   };
 
-  // Token rows: 8 bf16 K steps per lane as loaded; quantised in place to
-  // the bf16 values of their E4M3 codes (K step k stays in xb[k]).
-  uint4 w0[kFrags], w1[kFrags], w2[kFrags], xb[8];
-  float xscale = 0.f;
+  // Token rows: 8 bf16 K steps per group and lane as loaded; quantised in
+  // place to the bf16 values of their E4M3 codes (K step k stays in xb[k]).
+  uint4 w0[kFrags], w1[kFrags], w2[kFrags], xb[kSteps];
+  float xscale[GPW] = {};
   bool fresh = false;
   int xe = -1, xpass = -1;
   auto load_rows = [&](const Cursor& c) {
@@ -428,32 +433,36 @@ __device__ __forceinline__ void stream_units_fp8(const uint16_t* __restrict__ B,
     const int slot = pass_slot(S.G.list + S.G.off[e] + r0, rows, lane);
     const uint32_t bo = (GATEUP ? slot / kTopK : slot) * (K * 2) + kcol_bytes;
 #pragma unroll
-    for (int f = 0; f < 8; ++f) xb[f] = buf_ld<false>(br, bo, f * 32);
+    for (int f = 0; f < kSteps; ++f) xb[f] = buf_ld<false>(br, bo, f * 32);
     xe = e;
     xpass = c.pass;
     fresh = true;
   };
   auto quantize_rows = [&] {
-    // Largest magnitude: on the bf16 bit patterns (the order of finite
-    // non-negative floats is that of their bits).
-    uint32_t m = 0;
 #pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      const uint32_t w4[4] = {xb[f].x, xb[f].y, xb[f].z, xb[f].w};
+    for (int g = 0; g < GPW; ++g) {
+      // Largest magnitude of the group: on the bf16 bit patterns (the order
+      // of finite non-negative floats is that of their bits).
+      uint32_t m = 0;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) m = max(m, max(w4[k] & 0x7fffu, (w4[k] >> 16) & 0x7fffu));
+      for (int f = 8 * g; f < 8 * g + 8; ++f) {
+        const uint32_t w4[4] = {xb[f].x, xb[f].y, xb[f].z, xb[f].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) m = max(m, max(w4[k] & 0x7fffu, (w4[k] >> 16) & 0x7fffu));
+      }
+      float amax = __uint_as_float(m << 16);
+      // Lanes l and l ^ 32 hold the two halves of the same token's group.
+      amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+      const float inv = amax > 0.f ? 448.f / amax : 0.f;
+      xscale[g] = amax / 448.f;
+      auto q4 = [&](uint32_t lo, uint32_t hi) {
+        return e4m3x4(__uint_as_float(lo << 16) * inv, __uint_as_float(lo & 0xffff0000u) * inv,
+                      __uint_as_float(hi << 16) * inv, __uint_as_float(hi & 0xffff0000u) * inv);
+      };
+#pragma unroll
+      for (int k = 8 * g; k < 8 * g + 8; ++k)
+        xb[k] = e4m3x8_to_bf16(q4(xb[k].x, xb[k].y), q4(xb[k].z, xb[k].w));
     }
-    float amax = __uint_as_float(m << 16);
-    // Lanes l and l ^ 32 hold the two halves of the same token's group.
-    amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
-    const float inv = amax > 0.f ? 448.f / amax : 0.f;
-    xscale = amax / 448.f;
-    auto q4 = [&](uint32_t lo, uint32_t hi) {
-      return e4m3x4(__uint_as_float(lo << 16) * inv, __uint_as_float(lo & 0xffff0000u) * inv,
-                    __uint_as_float(hi << 16) * inv, __uint_as_float(hi & 0xffff0000u) * inv);
-    };
-#pragma unroll
-    for (int k = 0; k < 8; ++k) xb[k] = e4m3x8_to_bf16(q4(xb[k].x, xb[k].y), q4(xb[k].z, xb[k].w));
   };
 
   Cursor cp{begin, 0, 0}, ld{begin, 0, 0};
@@ -469,27 +478,50 @@ __device__ __forceinline__ void stream_units_fp8(const uint16_t* __restrict__ B,
       quantize_rows();
       fresh = false;
     }
-    f32x16 acc;
+    // One accumulator per K group: the groups have their own scales.
+    f32x16 acc[GPW];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    for (int g = 0; g < GPW; ++g) {
 #pragma unroll
-    for (int f = 0; f < kFrags; ++f) {
-      acc = mfma32(e4m3x8_to_bf16(wc[f].x, wc[f].y), xb[2 * f], acc);
-      acc = mfma32(e4m3x8_to_bf16(wc[f].z, wc[f].w), xb[2 * f + 1], acc);
+      for (int r = 0; r < 16; ++r) acc[g][r] = 0.f;
+#pragma unroll
+      for (int f = 4 * g; f < 4 * g + 4; ++f) {
+        acc[g] = mfma32(e4m3x8_to_bf16(wc[f].x, wc[f].y), xb[2 * f], acc[g]);
+        acc[g] = mfma32(e4m3x8_to_bf16(wc[f].z, wc[f].w), xb[2 * f + 1], acc[g]);
+      }
     }
     const Cursor cur = cp;
     const int e = expert_of(cur.u);
     const int b = cur.u % kUnitsPerExpert;
-    // Weight scales of this unit's rows and this wavefront's K group.
+    // Each group's products times weight scale x token scale, the groups
+    // added in order: this wavefront's partial tile.
     if (GATEUP) {
-      const float sg = Ws[((e * 2 + 0) * (kFF / 128) + b / 8) * (kHidden / 128) + wave] * xscale;
-      const float su = Ws[((e * 2 + 1) * (kFF / 128) + b / 8) * (kHidden / 128) + wave] * xscale;
+      float sg[GPW], su[GPW];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) S.red[wave][r][lane] = acc[r] * (r < 8 ? sg : su);
+      for (int g = 0; g < GPW; ++g) {
+        const int kg = wave * GPW + g;
+        sg[g] = Ws[((e * 2 + 0) * (kFF / 128) + b / 8) * (kHidden / 128) + kg] * xscale[g];
+        su[g] = Ws[((e * 2 + 1) * (kFF / 128) + b / 8) * (kHidden / 128) + kg] * xscale[g];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = acc[0][r] * (r < 8 ? sg[0] : su[0]);
+#pragma unroll
+        for (int g = 1; g < GPW; ++g) v += acc[g][r] * (r < 8 ? sg[g] : su[g]);
+        S.red[wave][r][lane] = v;
+      }
     } else {
-      const float sd = Ws[(e * (kHidden / 128) + b / 4) * (kFF / 128) + wave] * xscale;
+      float sd[GPW];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) S.red[wave][r][lane] = acc[r] * sd;
+      for (int g = 0; g < GPW; ++g)
+        sd[g] = Ws[(e * (kHidden / 128) + b / 4) * (kFF / 128) + wave * GPW + g] * xscale[g];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = acc[0][r] * sd[0];
+#pragma unroll
+        for (int g = 1; g < GPW; ++g) v += acc[g][r] * sd[g];
+        S.red[wave][r][lane] = v;
+      }
     }
     advance(cp);
     load_rows(cp);
@@ -534,15 +566,18 @@ __device__ __forceinline__ void stream_units_fp8(const uint16_t* __restrict__ B,
   }
 }
 
-constexpr int kFp8GateupThreads = kHidden / 128 * kWave;  // 16 wavefronts
-constexpr int kFp8DownThreads = kFF / 128 * kWave;        // 12 wavefronts
+// K groups of 128 per wavefront: gate/up 2 (8 wavefronts), down 1 (12).
+constexpr int kFp8GateupGroups = 2;
+constexpr int kFp8DownGroups = 1;
+constexpr int kFp8GateupThreads = kHidden / (128 * kFp8GateupGroups) * kWave;
+constexpr int kFp8DownThreads = kFF / (128 * kFp8DownGroups) * kWave;
 
 __global__ __launch_bounds__(kFp8GateupThreads) void gateup_decode_fp8_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ Wq, const float* __restrict__ Ws,
     const int32_t* __restrict__ idx, uint16_t* __restrict__ H, int N) {
   __shared__ StreamShared S;
   group_slots(idx, N, S.G);
-  stream_units_fp8<true>(X, Wq, Ws, H, nullptr, N, S);
+  stream_units_fp8<true, kFp8GateupGroups>(X, Wq, Ws, H, nullptr, N, S);
 }
 
 __global__ __launch_bounds__(kFp8DownThreads) void down_decode_fp8_kernel(
@@ -550,7 +585,7 @@ __global__ __launch_bounds__(kFp8DownThreads) void down_decode_fp8_kernel(
     const int32_t* __restrict__ idx, float* __restrict__ Y, int N) {
   __shared__ StreamShared S;
   group_slots(idx, N, S.G);
-  stream_units_fp8<false>(H, Wq, Ws, nullptr, Y, N, S);
+  stream_units_fp8<false, kFp8DownGroups>(H, Wq, Ws, nullptr, Y, N, S);
 }
 
 __global__ __launch_bounds__(kStreamThreads) void gateup_decode_kernel(
