@@ -163,13 +163,13 @@ struct Cursor {
 // a ring of three register buffers, so two halves are in flight while one
 // is multiplied.  The 16 partial 32x32 tiles of a unit are added in LDS in
 // wavefront order.
-template <bool GATEUP>
+template <bool GATEUP, int WAVES>
 __device__ __forceinline__ void stream_units(const uint16_t* __restrict__ B,
                                              const uint16_t* __restrict__ Wp,
                                              uint16_t* __restrict__ H, float* __restrict__ Y,
                                              int N, StreamShared& S) {
   constexpr int K = GATEUP ? kHidden : kFF;
-  constexpr int kS = (GATEUP ? kGateupSteps : kDownSteps) / kStreamWaves;  // 8 or 6
+  constexpr int kS = (GATEUP ? kGateupSteps : kDownSteps) / WAVES;  // K steps per wavefront
   constexpr int kF = kS / 2;
   constexpr int kUnitsPerExpert = GATEUP ? kGateupBlocks : kDownBlocks;
   int begin, end;
@@ -275,27 +275,30 @@ __device__ __forceinline__ void stream_units(const uint16_t* __restrict__ B,
       const int rows = min(kPassRows, count_of(e) - r0);
       const int* slots = S.G.list + S.G.off[e] + r0;
       const int b = cur.u % kUnitsPerExpert;
-      // Thread (r, ln) adds value r of lane ln over the wavefronts: token
-      // ln % 32, row mfma32_row(r, ln) of the unit's 32-row tile.
+      // Thread (r, ln) adds value r of lane ln over the wavefronts (token
+      // ln % 32, row mfma32_row(r, ln) of the unit's 32-row tile), for r =
+      // its wavefront index and, with fewer than 16 wavefronts, r + WAVES.
       const int ln = threadIdx.x % kWave;
-      const int r = threadIdx.x / kWave;
       if (ln % 32 < rows) {
         const int slot = slots[ln % 32];
-        if (GATEUP) {
-          if (r < 8) {  // rows r (gate) and r + 8 (up) hold H column mfma32_row(r, ln)
-            float gs = 0.f, us = 0.f;
+        for (int r = threadIdx.x / kWave; r < 16; r += WAVES) {
+          if (GATEUP) {
+            if (r < 8) {  // rows r (gate) and r + 8 (up) hold H column mfma32_row(r, ln)
+              float gs = 0.f, us = 0.f;
 #pragma unroll
-            for (int w = 0; w < kStreamWaves; ++w) {
-              gs += S.red[w][r][ln];
-              us += S.red[w][r + 8][ln];
+              for (int w = 0; w < WAVES; ++w) {
+                gs += S.red[w][r][ln];
+                us += S.red[w][r + 8][ln];
+              }
+              H[static_cast<size_t>(slot) * kFF + b * 16 + mfma32_row(r, ln)] =
+                  f32_to_bf16(silu(gs) * us);
             }
-            H[static_cast<size_t>(slot) * kFF + b * 16 + mfma32_row(r, ln)] = f32_to_bf16(silu(gs) * us);
-          }
-        } else {
-          float ys = 0.f;
+          } else {
+            float ys = 0.f;
 #pragma unroll
-          for (int w = 0; w < kStreamWaves; ++w) ys += S.red[w][r][ln];
-          Y[static_cast<size_t>(slot) * kHidden + b * 32 + mfma32_row(r, ln)] = ys;
+            for (int w = 0; w < WAVES; ++w) ys += S.red[w][r][ln];
+            Y[static_cast<size_t>(slot) * kHidden + b * 32 + mfma32_row(r, ln)] = ys;
+          }
         }
       }
       __syncthreads();
@@ -588,20 +591,28 @@ __global__ __launch_bounds__(kFp8DownThreads) void down_decode_fp8_kernel(
   stream_units_fp8<false, kFp8DownGroups>(H, Wq, Ws, nullptr, Y, N, S);
 }
 
-__global__ __launch_bounds__(kStreamThreads) void gateup_decode_kernel(
+// Wavefronts splitting K: gate/up 16 (8 K steps each), down 16 (6 each).
+// Eight wavefronts with twice the K each (half the partial tiles per unit)
+// measured the same at N = 64 (gate/up 89.5-91.7 us, down 53.2-53.7 us
+// either way, one box): unlike the FP8 kernels, a bf16 unit carries enough
+// bytes for its reduction to stay a small share of its time.
+constexpr int kGateupWaves = 16;
+constexpr int kDownWaves = 16;
+
+__global__ __launch_bounds__(kGateupWaves * kWave) void gateup_decode_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wgu,
     const int32_t* __restrict__ idx, uint16_t* __restrict__ H, int N) {
   __shared__ StreamShared S;
   group_slots(idx, N, S.G);
-  stream_units<true>(X, Wgu, H, nullptr, N, S);
+  stream_units<true, kGateupWaves>(X, Wgu, H, nullptr, N, S);
 }
 
-__global__ __launch_bounds__(kStreamThreads) void down_decode_kernel(
+__global__ __launch_bounds__(kDownWaves * kWave) void down_decode_kernel(
     const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wd,
     const int32_t* __restrict__ idx, float* __restrict__ Y, int N) {
   __shared__ StreamShared S;
   group_slots(idx, N, S.G);
-  stream_units<false>(H, Wd, nullptr, Y, N, S);
+  stream_units<false, kDownWaves>(H, Wd, nullptr, Y, N, S);
 }
 
 int cu_count() {
@@ -628,14 +639,14 @@ int64_t max_mtiles(int64_t N, int tile_rows) {
 
 hipError_t launch_gateup_decode(const uint16_t* X, const uint16_t* Wgu, const int32_t* idx,
                                 uint16_t* H, int N, hipStream_t stream) {
-  hipLaunchKernelGGL(gateup_decode_kernel, dim3(cu_count()), dim3(kStreamThreads), 0, stream, X,
+  hipLaunchKernelGGL(gateup_decode_kernel, dim3(cu_count()), dim3(kGateupWaves * kWave), 0, stream, X,
                      Wgu, idx, H, N);
   return hipGetLastError();
 }
 
 hipError_t launch_down_decode(const uint16_t* H, const uint16_t* Wd, const int32_t* idx,
                               float* Y, int N, hipStream_t stream) {
-  hipLaunchKernelGGL(down_decode_kernel, dim3(cu_count()), dim3(kStreamThreads), 0, stream, H, Wd,
+  hipLaunchKernelGGL(down_decode_kernel, dim3(cu_count()), dim3(kDownWaves * kWave), 0, stream, H, Wd,
                      idx, Y, N);
   return hipGetLastError();
 }
