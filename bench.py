@@ -108,6 +108,18 @@ def expert_counts(p, N):
     return torch.bincount(sel.reshape(-1), minlength=E).tolist()
 
 
+def inputs_sha256(layer):
+    """SHA-256 over the generated tensors of a workload (z, W_r, bias, W_gate,
+    W_up, W_down, in that order): the same digest on two machines means the
+    same inputs."""
+    import hashlib
+    import torch
+    h = hashlib.sha256()
+    for k in ("z", "W_r", "bias", "W_gate", "W_up", "W_down"):
+        h.update(layer[k].contiguous().view(-1).view(torch.uint8).numpy().tobytes())
+    return h.hexdigest()
+
+
 def prepare_layer(name, N, seed, layer, copies):
     import torch
     import biased_sigmoid_top_amd as moe
@@ -366,6 +378,7 @@ def main():
     log(f"timing {args.workload}: {args.steps} steps after {args.warmup} warm-up")
     wall_ms, per_kernel = time_steps(head, args.steps, args.warmup)
     h = summarize(head, wall_ms, per_kernel)
+    h["inputs_sha256"] = inputs_sha256(head["layer"])
     log(json.dumps(h))
 
     from biased_sigmoid_top_amd._lib import FP8_MAX_TOKENS
@@ -406,6 +419,7 @@ def build_line(args, h, seed, second=None, cpu=None):
         warmup=args.warmup, ms_per_step=h["ms_per_step"], higher_is_better=True, scaling="weak",
         vs_baseline=None, dtype="bf16", data="synthetic",
         config=dict(workload=args.workload, N=h["N"], d=D, experts=E, top_k=K, ff=FF, seed=seed,
+                    inputs_sha256=h.get("inputs_sha256"),
                     active_experts=h["active_experts"],
                     max_tokens_per_expert=h["max_tokens_per_expert"], weight_copies=args.copies),
         layer=dict(gbs=h["layer_gbs"], hbm_frac=h["layer_hbm_frac"], tflops=h["layer_tflops"],

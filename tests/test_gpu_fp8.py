@@ -206,3 +206,18 @@ def test_fp8_graph_capture_replays_match_eager(moe):
     _step(f"graph capture forward_fp8 N={N}")
     eager = moe.forward_fp8(*args, workspace=ws).clone()
     _graph_replays_match(moe, lambda out: moe.forward_fp8(*args, out=out, workspace=ws), eager)
+
+
+def test_fp8_writes_stay_in_bounds(moe):
+    inp0, dev0, q = _decode_case(moe)
+    N = 100
+    X = torch.from_numpy(oracle.block_input(synth.hidden_states(N, 777).numpy())).to(torch.bfloat16).cuda()
+    out_all = torch.full((N + 8, 2048), 12345.0, dtype=torch.float32, device="cuda")
+    nbytes = moe.workspace_bytes(N)
+    ws_all = torch.full((nbytes + 4096,), 0xAB, dtype=torch.uint8, device="cuda")
+    _step(f"FP8 canaries N={N}")
+    moe.forward_fp8(X, dev0["W_r"], dev0["bias"], dev0["gateup_fp8"], dev0["down_fp8"],
+                    out=out_all[:N], workspace=ws_all[:nbytes])
+    torch.cuda.synchronize()
+    assert torch.all(out_all[N:] == 12345.0).item(), "rows past N written"
+    assert torch.all(ws_all[nbytes:] == 0xAB).item(), "bytes past the workspace written"

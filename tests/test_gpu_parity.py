@@ -300,6 +300,43 @@ def test_verification_batches(moe, c):
     check_out(_np(out), expected_outputs(inp, r, np.arange(N), alt))
 
 
+@pytest.mark.parametrize("N", [17, 300, 4096])
+def test_writes_stay_in_bounds(moe, N):
+    """Canaries after the output rows and after the workspace's documented
+    size are left untouched (decode path, narrow and wide grouped tiles)."""
+    inp, dev = _layer_case(N, 700 + N)
+    _step(f"canaries N={N}")
+    out_all = torch.full((N + 8, 2048), 12345.0, dtype=torch.float32, device="cuda")
+    nbytes = moe.workspace_bytes(N)
+    ws_all = torch.full((nbytes + 4096,), 0xAB, dtype=torch.uint8, device="cuda")
+    moe.forward(dev["X"], dev["W_r"], dev["bias"], dev["W_gateup"], dev["W_down"],
+                out=out_all[:N], workspace=ws_all[:nbytes])
+    torch.cuda.synchronize()
+    assert torch.all(out_all[N:] == 12345.0).item(), "rows past N written"
+    assert torch.all(ws_all[nbytes:] == 0xAB).item(), "bytes past the workspace written"
+    assert torch.isfinite(out_all[:N]).all().item()
+
+
+def test_out_of_memory_is_reported(moe):
+    """A layer call whose workspace cannot be allocated returns
+    LFM_MOE_ERR_OUT_OF_MEMORY with a message, before any launch (the tensor
+    pointers are never dereferenced), and the next call grows the workspace
+    again."""
+    from biased_sigmoid_top_amd import _lib
+    lib = _lib.load()
+    N = (1 << 24)                      # LFM_MOE_MAX_TOKENS: ~0.8 TB of workspace
+    assert moe.workspace_bytes(N) > 400 * (1 << 30)
+    fake = [0x7F00_0000_0000 + i * (1 << 36) for i in range(6)]
+    _step("out-of-memory path")
+    st = lib.lfm_moe_forward(*fake[:5], fake[5], N, None)
+    assert st == _lib.ERR_OUT_OF_MEMORY, st
+    assert b"hipMalloc" in lib.lfm_moe_last_error()
+    inp, dev = _layer_case(16, 900)
+    out = moe.forward(dev["X"], dev["W_r"], dev["bias"], dev["W_gateup"], dev["W_down"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item()
+
+
 def test_zero_tokens_is_a_no_op(moe):
     inp, dev = _layer_case(1, 7)
     X0 = dev["X"][:0]
