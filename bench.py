@@ -324,6 +324,25 @@ def cpu_baseline(p, budget_s):
                        f"({p['N']} tokens each, float64 NumPy), {el:.1f} s")
 
 
+def device_info():
+    """The device as torch reports it, plus (best effort) the clocks and
+    power that rocm-smi reports right after the timed work: boxes of the
+    same model measured up to ~20% apart, and this records what differed."""
+    import subprocess
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    info = dict(name=p.name, arch=getattr(p, "gcnArchName", None), cus=p.multi_processor_count,
+                memory_gib=round(p.total_memory / 2**30, 1), smi=None)
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showtemp", "--json"],
+                           capture_output=True, text=True, timeout=20)
+        if r.returncode == 0:
+            info["smi"] = json.loads(r.stdout)
+    except (OSError, subprocess.SubprocessError, ValueError):
+        pass
+    return info
+
+
 def copy_probe():
     """A plain 1 GiB device copy, for calibrating HBM byte counters."""
     import torch
@@ -378,6 +397,7 @@ def main():
     log(f"timing {args.workload}: {args.steps} steps after {args.warmup} warm-up")
     wall_ms, per_kernel = time_steps(head, args.steps, args.warmup)
     h = summarize(head, wall_ms, per_kernel)
+    dev_info = device_info()
     h["inputs_sha256"] = inputs_sha256(head["layer"])
     log(json.dumps(h))
 
@@ -405,6 +425,7 @@ def main():
 
     line = build_line(args, h, head["seed"], second, cpu)
     line["fp8_decode"] = fp8
+    line["device"] = dev_info
     if args.configs:
         del head
         torch.cuda.empty_cache()
