@@ -18,16 +18,16 @@
 //
 // Work split: the work is cut into units -- one expert's 16 H columns (128
 // KB of gate/up weights) or 32 output features (96 KB of down weights) --
-// and the grid is one 16-wavefront workgroup per CU, each taking an equal
-// contiguous range of units (measured: handing units out from a device
-// counter is slower, because same-address atomics serialise).  The 16
-// wavefronts of a workgroup stream a unit together, each over one
-// sixteenth of K, and add their partial tiles in LDS in wavefront order
-// (so the result does not depend on the grid).  While a unit is computed
-// the next unit's weights are already in flight.  A wavefront keeps its
-// slice of the token rows (the B operand) in registers across the units of
-// one expert, and loads them ahead of the weight prefetch when the expert
-// changes.  Every workgroup first groups the batch's slots by expert in
+// and the grid is one workgroup per CU, each taking a contiguous range of
+// units cut at equal numbers of (unit, 32-token pass) sub-units (measured:
+// handing units out from a device counter is slower, because same-address
+// atomics serialise).  The wavefronts of a workgroup stream a unit
+// together, each over its slice of K, and add their partial tiles in LDS in
+// wavefront order (so the result does not depend on the grid).  While a
+// unit is computed the next units' weights are already in flight.  A
+// wavefront keeps its slice of the token rows (the B operand) in registers
+// across the units of one expert and pass, and loads them ahead of the
+// weight prefetch when they change.  Every workgroup first groups the batch's slots by expert in
 // LDS (a stable counting sort with per-expert token bitmasks); no dispatch
 // step and no host readback are needed.
 //
@@ -43,8 +43,7 @@ namespace lfm {
 namespace {
 
 constexpr int kPassRows = 32;                      // tokens per pass (one 32x32 MFMA tile)
-constexpr int kStreamThreads = 1024;               // 16 wavefronts: one workgroup per CU
-constexpr int kStreamWaves = kStreamThreads / kWave;
+constexpr int kStreamWaves = 16;                   // most wavefronts of a streaming workgroup
 constexpr int kMaskWords = kStreamMaxTokens / 32;
 
 // Byte offset of the first K-step fragment of row block b of expert e.

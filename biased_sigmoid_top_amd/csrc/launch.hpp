@@ -33,8 +33,9 @@ hipError_t launch_route(const uint16_t* X, const uint16_t* Wr, const float* bias
 hipError_t launch_dispatch(const int32_t* idx, const int32_t* blockcounts, int32_t* offsets,
                            int32_t* row2slot, int N, hipStream_t stream);
 
-// Decode path: persistent kernels (one workgroup per CU) that group their
-// own tokens (N <= kDecodeMaxTokens).
+// Weight-streaming path: persistent kernels (one workgroup per CU) that
+// group their own tokens (bf16 experts: N <= kDecodeMaxTokens; FP8 experts:
+// N <= kStreamMaxTokens).
 hipError_t launch_gateup_decode(const uint16_t* X, const uint16_t* Wgu, const int32_t* idx,
                                 uint16_t* H, int N, hipStream_t stream);
 hipError_t launch_down_decode(const uint16_t* H, const uint16_t* Wd, const int32_t* idx,

@@ -221,3 +221,30 @@ def test_fp8_writes_stay_in_bounds(moe):
     torch.cuda.synchronize()
     assert torch.all(out_all[N:] == 12345.0).item(), "rows past N written"
     assert torch.all(ws_all[nbytes:] == 0xAB).item(), "bytes past the workspace written"
+
+
+@pytest.mark.parametrize("N", [5, 96, 256])
+def test_fp8_every_token_on_the_same_four_experts(moe, N):
+    """Degenerate routing: a large bias puts every token on experts 60..63,
+    so each has N rows (up to eight 32-token passes) and 60 experts are
+    empty."""
+    inp0, dev0, q = _decode_case(moe)
+    bias = torch.zeros(64)
+    bias[60:] = 10.0
+    X = oracle.block_input(synth.hidden_states(N, 1300 + N).numpy())
+    inp = dict(inp0, X=X, bias=bias.numpy().astype(np.float64))
+    dev = dict(dev0, X=torch.from_numpy(X).to(torch.bfloat16).cuda(), bias=bias.cuda())
+    r = oracle.route(inp["X"], inp["W_r"], inp["bias"])
+    assert np.all(np.sort(r.idx, 1) == [60, 61, 62, 63])
+    _check_fp8_forward(moe, inp, dev, q, N)
+
+
+def test_fp8_bitwise_determinism(moe):
+    inp0, dev0, q = _decode_case(moe)
+    N = 160
+    X = torch.from_numpy(oracle.block_input(synth.hidden_states(N, 1500).numpy())).to(torch.bfloat16).cuda()
+    args = (X, dev0["W_r"], dev0["bias"], dev0["gateup_fp8"], dev0["down_fp8"])
+    _step("FP8 determinism N=160")
+    a = moe.forward_fp8(*args)
+    b = moe.forward_fp8(*args)
+    assert torch.equal(a, b)
