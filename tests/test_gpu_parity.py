@@ -337,6 +337,34 @@ def test_out_of_memory_is_reported(moe):
     assert torch.isfinite(out).all().item()
 
 
+def test_concurrent_streams_with_distinct_workspaces(moe):
+    """Calls on two streams with their own workspaces, issued back to back
+    so that they can overlap, give the results of the same calls made one
+    at a time (decode-shaped and grouped batches)."""
+    cases = [_layer_case(64, 1100), _layer_case(700, 1101)]
+    alone = []
+    for inp, dev in cases:
+        N = inp["X"].shape[0]
+        alone.append(moe.forward(dev["X"], dev["W_r"], dev["bias"], dev["W_gateup"], dev["W_down"],
+                                 workspace=moe.alloc_workspace(N)).clone())
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    _step("two streams, distinct workspaces")
+    for rep in range(3):
+        outs.clear()
+        for (inp, dev), st in zip(cases, streams):
+            N = inp["X"].shape[0]
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                ws = moe.alloc_workspace(N)
+                outs.append(moe.forward(dev["X"], dev["W_r"], dev["bias"], dev["W_gateup"], dev["W_down"],
+                                        workspace=ws, stream=st))
+        torch.cuda.synchronize()
+        for a, b in zip(outs, alone):
+            assert torch.equal(a, b), f"repetition {rep}"
+
+
 def test_zero_tokens_is_a_no_op(moe):
     inp, dev = _layer_case(1, 7)
     X0 = dev["X"][:0]
