@@ -42,7 +42,6 @@ namespace lfm {
 
 namespace {
 
-constexpr int kBM = 128;                  // grouped rows per tile
 constexpr int kKS = 2;                    // 16-wide K steps per stage
 constexpr int kBK = 16 * kKS;             // K per stage
 constexpr int kWSlots = 4;                // weight register ring: three stages ahead
@@ -60,12 +59,16 @@ __device__ __forceinline__ int swz(int c) { return c + 8 * (c & 1); }
 // 4 wavefronts (128 x 256), two per CU -- its 8 column tiles then deal
 // evenly over the CUs where 4 wide ones would leave a half-empty last round
 // (N = 4096: down 159 us against 164; gate/up 256 against 267 with 4).
-template <bool GATEUP, int FB_, int WAVES_ = (GATEUP ? 8 : 4)>
+template <bool GATEUP, int FB_, int WAVES_ = (GATEUP ? 8 : 4), int TB_ = 4>
 struct TileShape {
   static constexpr int FB = FB_;  // packed 32-row blocks per wavefront
+  static constexpr int kTB = TB_;  // 32-row token blocks per tile
+  static constexpr int kBM = 32 * kTB;  // grouped rows per tile
   static constexpr int kWaves = WAVES_;
   static constexpr int kThreads = kWaves * kWave;
-  static constexpr int kPerCu = kWaves == 8 ? 1 : 2;  // workgroups per CU the register budget is set for
+  // Workgroups per CU the register budget is set for: one for 8 wavefronts
+  // or for 256-token tiles (whose accumulators take a whole register file).
+  static constexpr int kPerCu = (kWaves == 8 || kTB == 8) ? 1 : 2;
   static constexpr int kChunks = kBM * (kPairBytes / 16) / kThreads;  // 16-byte token pieces per thread per pair
   static constexpr int kRowStep = kThreads / 8;  // tile rows one pass of the workgroup loads
   static constexpr int K = GATEUP ? kHidden : kFF;
@@ -81,18 +84,19 @@ struct TileShape {
   static_assert(kGroup * kColTiles % kXcds == 0, "a launch group deals evenly over the XCDs");
 };
 
-template <bool GATEUP, int FB_, int WAVES_>
-__global__ __launch_bounds__((TileShape<GATEUP, FB_, WAVES_>::kThreads),
-                             (TileShape<GATEUP, FB_, WAVES_>::kPerCu))
+template <bool GATEUP, int FB_, int WAVES_, int TB_>
+__global__ __launch_bounds__((TileShape<GATEUP, FB_, WAVES_, TB_>::kThreads),
+                             (TileShape<GATEUP, FB_, WAVES_, TB_>::kPerCu))
 void expert_tiled_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Wp,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ row2slot,
     uint16_t* __restrict__ H, float* __restrict__ Y) {
-  using T = TileShape<GATEUP, FB_, WAVES_>;
+  using T = TileShape<GATEUP, FB_, WAVES_, TB_>;
   constexpr int FB = T::FB;
+  constexpr int TB = T::kTB;
   static_assert(T::kStages % kWSlots == 0, "the stage loop is unrolled by the ring size");
   // Token fragments: 2 pair buffers x (2 stages x 4 token blocks x kKS steps).
-  __shared__ uint4 tok[2][2 * 4 * kKS * kWave];
+  __shared__ uint4 tok[2][2 * TB * kKS * kWave];
 
   // Launch groups of kGroup m-tiles x kColTiles column tiles; workgroup ids
   // are dealt to the XCDs round-robin, so id w of a group runs on XCD w % 8.
@@ -106,7 +110,7 @@ void expert_tiled_kernel(
   const int nb = t / T::kGroup;
   const int mt = blockIdx.x / (T::kGroup * T::kColTiles) * T::kGroup + t % T::kGroup;
   MTile tile;
-  if (!map_mtile(offsets, mt, kBM, tile)) return;
+  if (!map_mtile(offsets, mt, T::kBM, tile)) return;
   const int live_rows = uniform(tile.rows);
 
   const int tid = threadIdx.x;
@@ -125,7 +129,7 @@ void expert_tiled_kernel(
     const int slot = row2slot[tile.row_begin + (r < tile.rows ? r : 0)];
     arow[i] = A + static_cast<size_t>(GATEUP ? slot / kTopK : slot) * T::K + c * 8;
   }
-  const int st_pos = ((c / 4) * 4 * kKS + (c / 2) % 2) * kWave + (c % 2) * 32 + ((r0 % 32) ^ swz(c)) +
+  const int st_pos = ((c / 4) * TB * kKS + (c / 2) % 2) * kWave + (c % 2) * 32 + ((r0 % 32) ^ swz(c)) +
                      (r0 / 32) * kKS * kWave;
   static_assert(T::kRowStep % 32 == 0, "a thread's pieces share their row within a token block");
   // MFMA operand position of this lane for stage sp of a pair, K step j.
@@ -134,7 +138,7 @@ void expert_tiled_kernel(
   for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
     for (int j = 0; j < kKS; ++j)
-      rd_pos[sp][j] = (sp * 4 * kKS + j) * kWave + (lane & 32) + ((lane & 31) ^ swz(sp * 4 + j * 2 + lane / 32));
+      rd_pos[sp][j] = (sp * TB * kKS + j) * kWave + (lane & 32) + ((lane & 31) ^ swz(sp * 4 + j * 2 + lane / 32));
 
   // This wavefront's FB packed row blocks, K steps of a block contiguous,
   // read as buffer loads: the expert's packed matrix (12 MB at most) is the
@@ -168,9 +172,9 @@ void expert_tiled_kernel(
     for (int i = 0; i < T::kChunks; ++i) tok[pb][st_pos + i * (T::kRowStep / 32) * kKS * kWave] = stg[i];
   };
 
-  f32x16 acc[4][FB];
+  f32x16 acc[TB][FB];
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb)
+  for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
     for (int f = 0; f < FB; ++f)
 #pragma unroll
@@ -185,17 +189,17 @@ void expert_tiled_kernel(
 
   // Token operands, double-buffered: tk[x] holds the four token-block
   // fragments of one K step.
-  uint4 tk[2][4];
-  auto read_tk = [&](int pb, int sp, int j, uint4 (&d)[4]) {
+  uint4 tk[2][TB];
+  auto read_tk = [&](int pb, int sp, int j, uint4 (&d)[TB]) {
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) d[tb] = tok[pb][rd_pos[sp][j] + tb * kKS * kWave];
+    for (int tb = 0; tb < TB; ++tb) d[tb] = tok[pb][rd_pos[sp][j] + tb * kKS * kWave];
   };
   // Gate/up skips the MFMAs of 32-row token blocks that are all padding
   // (the last m-tile of an expert); in the down kernel the branches cost
   // more registers than it has.
-  auto mma = [&](const uint4 (&wj)[FB][kKS], int j, const uint4 (&d)[4]) {
+  auto mma = [&](const uint4 (&wj)[FB][kKS], int j, const uint4 (&d)[TB]) {
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+    for (int tb = 0; tb < TB; ++tb)
       if (!GATEUP || tb == 0 || tb * 32 < live_rows)
 #pragma unroll
         for (int f = 0; f < FB; ++f) acc[tb][f] = mfma32(wj[f][j], d[tb], acc[tb][f]);
@@ -245,7 +249,7 @@ void expert_tiled_kernel(
   // acc[tb][f]: token row tb*32 + lane % 32 of the tile; rows
   // mfma32_row(r, lane) of packed block nb * kBlocksPerTile + wave * FB + f.
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
+  for (int tb = 0; tb < TB; ++tb) {
     const int row = tb * 32 + lane % 32;
     if (row >= tile.rows) continue;
     const int slot = row2slot[tile.row_begin + row];
@@ -279,10 +283,10 @@ void expert_tiled_kernel(
   }
 }
 
-template <bool GATEUP, int FB, int WAVES>
+template <bool GATEUP, int FB, int WAVES, int TB>
 int64_t tiled_grid(int64_t N) {
-  using T = TileShape<GATEUP, FB, WAVES>;
-  const int64_t groups = (max_mtiles(N, kBM) + T::kGroup - 1) / T::kGroup;
+  using T = TileShape<GATEUP, FB, WAVES, TB>;
+  const int64_t groups = (max_mtiles(N, T::kBM) + T::kGroup - 1) / T::kGroup;
   return groups * T::kGroup * T::kColTiles;
 }
 
@@ -307,15 +311,16 @@ GateupTiles gateup_tiles(int64_t N) {
 }
 bool narrow_down_tiles(int64_t N) { return N <= 512; }
 
-template <bool GATEUP, int FB, int WAVES = (GATEUP ? 8 : 4), typename Out>
+template <bool GATEUP, int FB, int WAVES = (GATEUP ? 8 : 4), int TB = 4, typename Out>
 hipError_t launch_tiled(const uint16_t* A, const uint16_t* W, const int32_t* offsets,
                         const int32_t* row2slot, Out* out, int64_t N, hipStream_t stream) {
   uint16_t* H = nullptr;
   float* Y = nullptr;
   if constexpr (GATEUP) H = out; else Y = out;
-  hipLaunchKernelGGL((expert_tiled_kernel<GATEUP, FB, WAVES>), dim3(tiled_grid<GATEUP, FB, WAVES>(N)),
-                     dim3(TileShape<GATEUP, FB, WAVES>::kThreads), 0, stream, A, W, offsets, row2slot,
-                     H, Y);
+  hipLaunchKernelGGL((expert_tiled_kernel<GATEUP, FB, WAVES, TB>),
+                     dim3(tiled_grid<GATEUP, FB, WAVES, TB>(N)),
+                     dim3(TileShape<GATEUP, FB, WAVES, TB>::kThreads), 0, stream, A, W, offsets,
+                     row2slot, H, Y);
   return hipGetLastError();
 }
 
