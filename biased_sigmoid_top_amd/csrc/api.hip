@@ -190,20 +190,28 @@ class StageTimer {
     if (record(call_.n + 1)) ++call_.n;
     else on_ = false;
   }
+  // Hands a complete record to the pending list; otherwise (timing off
+  // mid-call after a failed event call, or no kernel recorded) destroys the
+  // events it created.
   ~StageTimer() {
-    if (!on_ || call_.n == 0) return;
-    std::lock_guard<std::mutex> lock(g_timing.mu);
-    if (g_timing.pending.size() >= kMaxPending) (void)drain_pending();
-    g_timing.pending.push_back(call_);
+    if (on_ && call_.n > 0) {
+      std::lock_guard<std::mutex> lock(g_timing.mu);
+      if (g_timing.pending.size() >= kMaxPending) (void)drain_pending();
+      g_timing.pending.push_back(call_);
+      return;
+    }
+    for (int i = 0; i < created_; ++i) (void)hipEventDestroy(call_.ev[i]);
   }
 
  private:
   bool record(int i) {
     if (hipEventCreate(&call_.ev[i]) != hipSuccess) return false;
+    created_ = i + 1;
     return hipEventRecord(call_.ev[i], stream_) == hipSuccess;
   }
   hipStream_t stream_;
   bool on_ = false;
+  int created_ = 0;  // events created so far (ev[0 .. created_ - 1])
   TimedCall call_;
 };
 
