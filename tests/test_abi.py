@@ -150,5 +150,9 @@ def test_fp8_argument_checks(lib):
     assert d(a[0], a[0] + 64, a[2], None) == _lib.ERR_INVALID_ARGUMENT
 
 
+def test_timing_read_checks_its_arguments(lib):
+    assert lib.lfm_moe_timing_read(None, None) == _lib.ERR_INVALID_ARGUMENT
+
+
 def test_release_without_allocation_is_a_no_op(lib):
     lib.lfm_moe_release()

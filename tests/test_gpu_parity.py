@@ -365,6 +365,30 @@ def test_concurrent_streams_with_distinct_workspaces(moe):
             assert torch.equal(a, b), f"repetition {rep}"
 
 
+def test_stage_timing_counts_and_times(moe):
+    """lfm_moe_timing_*: with timing on, each call records one launch per
+    stage it runs (the decode path has no dispatch stage) with a positive
+    time; after timing is switched off nothing more is recorded."""
+    for N, stages in ((64, ("route", "gateup", "down", "combine")),
+                      (300, ("route", "dispatch", "gateup", "down", "combine"))):
+        inp, dev = _layer_case(N, 1200 + N)
+        args = (dev["X"], dev["W_r"], dev["bias"], dev["W_gateup"], dev["W_down"])
+        _step(f"stage timing N={N}")
+        moe.timing_enable(True)
+        for _ in range(3):
+            moe.forward(*args)
+        t = moe.timing_read()
+        moe.timing_enable(False)
+        moe.forward(*args)
+        torch.cuda.synchronize()
+        for name, (ms, n) in t.items():
+            if name in stages:
+                assert n == 3 and ms > 0, (N, name, ms, n)
+            else:
+                assert n == 0, (N, name, n)
+        assert all(n == 0 for _, n in moe.timing_read().values())
+
+
 def test_zero_tokens_is_a_no_op(moe):
     inp, dev = _layer_case(1, 7)
     X0 = dev["X"][:0]
