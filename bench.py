@@ -225,25 +225,38 @@ def summarize(p, wall_ms, per_kernel):
     )
 
 
+FP8_STREAM = 256  # FP8 layer: weight-streaming kernels up to this many tokens
+
+
 def summarize_fp8(p, wall_ms, per_kernel, label, note):
     """Summary of FP8-expert steps: bytes are the FP8 codes and scales of the
-    active experts, the router, x in and out."""
+    active experts, the router, x in and out; FLOPs are the layer's (the
+    products run on the bf16 MFMA on widened codes)."""
     N = p["N"]
     A = sum(1 for c in p["counts"] if c > 0)
     s = wall_ms * 1e-3
     gu_ms, dn_ms = per_kernel["gateup"], per_kernel["down"]
     gu_gbs = fp8_gateup_bytes(A, N) / (gu_ms * 1e-3) / 1e9
+    gu_tflops = gateup_flops(N) / (gu_ms * 1e-3) / 1e12
     gbs = fp8_layer_bytes(A, N) / s / 1e9
+    tflops = N * FLOP_PER_TOKEN / s / 1e12
+    hbm = tflops * 1e3 / gbs < 0.5 * BF16_PEAK_TFLOPS * 1e3 / HBM_PEAK_GBS
+    kernel = "gateup_decode_fp8" if N <= FP8_STREAM else "gateup_tiled_fp8"
+    if hbm:
+        roof = dict(bound="hbm", kernel=kernel, achieved=gu_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=gu_gbs / HBM_PEAK_GBS, traffic=measured_traffic(p["name"], "gateup_fp8"),
+                    bytes_per_launch=fp8_gateup_bytes(A, N), avg_launch_ms=gu_ms,
+                    down_gbs=fp8_down_bytes(A, N) / (dn_ms * 1e-3) / 1e9)
+    else:
+        roof = dict(bound="mfma", kernel=kernel, achieved=gu_tflops, peak=BF16_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=gu_tflops / BF16_PEAK_TFLOPS, traffic=None,
+                    flops_per_launch=gateup_flops(N), avg_launch_ms=gu_ms)
     return dict(config=label, N=N, dtype="fp8-e4m3 experts (bf16 router, fp32 accumulation)",
                 active_experts=A, max_tokens_per_expert=max(p["counts"]), ms_per_step=wall_ms,
-                tokens_per_s=N / s, gbs=gbs, hbm_frac=gbs / HBM_PEAK_GBS, bound="hbm",
-                roofline_frac=gbs / HBM_PEAK_GBS, kernel_ms=per_kernel,
-                roofline=dict(bound="hbm", kernel="gateup_decode_fp8", achieved=gu_gbs,
-                              peak=HBM_PEAK_GBS, unit="GB/s", frac=gu_gbs / HBM_PEAK_GBS,
-                              traffic=measured_traffic(p["name"], "gateup_fp8"),
-                              bytes_per_launch=fp8_gateup_bytes(A, N), avg_launch_ms=gu_ms,
-                              down_gbs=fp8_down_bytes(A, N) / (dn_ms * 1e-3) / 1e9),
-                note=note)
+                tokens_per_s=N / s, gbs=gbs, hbm_frac=gbs / HBM_PEAK_GBS, tflops=tflops,
+                mfma_frac=tflops / BF16_PEAK_TFLOPS, bound="hbm" if hbm else "mfma",
+                roofline_frac=gbs / HBM_PEAK_GBS if hbm else tflops / BF16_PEAK_TFLOPS,
+                kernel_ms=per_kernel, roofline=roof, note=note)
 
 
 def measure_fp8(p, steps, warmup, label, note, q=None):
@@ -592,6 +605,10 @@ def measure_configs(args):
         if label == "C1u":
             out.append(measure_fp8(p, steps, args.warmup, "F1u",
                                    "supplementary: C1u with FP8 block-scaled experts"))
+        if label == "C2":
+            out.append(measure_fp8(p, steps, max(2, args.warmup // 10), "F2",
+                                   "supplementary: C2 with FP8 block-scaled experts (grouped kernels "
+                                   "in FP8 mode)"))
         del p
         torch.cuda.empty_cache()
     e = measure_stack(max(3, args.steps // 40), 1)

@@ -20,9 +20,11 @@ ERR_WORKSPACE_TOO_SMALL = 2
 ERR_OUT_OF_MEMORY = 3
 ERR_HIP = 4
 
-WS_IDX, WS_W, WS_BLOCKCOUNTS, WS_OFFSETS, WS_ROW2SLOT, WS_H, WS_Y, WS_X, WS_ROUTER_PARTIAL = range(9)
+(WS_IDX, WS_W, WS_BLOCKCOUNTS, WS_OFFSETS, WS_ROW2SLOT, WS_H, WS_Y, WS_X, WS_ROUTER_PARTIAL,
+ WS_XQ, WS_XS, WS_HQ, WS_HS) = range(13)
 DECODE_MAX_TOKENS = 96
-FP8_MAX_TOKENS = 256
+FP8_MAX_TOKENS = 1 << 24
+FP8_STREAM_TOKENS = 256
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64

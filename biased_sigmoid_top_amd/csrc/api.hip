@@ -42,6 +42,12 @@ void region_sizes(int64_t N, size_t (&sz)[LFM_MOE_WS_REGIONS]) {
   sz[LFM_MOE_WS_Y] = rows * kHidden * sizeof(float);
   sz[LFM_MOE_WS_X] = n * kHidden * sizeof(uint16_t);
   sz[LFM_MOE_WS_ROUTER_PARTIAL] = route_partial_bytes(N);
+  // FP8 grouped path only: quantised rows and their per-128 group scales.
+  const bool fp8_grouped = N > LFM_MOE_FP8_STREAM_TOKENS;
+  sz[LFM_MOE_WS_XQ] = fp8_grouped ? n * kHidden * sizeof(uint16_t) : 0;
+  sz[LFM_MOE_WS_XS] = fp8_grouped ? n * (kHidden / 128) * sizeof(float) : 0;
+  sz[LFM_MOE_WS_HQ] = fp8_grouped ? rows * kFF * sizeof(uint16_t) : 0;
+  sz[LFM_MOE_WS_HS] = fp8_grouped ? rows * (kFF / 128) * sizeof(float) : 0;
 }
 
 size_t region_offset(int64_t N, int region) {
@@ -223,6 +229,8 @@ T* region(void* ws, int64_t N, lfm_moe_ws_region r) {
 // Decode-shaped batches take the expert-major streaming kernels, which
 // group their own tokens; larger batches go through the dispatch step.
 bool use_decode_path(int64_t N) { return N <= kDecodeMaxTokens; }
+static_assert(kStreamMaxTokens == LFM_MOE_FP8_STREAM_TOKENS,
+              "the FP8 layer streams exactly the batches the streaming kernels can group");
 
 // route -> [dispatch] -> gate/up -> down -> combine.  Arguments already checked.
 lfm_moe_status run_layer(const uint16_t* X, const uint16_t* W_r, const float* bias,
@@ -282,8 +290,7 @@ lfm_moe_status check_fp8_args(const uint16_t* X, const uint16_t* W_r, const floa
                               const uint8_t* W_down_fp8, const float* scales_down, const float* out,
                               int64_t N) {
   if (N < 0) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "N must be >= 0");
-  if (N > LFM_MOE_FP8_MAX_TOKENS)
-    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "N exceeds LFM_MOE_FP8_MAX_TOKENS (FP8 experts: batches of up to 256 tokens)");
+  if (N > LFM_MOE_FP8_MAX_TOKENS) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "N exceeds LFM_MOE_FP8_MAX_TOKENS");
   if (N == 0) return LFM_MOE_OK;
   if (!X || !W_r || !bias || !W_gateup_fp8 || !scales_gateup || !W_down_fp8 || !scales_down || !out)
     return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "null tensor pointer");
@@ -316,16 +323,45 @@ lfm_moe_status run_fp8(const uint16_t* X, const uint16_t* W_r, const float* bias
   float* Y = region<float>(ws, N, LFM_MOE_WS_Y);
   float* part = region<float>(ws, N, LFM_MOE_WS_ROUTER_PARTIAL);
   const int n = static_cast<int>(N);
+  const bool streaming = N <= LFM_MOE_FP8_STREAM_TOKENS;
+  int32_t* blockcounts = region<int32_t>(ws, N, LFM_MOE_WS_BLOCKCOUNTS);
   hipError_t e;
-  if ((e = launch_route(X, W_r, bias, idx, w, nullptr, part, n, stream)) != hipSuccess)
+  if ((e = launch_route(X, W_r, bias, idx, w, streaming ? nullptr : blockcounts, part, n, stream)) !=
+      hipSuccess)
     return hip_fail(e, "route kernel launch");
   timer.after(1);
-  if ((e = launch_gateup_decode_fp8(X, W_gateup_fp8, scales_gateup, idx, H, n, stream)) != hipSuccess)
-    return hip_fail(e, "fp8 gate/up kernel launch");
-  timer.after(3);
-  if ((e = launch_down_decode_fp8(H, W_down_fp8, scales_down, idx, Y, n, stream)) != hipSuccess)
-    return hip_fail(e, "fp8 down kernel launch");
-  timer.after(4);
+  if (streaming) {
+    if ((e = launch_gateup_decode_fp8(X, W_gateup_fp8, scales_gateup, idx, H, n, stream)) != hipSuccess)
+      return hip_fail(e, "fp8 gate/up kernel launch");
+    timer.after(3);
+    if ((e = launch_down_decode_fp8(H, W_down_fp8, scales_down, idx, Y, n, stream)) != hipSuccess)
+      return hip_fail(e, "fp8 down kernel launch");
+    timer.after(4);
+  } else {
+    // Grouped: dispatch, X quantised per group (timed with the dispatch),
+    // gate/up, H quantised per group (timed with down), down.
+    int32_t* offsets = region<int32_t>(ws, N, LFM_MOE_WS_OFFSETS);
+    int32_t* row2slot = region<int32_t>(ws, N, LFM_MOE_WS_ROW2SLOT);
+    uint16_t* Xq = region<uint16_t>(ws, N, LFM_MOE_WS_XQ);
+    float* Xs = region<float>(ws, N, LFM_MOE_WS_XS);
+    uint16_t* Hq = region<uint16_t>(ws, N, LFM_MOE_WS_HQ);
+    float* Hs = region<float>(ws, N, LFM_MOE_WS_HS);
+    if ((e = launch_dispatch(idx, blockcounts, offsets, row2slot, n, stream)) != hipSuccess)
+      return hip_fail(e, "dispatch kernel launch");
+    if ((e = launch_quantize_groups(X, N, kHidden, Xq, Xs, stream)) != hipSuccess)
+      return hip_fail(e, "quantize kernel launch");
+    timer.after(2);
+    if ((e = launch_gateup_tiled_fp8(Xq, W_gateup_fp8, scales_gateup, Xs, offsets, row2slot, H, N,
+                                     stream)) != hipSuccess)
+      return hip_fail(e, "fp8 gate/up kernel launch");
+    timer.after(3);
+    if ((e = launch_quantize_groups(H, N * kTopK, kFF, Hq, Hs, stream)) != hipSuccess)
+      return hip_fail(e, "quantize kernel launch");
+    if ((e = launch_down_tiled_fp8(Hq, W_down_fp8, scales_down, Hs, offsets, row2slot, Y, N,
+                                   stream)) != hipSuccess)
+      return hip_fail(e, "fp8 down kernel launch");
+    timer.after(4);
+  }
   if ((e = launch_combine(Y, w, nullptr, out, N, stream)) != hipSuccess)
     return hip_fail(e, "combine kernel launch");
   timer.after(5);

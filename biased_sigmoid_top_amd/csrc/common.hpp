@@ -19,7 +19,7 @@ constexpr float kRmsEps = 1e-6f;
 // grouped path); beyond it they stream an expert's weights once per pass
 // (N = 128: 307 us against 192 us).
 constexpr int kDecodeMaxTokens = 96;   // bf16 layer: weight-streaming path up to here
-constexpr int kStreamMaxTokens = 256;  // tokens the weight-streaming kernels can group (FP8 layer limit)
+constexpr int kStreamMaxTokens = 256;  // tokens the weight-streaming kernels can group (FP8 layer up to here)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -157,6 +157,27 @@ __device__ __forceinline__ bool map_mtile(const int* __restrict__ offsets, int m
   t.row_begin = beg_e + m0;
   t.rows = min(tile_rows, cnt_e - m0);
   return true;
+}
+
+// FP8 (OCP E4M3) helpers.  Four floats to four codes, round to nearest
+// even (the gfx950 conversion instruction; a value rounding to zero keeps its
+// sign).  The callers scale by 448 / amax first, so no input exceeds 448.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
+}
+
+// Eight E4M3 codes (bytes of lo, then hi) as eight bf16 values (exact: every
+// E4M3 value is a bf16 value).
+__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  using bf16x2 = __bf16 __attribute__((ext_vector_type(2)));
+  const bf16x2 v[4] = {__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, false),
+                       __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, true),
+                       __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, false),
+                       __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, true)};
+  uint4 r;
+  __builtin_memcpy(&r, v, sizeof(r));
+  return r;
 }
 
 }  // namespace lfm

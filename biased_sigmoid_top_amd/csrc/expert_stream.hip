@@ -350,23 +350,6 @@ __device__ __forceinline__ uint32_t fp8_block_bytes(int e, int b) {
   return static_cast<uint32_t>((e * kBlocks + b) * kPairs) * kFp8FragBytes;
 }
 
-__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
-}
-
-// Eight E4M3 codes (bytes of lo, then hi) as eight bf16 values (exact).
-__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
-  using bf16x2 = __bf16 __attribute__((ext_vector_type(2)));
-  const bf16x2 v[4] = {__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, false),
-                       __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, true),
-                       __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, false),
-                       __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, true)};
-  uint4 r;
-  __builtin_memcpy(&r, v, sizeof(r));
-  return r;
-}
-
 template <bool GATEUP, int GPW>
 __device__ __forceinline__ void stream_units_fp8(const uint16_t* __restrict__ B,
                                                  const uint8_t* __restrict__ Wq,

@@ -28,6 +28,15 @@
 // block are 16 gate rows and the matching 16 up rows, so the SiLU product
 // is formed in registers.
 //
+// FP8 mode (the FP8 layer above 256 tokens): the weights are the FP8 codes
+// of pack_fp8.hip, one 1 KB fragment per 32-row block and K stage, widened
+// to bf16 in registers before each MFMA; the token rows are the bf16 values
+// of their E4M3 codes (quant.hip).  Each 128-wide K group -- one pass of the
+// four-stage loop -- is accumulated on its own (products of codes, exact,
+// summed in fp32) and added into the result times weight block scale x the
+// token row's scale, as the block-scaled format defines.  That second set of
+// accumulators leaves room for one weight block per wavefront only.
+//
 // Grid: workgroup ids are dealt to the 8 XCDs round-robin.  Tiles are
 // launched in groups of m-tiles x column tiles that hold a multiple of 8
 // tiles, each XCD taking a run of consecutive (column-major) tiles of the
@@ -84,16 +93,24 @@ struct TileShape {
   static_assert(kGroup * kColTiles % kXcds == 0, "a launch group deals evenly over the XCDs");
 };
 
-template <bool GATEUP, int FB_, int WAVES_, int TB_>
+// FP8: Wp holds the FP8 codes of the experts (pack_fp8.hip layout: 1 KB
+// fragments of 32 rows x 32 K, one per K stage), Ws their fp32 block scales,
+// A the bf16 values of the token rows' E4M3 codes and As the rows' scales per
+// 128-wide K group.  Each group of four stages (128 K) is accumulated on its
+// own and added into the result times weight scale x token scale.
+template <bool GATEUP, int FB_, int WAVES_, int TB_, bool FP8 = false>
 __global__ __launch_bounds__((TileShape<GATEUP, FB_, WAVES_, TB_>::kThreads),
                              (TileShape<GATEUP, FB_, WAVES_, TB_>::kPerCu))
 void expert_tiled_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Wp,
+    const uint16_t* __restrict__ A, const void* __restrict__ Wp,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ row2slot,
-    uint16_t* __restrict__ H, float* __restrict__ Y) {
+    uint16_t* __restrict__ H, float* __restrict__ Y, const float* __restrict__ Ws,
+    const float* __restrict__ As) {
   using T = TileShape<GATEUP, FB_, WAVES_, TB_>;
   constexpr int FB = T::FB;
   constexpr int TB = T::kTB;
+  constexpr int kWK = FP8 ? 1 : kKS;  // 16-byte weight loads per block and stage
+  static_assert(!FP8 || kWSlots * kBK == 128, "an FP8 scale group is one pass of the stage loop");
   static_assert(T::kStages % kWSlots == 0, "the stage loop is unrolled by the ring size");
   // Token fragments: 2 pair buffers x (2 stages x 4 token blocks x kKS steps).
   __shared__ uint4 tok[2][2 * TB * kKS * kWave];
@@ -144,21 +161,22 @@ void expert_tiled_kernel(
   // read as buffer loads: the expert's packed matrix (12 MB at most) is the
   // buffer, the wavefront's first block a scalar offset, the lane's 16 bytes
   // of a fragment the only per-lane offset.
-  constexpr uint32_t kBlockBytes = static_cast<uint32_t>(T::kSteps) * kFragBytes;
-  const Rsrc wr = make_rsrc(Wp + static_cast<size_t>(uniform(tile.expert)) * T::kBlocks * (kBlockBytes / 2),
+  constexpr uint32_t kBlockBytes = static_cast<uint32_t>(T::kStages * kWK) * kFragBytes;
+  const Rsrc wr = make_rsrc(static_cast<const uint8_t*>(Wp) +
+                                static_cast<size_t>(uniform(tile.expert)) * T::kBlocks * kBlockBytes,
                             T::kBlocks * kBlockBytes);
   const uint32_t wbase = uniform(static_cast<uint32_t>((nb * T::kBlocksPerTile + wave * FB) * kBlockBytes));
   const uint32_t wlane = lane * 16;
 
-  uint4 wring[kWSlots][FB][kKS];
+  uint4 wring[kWSlots][FB][kWK];
   // Stages past the end reload the last stage (in bounds, never used).
-  auto load_w = [&](int s, uint4 (&wv)[FB][kKS]) {
+  auto load_w = [&](int s, uint4 (&wv)[FB][kWK]) {
     const uint32_t sc = s < T::kStages ? s : T::kStages - 1;
 #pragma unroll
     for (int f = 0; f < FB; ++f)
 #pragma unroll
-      for (int j = 0; j < kKS; ++j)
-        wv[f][j] = buf_ld<false>(wr, wlane, wbase + f * kBlockBytes + (sc * kKS + j) * kFragBytes);
+      for (int j = 0; j < kWK; ++j)
+        wv[f][j] = buf_ld<false>(wr, wlane, wbase + f * kBlockBytes + (sc * kWK + j) * kFragBytes);
   };
   constexpr int kPairs = T::kStages / 2;
   uint4 stg[T::kChunks];
@@ -173,6 +191,8 @@ void expert_tiled_kernel(
   };
 
   f32x16 acc[TB][FB];
+  // FP8: the current K group's products (unused otherwise).
+  f32x16 part[FP8 ? TB : 1][FP8 ? FB : 1];
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
@@ -197,12 +217,21 @@ void expert_tiled_kernel(
   // Gate/up skips the MFMAs of 32-row token blocks that are all padding
   // (the last m-tile of an expert); in the down kernel the branches cost
   // more registers than it has.
-  auto mma = [&](const uint4 (&wj)[FB][kKS], int j, const uint4 (&d)[TB]) {
+  auto mma = [&](const uint4 (&wj)[FB][kWK], int j, const uint4 (&d)[TB]) {
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb)
       if (!GATEUP || tb == 0 || tb * 32 < live_rows)
 #pragma unroll
-        for (int f = 0; f < FB; ++f) acc[tb][f] = mfma32(wj[f][j], d[tb], acc[tb][f]);
+        for (int f = 0; f < FB; ++f) {
+          if constexpr (FP8) {
+            // Lane bytes 0..7: K step 0 of the stage, 8..15: K step 1.
+            const uint4 wbf = j == 0 ? e4m3x8_to_bf16(wj[f][0].x, wj[f][0].y)
+                                     : e4m3x8_to_bf16(wj[f][0].z, wj[f][0].w);
+            part[tb][f] = mfma32(wbf, d[tb], part[tb][f]);
+          } else {
+            acc[tb][f] = mfma32(wj[f][j], d[tb], acc[tb][f]);
+          }
+        }
   };
   // The fences keep the issue order written here, which the wait counts
   // below rely on: weight loads, then the next LDS operands, then MFMAs.
@@ -217,7 +246,7 @@ void expert_tiled_kernel(
   // pair after that.  The second stage's barrier comes once its own LDS
   // reads are done, before its last MFMAs: it publishes the stored tokens
   // and frees buffer pb for the next store.
-  auto stage = [&](int s, int sp, int pb, uint4 (&wc)[FB][kKS], uint4 (&wn)[FB][kKS]) {
+  auto stage = [&](int s, int sp, int pb, uint4 (&wc)[FB][kWK], uint4 (&wn)[FB][kWK]) {
     static_assert(kKS == 2, "two K steps per stage");
     load_w(s + kWSlots - 1, wn);
     read_tk(pb, sp, 1, tk[1]);
@@ -240,10 +269,56 @@ void expert_tiled_kernel(
       fence();
     }
   };
+  // FP8 scales: this wavefront's weight row blocks (128 rows) and the
+  // tile rows' token rows (padding rows take row 0's; their results are
+  // dropped).
+  int srow[FP8 ? TB : 1];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const int row = tb * 32 + lane % 32;
+      const int slot = row2slot[tile.row_begin + (row < tile.rows ? row : 0)];
+      srow[tb] = GATEUP ? slot / kTopK : slot;
+    }
+  }
   for (int s = 0; s < T::kStages; s += kWSlots) {
+    float xs[FP8 ? TB : 1], wsa[FP8 ? FB : 1], wsb[FP8 ? FB : 1];
+    if constexpr (FP8) {
+      const int g = s / kWSlots;
+      constexpr int kG = T::K / 128;
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) xs[tb] = As[static_cast<size_t>(srow[tb]) * kG + g];
+      const int e = uniform(tile.expert);
+#pragma unroll
+      for (int f = 0; f < FB; ++f) {
+        const int blk = nb * T::kBlocksPerTile + wave * FB + f;
+        if (GATEUP) {  // gate rows (values r < 8 of a tile) and up rows
+          wsa[f] = Ws[((e * 2 + 0) * (kFF / 128) + blk / 8) * kG + g];
+          wsb[f] = Ws[((e * 2 + 1) * (kFF / 128) + blk / 8) * kG + g];
+        } else {
+          wsa[f] = wsb[f] = Ws[(e * (kHidden / 128) + blk / 4) * kG + g];
+        }
+      }
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int f = 0; f < FB; ++f)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) part[tb][f][r] = 0.f;
+    }
 #pragma unroll
     for (int q = 0; q < kWSlots; ++q)
       stage(s + q, q % 2, q / 2, wring[q], wring[(q + kWSlots - 1) % kWSlots]);
+    if constexpr (FP8) {
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int f = 0; f < FB; ++f) {
+          const float sa = wsa[f] * xs[tb], sb = wsb[f] * xs[tb];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[tb][f][r] += part[tb][f][r] * (r < 8 ? sa : sb);
+        }
+    }
   }
 
   // acc[tb][f]: token row tb*32 + lane % 32 of the tile; rows
@@ -311,16 +386,18 @@ GateupTiles gateup_tiles(int64_t N) {
 }
 bool narrow_down_tiles(int64_t N) { return N <= 512; }
 
-template <bool GATEUP, int FB, int WAVES = (GATEUP ? 8 : 4), int TB = 4, typename Out>
-hipError_t launch_tiled(const uint16_t* A, const uint16_t* W, const int32_t* offsets,
-                        const int32_t* row2slot, Out* out, int64_t N, hipStream_t stream) {
+template <bool GATEUP, int FB, int WAVES = (GATEUP ? 8 : 4), int TB = 4, bool FP8 = false,
+          typename Out>
+hipError_t launch_tiled(const uint16_t* A, const void* W, const int32_t* offsets,
+                        const int32_t* row2slot, Out* out, int64_t N, hipStream_t stream,
+                        const float* Ws = nullptr, const float* As = nullptr) {
   uint16_t* H = nullptr;
   float* Y = nullptr;
   if constexpr (GATEUP) H = out; else Y = out;
-  hipLaunchKernelGGL((expert_tiled_kernel<GATEUP, FB, WAVES, TB>),
+  hipLaunchKernelGGL((expert_tiled_kernel<GATEUP, FB, WAVES, TB, FP8>),
                      dim3(tiled_grid<GATEUP, FB, WAVES, TB>(N)),
                      dim3(TileShape<GATEUP, FB, WAVES, TB>::kThreads), 0, stream, A, W, offsets,
-                     row2slot, H, Y);
+                     row2slot, H, Y, Ws, As);
   return hipGetLastError();
 }
 
@@ -343,6 +420,18 @@ hipError_t launch_down_tiled(const uint16_t* H, const uint16_t* Wd, const int32_
                              const int32_t* row2slot, float* Y, int64_t N, hipStream_t stream) {
   return narrow_down_tiles(N) ? launch_tiled<false, 1, 4>(H, Wd, offsets, row2slot, Y, N, stream)
                               : launch_tiled<false, 2>(H, Wd, offsets, row2slot, Y, N, stream);
+}
+
+hipError_t launch_gateup_tiled_fp8(const uint16_t* Xq, const uint8_t* Wq, const float* Ws,
+                                   const float* Xs, const int32_t* offsets, const int32_t* row2slot,
+                                   uint16_t* H, int64_t N, hipStream_t stream) {
+  return launch_tiled<true, 1, 8, 4, true>(Xq, Wq, offsets, row2slot, H, N, stream, Ws, Xs);
+}
+
+hipError_t launch_down_tiled_fp8(const uint16_t* Hq, const uint8_t* Wq, const float* Ws,
+                                 const float* Hs, const int32_t* offsets, const int32_t* row2slot,
+                                 float* Y, int64_t N, hipStream_t stream) {
+  return launch_tiled<false, 1, 4, 4, true>(Hq, Wq, offsets, row2slot, Y, N, stream, Ws, Hs);
 }
 
 }  // namespace lfm

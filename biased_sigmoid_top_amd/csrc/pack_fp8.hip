@@ -37,12 +37,6 @@ constexpr int kQBlock = 128;                  // rows and columns of a weight bl
 constexpr int kQThreads = 256;
 constexpr int kQChunks = kQBlock * kQBlock / 8 / kQThreads;  // 8-column runs per thread
 
-// Four floats to four E4M3 codes (round to nearest even).
-__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
-}
-
 // One workgroup per 128 x 128 block.  W: the matrix's first element of the
 // block's row 0, column 0 (row pitch `cols`); dst(r, c) gives the packed byte
 // offset of row r, column c (c a multiple of 8) of the block.

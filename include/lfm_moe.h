@@ -45,15 +45,18 @@
 extern "C" {
 #endif
 
-#define LFM_MOE_ABI_VERSION 2
+#define LFM_MOE_ABI_VERSION 3
 #define LFM_MOE_HIDDEN 2048
 #define LFM_MOE_EXPERTS 64
 #define LFM_MOE_TOPK 4
 #define LFM_MOE_FF 1536
 /* Largest N accepted: grouped rows (4N) and their element offsets stay in range. */
 #define LFM_MOE_MAX_TOKENS (1LL << 24)
-/* Largest N of lfm_moe_forward_fp8 (decode and verification-shaped batches). */
-#define LFM_MOE_FP8_MAX_TOKENS 256
+/* Largest N of lfm_moe_forward_fp8, and the largest N it runs on the
+ * weight-streaming kernels (decode and verification-shaped batches; larger
+ * batches take the grouped kernels in FP8 mode). */
+#define LFM_MOE_FP8_MAX_TOKENS LFM_MOE_MAX_TOKENS
+#define LFM_MOE_FP8_STREAM_TOKENS 256
 
 typedef enum {
   LFM_MOE_OK = 0,
@@ -156,7 +159,12 @@ typedef enum {
   LFM_MOE_WS_X = 7,         /* [N, 2048] bf16 normalised input (block forward only) */
   LFM_MOE_WS_ROUTER_PARTIAL = 8, /* [ceil(N/16), 16, 16, 64] fp32 router partial logits per K slice;
                                     empty above 2048 tokens, where the router keeps them in LDS */
-  LFM_MOE_WS_REGIONS = 9
+  LFM_MOE_WS_XQ = 9,        /* [N, 2048] bf16: the values of X's E4M3 codes per 128-wide group
+                               (FP8 layer above LFM_MOE_FP8_STREAM_TOKENS only) */
+  LFM_MOE_WS_XS = 10,       /* [N, 16] fp32: their scales */
+  LFM_MOE_WS_HQ = 11,       /* [4N, 1536] bf16: the values of H's E4M3 codes, slot order (same) */
+  LFM_MOE_WS_HS = 12,       /* [4N, 12] fp32: their scales */
+  LFM_MOE_WS_REGIONS = 13
 } lfm_moe_ws_region;
 
 /* Byte offset of `region` inside a workspace sized for N tokens; (size_t)-1 if invalid. */
@@ -217,15 +225,17 @@ lfm_moe_status lfm_moe_block_forward_ws(float* x_inout, const uint16_t* W_r, con
  *   W_down_fp8 [64 * 2048 * 1536] bytes, scales_down [64][16][12] fp32
  *   (written); fragment (e * 64 + b) * 48 + kp holds rows 32 b .. 32 b + 31,
  *   columns 32 kp .. 32 kp + 31, in the same lane order.
- * lfm_moe_forward_fp8: the layer with these experts, for N <= 256 tokens
- *   (LFM_MOE_FP8_MAX_TOKENS: decode and verification-shaped batches, where
- *   the layer streams its weights; larger N returns
- *   LFM_MOE_ERR_INVALID_ARGUMENT).  Router and mixture weights as in
+ * lfm_moe_forward_fp8: the layer with these experts, 0 <= N <=
+ *   LFM_MOE_FP8_MAX_TOKENS.  Router and mixture weights as in
  *   lfm_moe_forward; each expert's input rows (X, then the bf16 hidden rows)
  *   are quantised per group of 128 features as above; the products of
  *   codes are exact and summed in fp32, then scaled by weight scale x
- *   activation scale per 128-wide K group; out [N, 2048] fp32.
- *   Library-owned workspace, as lfm_moe_forward.
+ *   activation scale per 128-wide K group; out [N, 2048] fp32.  Up to
+ *   LFM_MOE_FP8_STREAM_TOKENS tokens the expert kernels stream the weights
+ *   and quantise the rows in registers; above, the dispatch step groups the
+ *   rows, X and H are quantised into the XQ/XS and HQ/HS workspace regions
+ *   and the grouped kernels run in FP8 mode.  Library-owned workspace, as
+ *   lfm_moe_forward.
  * lfm_moe_forward_fp8_ws: the same with a caller workspace, as
  *   lfm_moe_forward_ws (same size and regions: the routing, the bf16 hidden
  *   rows H and the fp32 expert rows Y, both in slot order t * 4 + j; the

@@ -35,21 +35,29 @@ def test_abi_version_matches_header(lib):
 
 
 def test_workspace_layout(lib):
-    for N in [1, 16, 17, 64, 255, 4096, 16384]:
+    for N in [1, 16, 17, 64, 255, 256, 257, 4096, 16384]:
         total = lib.lfm_moe_workspace_bytes(N)
-        offs = [lib.lfm_moe_workspace_offset(N, r) for r in range(9)]
+        offs = [lib.lfm_moe_workspace_offset(N, r) for r in range(13)] + [total]
         assert offs[0] == 0
         assert all(o % 256 == 0 for o in offs)
-        assert offs == sorted(offs) and offs[-1] <= total
+        assert offs == sorted(offs)
+        size = lambda r: offs[r + 1] - offs[r]
         # H and Y regions hold 4N rows.
-        assert offs[_lib.WS_Y] - offs[_lib.WS_H] >= 4 * N * 1536 * 2
-        assert offs[_lib.WS_X] - offs[_lib.WS_Y] >= 4 * N * 2048 * 4
-        assert offs[_lib.WS_ROUTER_PARTIAL] - offs[_lib.WS_X] >= N * 2048 * 2
-        part = total - offs[_lib.WS_ROUTER_PARTIAL]
+        assert size(_lib.WS_H) >= 4 * N * 1536 * 2
+        assert size(_lib.WS_Y) >= 4 * N * 2048 * 4
+        assert size(_lib.WS_X) >= N * 2048 * 2
         if N <= 2048:
-            assert part >= -(-N // 16) * 16 * 16 * 64 * 4
+            assert size(_lib.WS_ROUTER_PARTIAL) >= -(-N // 16) * 16 * 16 * 64 * 4
         else:
-            assert part == 0  # the fused router keeps its partial logits in LDS
+            assert size(_lib.WS_ROUTER_PARTIAL) == 0  # the fused router keeps its partials in LDS
+        # Quantised rows and scales of the FP8 layer's grouped path (above 256 tokens only).
+        fp8 = N > _lib.FP8_STREAM_TOKENS
+        assert size(_lib.WS_XQ) >= (N * 2048 * 2 if fp8 else 0)
+        assert size(_lib.WS_XS) >= (N * 16 * 4 if fp8 else 0)
+        assert size(_lib.WS_HQ) >= (4 * N * 1536 * 2 if fp8 else 0)
+        assert size(_lib.WS_HS) >= (4 * N * 12 * 4 if fp8 else 0)
+        if not fp8:
+            assert all(size(r) == 0 for r in (_lib.WS_XQ, _lib.WS_XS, _lib.WS_HQ, _lib.WS_HS))
     assert lib.lfm_moe_workspace_bytes(-1) == 0
     assert lib.lfm_moe_workspace_offset(10, 99) == ctypes.c_size_t(-1).value
 

@@ -5,7 +5,8 @@ Weights: the N = 64 decode workload's.  The packed codes and scales are
 compared bit-exactly with oracle.fp8's block quantisation of every expert
 (after undoing the documented fragment permutation); the layer output with
 the oracle's FP8 layer at N = 64 (the workload itself) and at ragged token
-counts up to the entry point's limit of 256.
+counts on both of the FP8 layer's kernel paths (weight streaming up to 256
+tokens, the grouped kernels in FP8 mode above).
 """
 
 import numpy as np
@@ -175,8 +176,9 @@ def test_fp8_forward_parity_decode_n64(moe):
     _check_fp8_forward(moe, inp, dev, q, inp["X"].shape[0])
 
 
-@pytest.mark.parametrize("N", [1, 17, 33, 95, 96, 97, 160, 255, 256])
+@pytest.mark.parametrize("N", [1, 17, 33, 95, 96, 97, 160, 255, 256, 257, 700, 2049, 4096])
 def test_fp8_forward_ragged(moe, N):
+    """Streaming kernels up to 256 tokens, grouped kernels in FP8 mode above."""
     inp0, dev0, q = _decode_case(moe)
     X = oracle.block_input(synth.hidden_states(N, 500 + N).numpy())
     inp = dict(inp0, X=X)
@@ -184,23 +186,23 @@ def test_fp8_forward_ragged(moe, N):
     _check_fp8_forward(moe, inp, dev, q, N)
 
 
-def test_fp8_zero_tokens_and_limit(moe):
+def test_fp8_zero_tokens(moe):
     inp, dev, q = _decode_case(moe)
     X = dev["X"][:0]
     out = torch.empty(0, 2048, dtype=torch.float32, device="cuda")
     moe.forward_fp8(X, dev["W_r"], dev["bias"], dev["gateup_fp8"], dev["down_fp8"], out=out)
-    from biased_sigmoid_top_amd import _lib
-    big = torch.zeros(_lib.FP8_MAX_TOKENS + 1, 2048, dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(RuntimeError):
-        moe.forward_fp8(big, dev["W_r"], dev["bias"], dev["gateup_fp8"], dev["down_fp8"])
 
 
-def test_fp8_graph_capture_replays_match_eager(moe):
-    """The FP8 layer's _ws form captured in a HIP graph replays to the eager
-    result, bit for bit, with eager work between the replays."""
+@pytest.mark.parametrize("N", [64, 700])
+def test_fp8_graph_capture_replays_match_eager(moe, N):
+    """The FP8 layer's _ws form (streaming and grouped kernels) captured in a
+    HIP graph replays to the eager result, bit for bit, with eager work
+    between the replays."""
     from test_gpu_parity import _graph_replays_match
-    inp, dev, q = _decode_case(moe)
-    N = inp["X"].shape[0]
+    inp, dev0, q = _decode_case(moe)
+    X = dev0["X"] if N == 64 else torch.from_numpy(
+        oracle.block_input(synth.hidden_states(N, 1700).numpy())).to(torch.bfloat16).cuda()
+    dev = dict(dev0, X=X)
     ws = moe.alloc_workspace(N)
     args = (dev["X"], dev["W_r"], dev["bias"], dev["gateup_fp8"], dev["down_fp8"])
     _step(f"graph capture forward_fp8 N={N}")
