@@ -437,7 +437,7 @@ def main():
         cpu = cpu_baseline(head, args.cpu_seconds)
 
     line = build_line(args, h, head["seed"], second, cpu)
-    line["fp8_decode"] = fp8
+    line["fp8"] = fp8
     line["device"] = dev_info
     if args.configs:
         del head
