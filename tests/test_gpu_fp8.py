@@ -225,10 +225,11 @@ def test_fp8_writes_stay_in_bounds(moe):
     assert torch.all(ws_all[nbytes:] == 0xAB).item(), "bytes past the workspace written"
 
 
-@pytest.mark.parametrize("N", [5, 96, 256])
+@pytest.mark.parametrize("N", [5, 96, 256, 1000])
 def test_fp8_every_token_on_the_same_four_experts(moe, N):
     """Degenerate routing: a large bias puts every token on experts 60..63,
-    so each has N rows (up to eight 32-token passes) and 60 experts are
+    so each has N rows (up to eight 32-token passes on the streaming
+    kernels, eight 128-row m-tiles on the grouped ones) and 60 experts are
     empty."""
     inp0, dev0, q = _decode_case(moe)
     bias = torch.zeros(64)
