@@ -370,6 +370,41 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": n, "copies": 3}))
 
 
+def vendor_gemm(steps=20, warmup=5):
+    """Context, not the product: the vendor BLAS (torch.bmm / torch.matmul on
+    ROCm) on uniform shapes with the FLOPs of the 4,096-token expert GEMMs --
+    64 experts x 256 rows, and the same rows against one dense weight matrix.
+    Nothing here touches the layer's kernels."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    out = {}
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(steps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / steps * 1e3
+
+    for name, (n_out, k) in {"gateup": (2 * FF, D), "down": (D, FF)}.items():
+        a = torch.randn(E, 256, k, device="cuda", dtype=torch.bfloat16, generator=g)
+        # Right operands materialised as [E, K, n_out] (contiguous, never a transposed view).
+        b = torch.randn(E, k, n_out, device="cuda", dtype=torch.bfloat16, generator=g)
+        flop = 2 * E * 256 * n_out * k
+        us = timed(lambda: torch.bmm(a, b))
+        out[f"{name}_bmm_64x256"] = {"us": round(us, 1), "tflops": round(flop / us / 1e6, 1)}
+        a2, b2 = a.reshape(E * 256, k), b[0].contiguous()
+        us = timed(lambda: torch.matmul(a2, b2))
+        out[f"{name}_dense_16384"] = {"us": round(us, 1), "tflops": round(flop / us / 1e6, 1)}
+    print(json.dumps({"vendor_gemm": out, "steps": steps, "dtype": "bf16"}))
+
+
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -381,6 +416,8 @@ def parse_args(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the oracle baseline (0 leaves it out)")
     ap.add_argument("--copy-probe", action="store_true", help="only run a plain 1 GiB copy")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only time the vendor BLAS on uniform shapes with the FLOPs of the 4,096-token expert GEMMs")
     ap.add_argument("--workload", default="decode_n64", help="headline workload")
     ap.add_argument("--configs", action="store_true",
                     help="also measure every configuration (C0-C4, the 38-block stack included; "
@@ -402,6 +439,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.vendor_gemm:
+        vendor_gemm()
         return
 
     import biased_sigmoid_top_amd  # noqa: F401  (fails loudly without the built library)
