@@ -6,7 +6,7 @@ Importing the package loads liblfm_moe.so and fails if it has not been built.
 
 from . import _lib
 from .api import (EXPERTS, FF, HIDDEN, TOP_K, abi_version, alloc_workspace,  # noqa: F401
-                  block_forward, forward, forward_fp8, pack_down, pack_fp8_down,
+                  block_forward, experts, experts_fp8, forward, forward_fp8, pack_down, pack_fp8_down,
                   pack_fp8_gateup, pack_gateup, release, rmsnorm,
                   route, timing_enable,
                   timing_read, workspace_bytes, workspace_offset, workspace_view)

@@ -42,12 +42,14 @@ SIGNATURES = {
     "lfm_moe_workspace_bytes": (_SZ, [_I64]),
     "lfm_moe_workspace_offset": (_SZ, [_I64, ctypes.c_int]),
     "lfm_moe_forward_ws": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _P, _SZ, _P]),
+    "lfm_moe_experts_ws": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _P, _SZ, _P]),
     "lfm_moe_block_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _P]),
     "lfm_moe_block_forward_ws": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _P, _SZ, _P]),
     "lfm_moe_pack_fp8_gateup": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "lfm_moe_pack_fp8_down": (ctypes.c_int, [_P, _P, _P, _P]),
     "lfm_moe_forward_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _P]),
     "lfm_moe_forward_fp8_ws": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _P, _SZ, _P]),
+    "lfm_moe_experts_fp8_ws": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _P, _SZ, _P]),
     "lfm_moe_release": (None, []),
     "lfm_moe_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "lfm_moe_timing_read": (ctypes.c_int, [_P, _P]),

@@ -139,9 +139,9 @@ def pack_fp8_down(W_down, stream=None):
 
 
 def forward_fp8(X, W_r, bias, gateup_fp8, down_fp8, out=None, workspace=None, stream=None):
-    """The layer with FP8 experts (N <= 256): gateup_fp8 and down_fp8 are the
-    (codes, scales) pairs of pack_fp8_gateup / pack_fp8_down.  With
-    ``workspace`` the _ws entry point is used."""
+    """The layer with FP8 experts (any N up to FP8_MAX_TOKENS): gateup_fp8 and
+    down_fp8 are the (codes, scales) pairs of pack_fp8_gateup /
+    pack_fp8_down.  With ``workspace`` the _ws entry point is used."""
     N = X.shape[0]
     pX = _req(X, "X", torch.bfloat16, (N, HIDDEN))
     pr = _req(W_r, "W_r", torch.bfloat16, (EXPERTS, HIDDEN))
@@ -158,6 +158,47 @@ def forward_fp8(X, W_r, bias, gateup_fp8, down_fp8, out=None, workspace=None, st
     else:
         _lib.call("lfm_moe_forward_fp8_ws", pX, pr, pb, gc, gs, dc, ds, po, N, workspace.data_ptr(),
                   workspace.numel() * workspace.element_size(), _stream(stream))
+    return out
+
+
+def _routing(idx, w, N):
+    return (_req(idx, "idx", torch.int32, (N, TOP_K)), _req(w, "w", torch.float32, (N, TOP_K)))
+
+
+def experts(X, idx, w, W_gateup, W_down, out=None, workspace=None, stream=None):
+    """The expert path on caller-given routing (lfm_moe_experts_ws): idx
+    [N, 4] int32, w [N, 4] fp32.  Without ``workspace`` one is allocated."""
+    N = X.shape[0]
+    pX = _req(X, "X", torch.bfloat16, (N, HIDDEN))
+    pi, pw = _routing(idx, w, N)
+    pg = _req(W_gateup, "W_gateup (packed)", torch.bfloat16, (EXPERTS * 2 * FF * HIDDEN,))
+    pd = _req(W_down, "W_down (packed)", torch.bfloat16, (EXPERTS * HIDDEN * FF,))
+    if out is None:
+        out = torch.empty(N, HIDDEN, dtype=torch.float32, device=X.device)
+    po = _req(out, "out", torch.float32, (N, HIDDEN))
+    if workspace is None:
+        workspace = alloc_workspace(N, X.device)
+    _lib.call("lfm_moe_experts_ws", pX, pi, pw, pg, pd, po, N, workspace.data_ptr(),
+              workspace.numel() * workspace.element_size(), _stream(stream))
+    return out
+
+
+def experts_fp8(X, idx, w, gateup_fp8, down_fp8, out=None, workspace=None, stream=None):
+    """The FP8 expert path on caller-given routing (lfm_moe_experts_fp8_ws)."""
+    N = X.shape[0]
+    pX = _req(X, "X", torch.bfloat16, (N, HIDDEN))
+    pi, pw = _routing(idx, w, N)
+    gc = _req(gateup_fp8[0], "W_gateup_fp8", torch.uint8, (EXPERTS * 2 * FF * HIDDEN,))
+    gs = _req(gateup_fp8[1], "scales_gateup", torch.float32, FP8_GATEUP_SCALES)
+    dc = _req(down_fp8[0], "W_down_fp8", torch.uint8, (EXPERTS * HIDDEN * FF,))
+    ds = _req(down_fp8[1], "scales_down", torch.float32, FP8_DOWN_SCALES)
+    if out is None:
+        out = torch.empty(N, HIDDEN, dtype=torch.float32, device=X.device)
+    po = _req(out, "out", torch.float32, (N, HIDDEN))
+    if workspace is None:
+        workspace = alloc_workspace(N, X.device)
+    _lib.call("lfm_moe_experts_fp8_ws", pX, pi, pw, gc, gs, dc, ds, po, N, workspace.data_ptr(),
+              workspace.numel() * workspace.element_size(), _stream(stream))
     return out
 
 

@@ -75,21 +75,23 @@ bool overlap(Span a, Span b) {
 }
 
 // Checks shared by every layer entry point.  Returns OK, or the error.
+// With_router false (the expert path on caller-given routing): W_r and
+// bias are not used and not checked.
 lfm_moe_status check_layer_args(const void* x, size_t x_bytes, const uint16_t* W_r,
                                 const float* bias, const uint16_t* W_gateup,
                                 const uint16_t* W_down, const void* out, size_t out_bytes,
-                                int64_t N, bool out_is_input) {
+                                int64_t N, bool out_is_input, bool with_router = true) {
   if (N < 0) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "N must be >= 0");
   if (N > LFM_MOE_MAX_TOKENS) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "N exceeds LFM_MOE_MAX_TOKENS");
   if (N == 0) return LFM_MOE_OK;
-  if (!x || !W_r || !bias || !W_gateup || !W_down || !out)
+  if (!x || (with_router && (!W_r || !bias)) || !W_gateup || !W_down || !out)
     return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "null tensor pointer");
-  if (misaligned(x) || misaligned(W_r) || misaligned(bias) || misaligned(W_gateup) ||
+  if (misaligned(x) || (with_router && (misaligned(W_r) || misaligned(bias))) || misaligned(W_gateup) ||
       misaligned(W_down) || misaligned(out))
     return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
   const Span o{out, out_bytes};
-  const Span ins[] = {{W_r, sizeof(uint16_t) * kExperts * kHidden},
-                      {bias, sizeof(float) * kExperts},
+  const Span ins[] = {{W_r, with_router ? sizeof(uint16_t) * kExperts * kHidden : 0},
+                      {bias, with_router ? sizeof(float) * kExperts : 0},
                       {W_gateup, sizeof(uint16_t) * kExperts * 2 * kFF * kHidden},
                       {W_down, sizeof(uint16_t) * kExperts * kHidden * kFF}};
   for (const Span& s : ins)
@@ -107,6 +109,24 @@ lfm_moe_status check_ws(void* ws, size_t ws_bytes, int64_t N, Span out) {
                 "workspace of " + std::to_string(ws_bytes) + " bytes, need " +
                     std::to_string(workspace_bytes(N)));
   if (overlap(Span{ws, ws_bytes}, out)) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "workspace overlaps the output");
+  return LFM_MOE_OK;
+}
+
+// Checks of the caller-given routing of the expert-path entry points: the
+// selections and weights are read once (at the start of the call) and may
+// overlap each other, but neither the output nor the workspace.
+lfm_moe_status check_routing_args(const int32_t* idx, const float* w, int64_t N, Span out, void* ws,
+                                  size_t ws_bytes) {
+  if (!idx || !w) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if (misaligned(idx) || misaligned(w))
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  const size_t sel = static_cast<size_t>(N) * kTopK * 4;
+  const Span ins[] = {{idx, sel}, {w, sel}};
+  for (const Span& s : ins) {
+    if (overlap(out, s)) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "output overlaps the routing");
+    if (overlap(Span{ws, ws_bytes}, s))
+      return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "workspace overlaps the routing");
+  }
   return LFM_MOE_OK;
 }
 
@@ -232,8 +252,20 @@ bool use_decode_path(int64_t N) { return N <= kDecodeMaxTokens; }
 static_assert(kStreamMaxTokens == LFM_MOE_FP8_STREAM_TOKENS,
               "the FP8 layer streams exactly the batches the streaming kernels can group");
 
-// route -> [dispatch] -> gate/up -> down -> combine.  Arguments already checked.
+// The router's outputs in the workspace: from the router, or copied from
+// caller-given selections and weights (idx_in, w_in not null), with the
+// per-block histogram when the grouped path needs it.
+hipError_t route_or_ingest(const uint16_t* X, const uint16_t* W_r, const float* bias,
+                           const int32_t* idx_in, const float* w_in, int32_t* idx, float* w,
+                           int32_t* blockcounts, float* part, int n, hipStream_t stream) {
+  if (idx_in != nullptr) return launch_ingest_routing(idx_in, w_in, idx, w, blockcounts, n, stream);
+  return launch_route(X, W_r, bias, idx, w, blockcounts, part, n, stream);
+}
+
+// route -> [dispatch] -> gate/up -> down -> combine.  Arguments already
+// checked.  With idx_in and w_in the router is replaced by a copy of them.
 lfm_moe_status run_layer(const uint16_t* X, const uint16_t* W_r, const float* bias,
+                         const int32_t* idx_in, const float* w_in,
                          const uint16_t* W_gateup, const uint16_t* W_down, const float* resid,
                          float* out, int64_t N, void* ws, hipStream_t stream, StageTimer& timer) {
   int32_t* idx = region<int32_t>(ws, N, LFM_MOE_WS_IDX);
@@ -247,8 +279,9 @@ lfm_moe_status run_layer(const uint16_t* X, const uint16_t* W_r, const float* bi
   const int n = static_cast<int>(N);
   const bool decode = use_decode_path(N);
   hipError_t e;
-  if ((e = launch_route(X, W_r, bias, idx, w, decode ? nullptr : blockcounts, part, n, stream)) != hipSuccess)
-    return hip_fail(e, "route kernel launch");
+  if ((e = route_or_ingest(X, W_r, bias, idx_in, w_in, idx, w, decode ? nullptr : blockcounts, part, n,
+                           stream)) != hipSuccess)
+    return hip_fail(e, idx_in ? "routing copy kernel launch" : "route kernel launch");
   timer.after(1);
   if (decode) {
     if ((e = launch_gateup_decode(X, W_gateup, idx, H, n, stream)) != hipSuccess)
@@ -284,23 +317,24 @@ constexpr size_t kFp8DownBytes = static_cast<size_t>(kExperts) * kHidden * kFF;
 constexpr size_t kFp8GateupScaleBytes = sizeof(float) * kExperts * 2 * (kFF / 128) * (kHidden / 128);
 constexpr size_t kFp8DownScaleBytes = sizeof(float) * kExperts * (kHidden / 128) * (kFF / 128);
 
-// Checks of the FP8 layer entry points.
+// Checks of the FP8 layer entry points (with_router as for check_layer_args).
 lfm_moe_status check_fp8_args(const uint16_t* X, const uint16_t* W_r, const float* bias,
                               const uint8_t* W_gateup_fp8, const float* scales_gateup,
                               const uint8_t* W_down_fp8, const float* scales_down, const float* out,
-                              int64_t N) {
+                              int64_t N, bool with_router = true) {
   if (N < 0) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "N must be >= 0");
   if (N > LFM_MOE_FP8_MAX_TOKENS) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "N exceeds LFM_MOE_FP8_MAX_TOKENS");
   if (N == 0) return LFM_MOE_OK;
-  if (!X || !W_r || !bias || !W_gateup_fp8 || !scales_gateup || !W_down_fp8 || !scales_down || !out)
+  if (!X || (with_router && (!W_r || !bias)) || !W_gateup_fp8 || !scales_gateup || !W_down_fp8 ||
+      !scales_down || !out)
     return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "null tensor pointer");
-  if (misaligned(X) || misaligned(W_r) || misaligned(bias) || misaligned(W_gateup_fp8) ||
+  if (misaligned(X) || (with_router && (misaligned(W_r) || misaligned(bias))) || misaligned(W_gateup_fp8) ||
       misaligned(scales_gateup) || misaligned(W_down_fp8) || misaligned(scales_down) || misaligned(out))
     return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
   const Span o{out, act_bytes(N, 4)};
   const Span ins[] = {{X, act_bytes(N, 2)},
-                      {W_r, sizeof(uint16_t) * kExperts * kHidden},
-                      {bias, sizeof(float) * kExperts},
+                      {W_r, with_router ? sizeof(uint16_t) * kExperts * kHidden : 0},
+                      {bias, with_router ? sizeof(float) * kExperts : 0},
                       {W_gateup_fp8, kFp8GateupBytes},
                       {scales_gateup, kFp8GateupScaleBytes},
                       {W_down_fp8, kFp8DownBytes},
@@ -310,10 +344,11 @@ lfm_moe_status check_fp8_args(const uint16_t* X, const uint16_t* W_r, const floa
   return LFM_MOE_OK;
 }
 
-// The FP8 layer on checked arguments: route, FP8 gate/up and down (weight
-// streaming, each workgroup groups the slots itself), combine.
+// The FP8 layer on checked arguments: route (or the caller's routing),
+// FP8 gate/up and down (weight streaming, each workgroup groups the slots
+// itself, or the grouped kernels in FP8 mode), combine.
 lfm_moe_status run_fp8(const uint16_t* X, const uint16_t* W_r, const float* bias,
-                       const uint8_t* W_gateup_fp8, const float* scales_gateup,
+                       const int32_t* idx_in, const float* w_in, const uint8_t* W_gateup_fp8, const float* scales_gateup,
                        const uint8_t* W_down_fp8, const float* scales_down, float* out, int64_t N,
                        void* ws, hipStream_t stream) {
   StageTimer timer(stream);
@@ -326,9 +361,9 @@ lfm_moe_status run_fp8(const uint16_t* X, const uint16_t* W_r, const float* bias
   const bool streaming = N <= LFM_MOE_FP8_STREAM_TOKENS;
   int32_t* blockcounts = region<int32_t>(ws, N, LFM_MOE_WS_BLOCKCOUNTS);
   hipError_t e;
-  if ((e = launch_route(X, W_r, bias, idx, w, streaming ? nullptr : blockcounts, part, n, stream)) !=
-      hipSuccess)
-    return hip_fail(e, "route kernel launch");
+  if ((e = route_or_ingest(X, W_r, bias, idx_in, w_in, idx, w, streaming ? nullptr : blockcounts, part,
+                           n, stream)) != hipSuccess)
+    return hip_fail(e, idx_in ? "routing copy kernel launch" : "route kernel launch");
   timer.after(1);
   if (streaming) {
     if ((e = launch_gateup_decode_fp8(X, W_gateup_fp8, scales_gateup, idx, H, n, stream)) != hipSuccess)
@@ -469,8 +504,23 @@ lfm_moe_status lfm_moe_forward_fp8_ws(const uint16_t* X, const uint16_t* W_r, co
                                      scales_down, out, N);
   if (st != LFM_MOE_OK || N == 0) return st;
   if ((st = check_ws(ws, ws_bytes, N, Span{out, act_bytes(N, 4)})) != LFM_MOE_OK) return st;
-  return run_fp8(X, W_r, bias, W_gateup_fp8, scales_gateup, W_down_fp8, scales_down, out, N, ws,
-                 stream);
+  return run_fp8(X, W_r, bias, nullptr, nullptr, W_gateup_fp8, scales_gateup, W_down_fp8, scales_down,
+                 out, N, ws, stream);
+}
+
+lfm_moe_status lfm_moe_experts_fp8_ws(const uint16_t* X, const int32_t* idx, const float* w,
+                                      const uint8_t* W_gateup_fp8, const float* scales_gateup,
+                                      const uint8_t* W_down_fp8, const float* scales_down, float* out,
+                                      int64_t N, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  lfm_moe_status st = check_fp8_args(X, nullptr, nullptr, W_gateup_fp8, scales_gateup, W_down_fp8,
+                                     scales_down, out, N, false);
+  if (st != LFM_MOE_OK || N == 0) return st;
+  const Span o{out, act_bytes(N, 4)};
+  if ((st = check_ws(ws, ws_bytes, N, o)) != LFM_MOE_OK) return st;
+  if ((st = check_routing_args(idx, w, N, o, ws, ws_bytes)) != LFM_MOE_OK) return st;
+  return run_fp8(X, nullptr, nullptr, idx, w, W_gateup_fp8, scales_gateup, W_down_fp8, scales_down,
+                 out, N, ws, stream);
 }
 
 lfm_moe_status lfm_moe_forward_fp8(const uint16_t* X, const uint16_t* W_r, const float* bias,
@@ -484,8 +534,8 @@ lfm_moe_status lfm_moe_forward_fp8(const uint16_t* X, const uint16_t* W_r, const
   void* ws = nullptr;
   size_t bytes = 0;
   if ((st = internal_ws(N, &ws, &bytes)) != LFM_MOE_OK) return st;
-  return run_fp8(X, W_r, bias, W_gateup_fp8, scales_gateup, W_down_fp8, scales_down, out, N, ws,
-                 stream);
+  return run_fp8(X, W_r, bias, nullptr, nullptr, W_gateup_fp8, scales_gateup, W_down_fp8, scales_down,
+                 out, N, ws, stream);
 }
 
 lfm_moe_status lfm_moe_route(const uint16_t* X, const uint16_t* W_r, const float* bias,
@@ -517,7 +567,7 @@ lfm_moe_status lfm_moe_forward_ws(const uint16_t* X, const uint16_t* W_r, const 
   if (st != LFM_MOE_OK || N == 0) return st;
   if ((st = check_ws(ws, ws_bytes, N, Span{out, act_bytes(N, 4)})) != LFM_MOE_OK) return st;
   StageTimer timer(stream);
-  return run_layer(X, W_r, bias, W_gateup, W_down, nullptr, out, N, ws, stream, timer);
+  return run_layer(X, W_r, bias, nullptr, nullptr, W_gateup, W_down, nullptr, out, N, ws, stream, timer);
 }
 
 lfm_moe_status lfm_moe_forward(const uint16_t* X, const uint16_t* W_r, const float* bias,
@@ -531,7 +581,21 @@ lfm_moe_status lfm_moe_forward(const uint16_t* X, const uint16_t* W_r, const flo
   size_t bytes = 0;
   if ((st = internal_ws(N, &ws, &bytes)) != LFM_MOE_OK) return st;
   StageTimer timer(stream);
-  return run_layer(X, W_r, bias, W_gateup, W_down, nullptr, out, N, ws, stream, timer);
+  return run_layer(X, W_r, bias, nullptr, nullptr, W_gateup, W_down, nullptr, out, N, ws, stream, timer);
+}
+
+lfm_moe_status lfm_moe_experts_ws(const uint16_t* X, const int32_t* idx, const float* w,
+                                  const uint16_t* W_gateup, const uint16_t* W_down, float* out,
+                                  int64_t N, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  lfm_moe_status st = check_layer_args(X, act_bytes(N, 2), nullptr, nullptr, W_gateup, W_down, out,
+                                       act_bytes(N, 4), N, false, false);
+  if (st != LFM_MOE_OK || N == 0) return st;
+  const Span o{out, act_bytes(N, 4)};
+  if ((st = check_ws(ws, ws_bytes, N, o)) != LFM_MOE_OK) return st;
+  if ((st = check_routing_args(idx, w, N, o, ws, ws_bytes)) != LFM_MOE_OK) return st;
+  StageTimer timer(stream);
+  return run_layer(X, nullptr, nullptr, idx, w, W_gateup, W_down, nullptr, out, N, ws, stream, timer);
 }
 
 lfm_moe_status lfm_moe_block_forward_ws(float* x_inout, const uint16_t* W_r, const float* bias,
@@ -547,7 +611,7 @@ lfm_moe_status lfm_moe_block_forward_ws(float* x_inout, const uint16_t* W_r, con
   hipError_t e = launch_rmsnorm(x_inout, X, N, stream);
   if (e != hipSuccess) return hip_fail(e, "rmsnorm kernel launch");
   timer.after(0);
-  return run_layer(X, W_r, bias, W_gateup, W_down, x_inout, x_inout, N, ws, stream, timer);
+  return run_layer(X, W_r, bias, nullptr, nullptr, W_gateup, W_down, x_inout, x_inout, N, ws, stream, timer);
 }
 
 lfm_moe_status lfm_moe_block_forward(float* x_inout, const uint16_t* W_r, const float* bias,

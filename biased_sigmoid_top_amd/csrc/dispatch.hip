@@ -119,7 +119,62 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(
   }
 }
 
+// Caller-given routing (the expert path without the router): copies the
+// selections and weights of 16 tokens per wavefront into the workspace and
+// writes the same per-16-token histogram the router writes.  The
+// selections become memory-safe on the way: an id is taken modulo 64, and
+// an id that repeats an earlier one of the same token is replaced by the
+// lowest id that is neither among the token's earlier (final) ids nor
+// among its later given ones, so every token ends with four distinct ids
+// in [0, 64) and valid input passes through unchanged.  Lane i holds entry
+// i % 4 of token 16 * block + i / 4.
+__global__ __launch_bounds__(kWave) void ingest_routing_kernel(
+    const int32_t* __restrict__ idx_in, const float* __restrict__ w_in, int32_t* __restrict__ idx,
+    float* __restrict__ w, int32_t* __restrict__ blockcounts, int route_tokens, int N) {
+  __shared__ int counts[kExperts];
+  const int lane = threadIdx.x;
+  const int j = lane % kTopK;
+  const int t = blockIdx.x * route_tokens + lane / kTopK;
+  const bool live = lane / kTopK < route_tokens && t < N;
+  const size_t at = static_cast<size_t>(t) * kTopK + j;
+  const int given = live ? (idx_in[at] & (kExperts - 1)) : 0;
+  // The four given ids of this lane's token, from the lanes of its quad.
+  int v[kTopK];
+#pragma unroll
+  for (int q = 0; q < kTopK; ++q) v[q] = __shfl(given, (lane & ~(kTopK - 1)) + q, kWave);
+#pragma unroll
+  for (int q = 1; q < kTopK; ++q) {
+    bool repeat = false;
+    for (int p = 0; p < q; ++p) repeat = repeat || v[p] == v[q];
+    if (!repeat) continue;
+    for (int e = 0; e < kExperts; ++e) {  // at most 6 ids are excluded
+      bool used = false;
+      for (int p = 0; p < kTopK; ++p) used = used || (p != q && v[p] == e);
+      if (!used) { v[q] = e; break; }
+    }
+  }
+  counts[lane] = 0;
+  __syncthreads();
+  if (live) {
+    idx[at] = v[j];
+    w[at] = w_in[at];
+    atomicAdd(&counts[v[j]], 1);
+  }
+  __syncthreads();
+  if (blockcounts != nullptr) blockcounts[static_cast<size_t>(blockIdx.x) * kExperts + lane] = counts[lane];
+}
+
 }  // namespace
+
+hipError_t launch_ingest_routing(const int32_t* idx_in, const float* w_in, int32_t* idx, float* w,
+                                 int32_t* blockcounts, int N, hipStream_t stream) {
+  const int rt = route_block_tokens(N);
+  if (rt != kWave / kTopK) return hipErrorInvalidValue;  // one wavefront holds a block's entries
+  const int grid = (N + rt - 1) / rt;
+  hipLaunchKernelGGL(ingest_routing_kernel, dim3(grid), dim3(kWave), 0, stream, idx_in, w_in, idx,
+                     w, blockcounts, rt, N);
+  return hipGetLastError();
+}
 
 hipError_t launch_dispatch(const int32_t* idx, const int32_t* blockcounts, int32_t* offsets,
                            int32_t* row2slot, int N, hipStream_t stream) {

@@ -30,6 +30,10 @@ size_t route_partial_bytes(int64_t N);
 hipError_t launch_route(const uint16_t* X, const uint16_t* Wr, const float* bias, int32_t* idx,
                         float* w, int32_t* blockcounts, float* part, int N, hipStream_t stream);
 
+// Caller-given selections and weights -> workspace copies (ids made
+// memory-safe) and the per-block histogram (when blockcounts is not null).
+hipError_t launch_ingest_routing(const int32_t* idx_in, const float* w_in, int32_t* idx, float* w,
+                                 int32_t* blockcounts, int N, hipStream_t stream);
 hipError_t launch_dispatch(const int32_t* idx, const int32_t* blockcounts, int32_t* offsets,
                            int32_t* row2slot, int N, hipStream_t stream);
 

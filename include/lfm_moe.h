@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define LFM_MOE_ABI_VERSION 3
+#define LFM_MOE_ABI_VERSION 4
 #define LFM_MOE_HIDDEN 2048
 #define LFM_MOE_EXPERTS 64
 #define LFM_MOE_TOPK 4
@@ -185,6 +185,31 @@ lfm_moe_status lfm_moe_forward_ws(const uint16_t* X, const uint16_t* W_r, const 
                                   hipStream_t stream);
 
 /*
+ * The expert path alone, on routing the caller supplies (steps after the
+ * router: grouping by expert, the gated SiLU experts and the weighted
+ * combine of the guide's sections "The router has two different scores"
+ * and "What to verify in a deployment"):
+ *   out[t] = sum_j w[t, j] * y_{idx[t, j]}(X[t]),  j = 0..3 in that order.
+ *   X:   [N, 2048] bf16 (read)
+ *   idx: [N, 4] int32 expert ids, w: [N, 4] fp32 mixture weights (read once,
+ *        copied into the IDX and W workspace regions; they may overlap each
+ *        other but neither out nor the workspace)
+ *   W_gateup, W_down, out, ws, ws_bytes, stream: as for lfm_moe_forward_ws.
+ * Ids are taken modulo 64, and an id that repeats an earlier id of the
+ * same token is replaced by the lowest id that is neither among the
+ * token's earlier ids (as replaced) nor among its later given ones; the
+ * IDX region shows the ids used.  Valid routing (four distinct ids in
+ * [0, 64) per token) is used as given, and then the result equals that of
+ * lfm_moe_forward_ws for a router that selected idx and w, bit for bit.
+ * For tests that hold the routing fixed (the oracle's) and for callers that
+ * route elsewhere.  0 <= N <= LFM_MOE_MAX_TOKENS; N == 0 is a no-op.
+ */
+lfm_moe_status lfm_moe_experts_ws(const uint16_t* X, const int32_t* idx, const float* w,
+                                  const uint16_t* W_gateup, const uint16_t* W_down,
+                                  float* out, int64_t N, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
+/*
  * One block's feed-forward half (guide, section "The exact checkpoint":
  * normalise, feed-forward network, residual):
  *   x_inout[t] <- x_inout[t] + MoE(bf16(RMSNorm(x_inout[t])))
@@ -238,8 +263,13 @@ lfm_moe_status lfm_moe_block_forward_ws(float* x_inout, const uint16_t* W_r, con
  *   lfm_moe_forward.
  * lfm_moe_forward_fp8_ws: the same with a caller workspace, as
  *   lfm_moe_forward_ws (same size and regions: the routing, the bf16 hidden
- *   rows H and the fp32 expert rows Y, both in slot order t * 4 + j; the
- *   regions of the grouped path are not written).
+ *   rows H and the fp32 expert rows Y, both in slot order t * 4 + j; up to
+ *   LFM_MOE_FP8_STREAM_TOKENS tokens the regions of the grouped path are not
+ *   written).
+ * lfm_moe_experts_fp8_ws: the FP8 expert path on caller-given routing
+ *   idx [N, 4] int32 and w [N, 4] fp32, with the same rules as
+ *   lfm_moe_experts_ws; on valid routing bit-identical to
+ *   lfm_moe_forward_fp8_ws for a router that selected idx and w.
  * Pointers 16-byte aligned; outputs must not overlap inputs; asynchronous on
  * `stream`.
  */
@@ -253,6 +283,10 @@ lfm_moe_status lfm_moe_forward_fp8(const uint16_t* X, const uint16_t* W_r, const
                                    const uint8_t* W_down_fp8, const float* scales_down, float* out,
                                    int64_t N, hipStream_t stream);
 lfm_moe_status lfm_moe_forward_fp8_ws(const uint16_t* X, const uint16_t* W_r, const float* bias,
+                                      const uint8_t* W_gateup_fp8, const float* scales_gateup,
+                                      const uint8_t* W_down_fp8, const float* scales_down, float* out,
+                                      int64_t N, void* ws, size_t ws_bytes, hipStream_t stream);
+lfm_moe_status lfm_moe_experts_fp8_ws(const uint16_t* X, const int32_t* idx, const float* w,
                                       const uint8_t* W_gateup_fp8, const float* scales_gateup,
                                       const uint8_t* W_down_fp8, const float* scales_down, float* out,
                                       int64_t N, void* ws, size_t ws_bytes, hipStream_t stream);

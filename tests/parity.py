@@ -117,6 +117,20 @@ def check_grouping_valid(idx: np.ndarray, offsets: np.ndarray, row2slot: np.ndar
         assert np.all(np.diff(r2s[a:b] // 4) > 0), f"expert {e} rows not in token order"
 
 
+def sanitize_routing(idx: np.ndarray) -> np.ndarray:
+    """Host mirror of the rule the expert-path entry points apply to given
+    selections: ids modulo 64; an id that repeats an earlier (final) id of
+    its token becomes the lowest id that is neither among the token's other
+    ids -- earlier ones as replaced, later ones as given."""
+    v = (np.asarray(idx, dtype=np.int64) & 63).astype(np.int32)
+    for row in v:
+        for q in range(1, 4):
+            if row[q] in row[:q]:
+                others = {int(row[p]) for p in range(4) if p != q}
+                row[q] = min(e for e in range(64) if e not in others)
+    return v
+
+
 def oracle_fp8_experts(inp: dict, workers: int = 8) -> dict:
     """oracle.fp8.quantize_experts of a workload's expert weights, one
     (matrix, expert) block quantisation per task on a thread pool (numpy

@@ -4,6 +4,8 @@ rejects bad arguments before any HIP call (so these run without a GPU)."""
 import ctypes
 import re
 
+import numpy as np
+
 import pytest
 
 from biased_sigmoid_top_amd import _lib
@@ -156,6 +158,67 @@ def test_fp8_argument_checks(lib):
     assert g(a[0], a[1], a[2], a[2] + 256, None) == _lib.ERR_INVALID_ARGUMENT   # scales over codes
     assert d(a[0], a[1], a[1] + 4, None) == _lib.ERR_INVALID_ARGUMENT
     assert d(a[0], a[0] + 64, a[2], None) == _lib.ERR_INVALID_ARGUMENT
+
+
+def test_experts_argument_checks(lib):
+    # X, idx, w, W_gateup, W_down, out
+    a = [_addr(i) for i in range(6)]
+    N = 100
+    need = lib.lfm_moe_workspace_bytes(N)
+    ws = _addr(7)
+    f = lib.lfm_moe_experts_ws
+    assert f(*a, 0, None, 0, None) == _lib.OK                              # N == 0: nothing launched
+    assert f(*a, -1, ws, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert f(*a, (1 << 24) + 1, ws, 1 << 50, None) == _lib.ERR_INVALID_ARGUMENT
+    for i in range(6):
+        b = list(a)
+        b[i] = None
+        assert f(*b, N, ws, need, None) == _lib.ERR_INVALID_ARGUMENT
+        assert b"null" in lib.lfm_moe_last_error()
+        b = list(a)
+        b[i] = a[i] + 4
+        assert f(*b, N, ws, need, None) == _lib.ERR_INVALID_ARGUMENT
+        assert b"aligned" in lib.lfm_moe_last_error()
+    assert f(*a, N, ws, need - 1, None) == _lib.ERR_WORKSPACE_TOO_SMALL
+    assert f(*a, N, None, need, None) == _lib.ERR_INVALID_ARGUMENT
+    b = list(a)
+    b[5] = a[1] + 256                                                      # out over the selections
+    assert f(*b, N, ws, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert b"routing" in lib.lfm_moe_last_error()
+    b = list(a)
+    b[2] = ws + 1024                                                       # weights inside the workspace
+    assert f(*b, N, ws, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert b"workspace overlaps the routing" in lib.lfm_moe_last_error()
+    # FP8: X, idx, w, codes_gu, scales_gu, codes_d, scales_d, out
+    a8 = [_addr(i) for i in range(8)]
+    g = lib.lfm_moe_experts_fp8_ws
+    assert g(*a8, 0, None, 0, None) == _lib.OK
+    for i in range(8):
+        b = list(a8)
+        b[i] = None
+        assert g(*b, N, ws, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert g(*a8, N, ws, need - 1, None) == _lib.ERR_WORKSPACE_TOO_SMALL
+    b = list(a8)
+    b[1] = ws                                                              # selections are the workspace
+    assert g(*b, N, ws, need, None) == _lib.ERR_INVALID_ARGUMENT
+
+
+def test_routing_replacement_rule():
+    """The rule include/lfm_moe.h states for given selections, on its host
+    mirror: ids modulo 64, repeats replaced by the lowest id not among the
+    token's other ids, valid rows unchanged."""
+    from parity import sanitize_routing
+    got = sanitize_routing(np.array([[5, 5, 5, 5], [-1, 63, 3, 3], [0, 64, 128, 1],
+                                     [7, 9, 11, 13], [2, 2, 0, 1]], dtype=np.int32))
+    np.testing.assert_array_equal(got, [[5, 0, 1, 2], [63, 0, 3, 1], [0, 2, 3, 1],
+                                        [7, 9, 11, 13], [2, 3, 0, 1]])
+    rng = np.random.default_rng(0)
+    raw = rng.integers(-300, 300, size=(5000, 4)).astype(np.int32)
+    out = sanitize_routing(raw)
+    assert np.all((out >= 0) & (out < 64))
+    assert all(len(set(r)) == 4 for r in out.tolist())
+    valid = np.array([rng.choice(64, 4, replace=False) for _ in range(500)], dtype=np.int32)
+    np.testing.assert_array_equal(sanitize_routing(valid), valid)
 
 
 def test_timing_read_checks_its_arguments(lib):
