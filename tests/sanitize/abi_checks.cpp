@@ -90,6 +90,21 @@ int main() {
          LFM_MOE_ERR_INVALID_ARGUMENT);
   EXPECT(lfm_moe_forward_fp8_ws(X, Wr, b, q8, s8, d8, t8, out, N, ws, need - 16, nullptr) ==
          LFM_MOE_ERR_WORKSPACE_TOO_SMALL);
+
+  // Expert path on given routing: nulls, workspace, routing overlapping out or the workspace.
+  const auto ri = fake<const int32_t>(16);
+  const auto rw = fake<const float>(17);
+  EXPECT(lfm_moe_experts_ws(X, ri, rw, Wgu, Wd, out, 0, nullptr, 0, nullptr) == LFM_MOE_OK);
+  EXPECT(lfm_moe_experts_ws(X, nullptr, rw, Wgu, Wd, out, N, ws, need, nullptr) == LFM_MOE_ERR_INVALID_ARGUMENT);
+  EXPECT(lfm_moe_experts_ws(X, ri, rw, Wgu, Wd, out, N, ws, need - 1, nullptr) == LFM_MOE_ERR_WORKSPACE_TOO_SMALL);
+  EXPECT(lfm_moe_experts_ws(X, ri, fake<const float>(6, 512), Wgu, Wd, out, N, ws, need, nullptr) ==
+         LFM_MOE_ERR_INVALID_ARGUMENT && has_message());
+  EXPECT(lfm_moe_experts_ws(X, ri, rw, Wgu, Wd, fake<float>(16, 0), N, ws, need, nullptr) ==
+         LFM_MOE_ERR_INVALID_ARGUMENT);
+  EXPECT(lfm_moe_experts_fp8_ws(X, ri, rw, q8, s8, d8, nullptr, out, N, ws, need, nullptr) ==
+         LFM_MOE_ERR_INVALID_ARGUMENT);
+  EXPECT(lfm_moe_experts_fp8_ws(X, ri, rw, q8, s8, d8, t8, out, LFM_MOE_FP8_MAX_TOKENS + 1, ws, need, nullptr) ==
+         LFM_MOE_ERR_INVALID_ARGUMENT);
   EXPECT(lfm_moe_pack_fp8_gateup(Wgu, Wgu, fake<uint8_t>(3, 512), fake<float>(15), nullptr) ==
          LFM_MOE_ERR_INVALID_ARGUMENT);
   EXPECT(lfm_moe_pack_fp8_down(Wd, fake<uint8_t>(16), nullptr, nullptr) == LFM_MOE_ERR_INVALID_ARGUMENT);
