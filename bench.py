@@ -402,6 +402,39 @@ def vendor_gemm(steps=20, warmup=5):
         a2, b2 = a.reshape(E * 256, k), b[0].contiguous()
         us = timed(lambda: torch.matmul(a2, b2))
         out[f"{name}_dense_16384"] = {"us": round(us, 1), "tflops": round(flop / us / 1e6, 1)}
+        del a, b, a2, b2
+
+    # This library's expert kernels on the same uniform shape: 4,096 tokens
+    # routed so that every expert gets exactly 256 slots (token t takes
+    # experts 4t .. 4t + 3 modulo 64), through lfm_moe_experts_ws, per-kernel
+    # times from the library's stage events.
+    import biased_sigmoid_top_amd as moe
+    N = 4096
+    Wg = (0.02 * torch.randn(E, FF, D, device="cuda", generator=g)).to(torch.bfloat16)
+    Wu = (0.02 * torch.randn(E, FF, D, device="cuda", generator=g)).to(torch.bfloat16)
+    Wd = (0.02 * torch.randn(E, D, FF, device="cuda", generator=g)).to(torch.bfloat16)
+    Wgu, Wdp = moe.pack_gateup(Wg, Wu), moe.pack_down(Wd)
+    del Wg, Wu, Wd
+    X = torch.randn(N, D, device="cuda", generator=g).to(torch.bfloat16)
+    t = torch.arange(N, device="cuda", dtype=torch.int32)
+    idx = ((4 * t[:, None] + torch.arange(4, device="cuda", dtype=torch.int32)) % E).contiguous()
+    w = torch.full((N, 4), 0.25, device="cuda")
+    res = torch.empty(N, D, device="cuda")
+    ws = moe.alloc_workspace(N)
+    for _ in range(warmup):
+        moe.experts(X, idx, w, Wgu, Wdp, out=res, workspace=ws)
+    torch.cuda.synchronize()
+    moe.timing_enable(True)
+    for _ in range(steps):
+        moe.experts(X, idx, w, Wgu, Wdp, out=res, workspace=ws)
+    torch.cuda.synchronize()
+    st = moe.timing_read()
+    moe.timing_enable(False)
+    for name, n_out, k in (("gateup", 2 * FF, D), ("down", D, FF)):
+        ms, n = st[name]
+        us = ms / max(n, 1) * 1e3
+        flop = 2 * E * 256 * n_out * k
+        out[f"{name}_ours_uniform_64x256"] = {"us": round(us, 1), "tflops": round(flop / us / 1e6, 1)}
     print(json.dumps({"vendor_gemm": out, "steps": steps, "dtype": "bf16"}))
 
 
