@@ -12,7 +12,8 @@
 // Tile: 128 grouped rows (tokens of one expert) x 64 weight rows per
 // wavefront, 32x32x16 bf16 MFMAs (on gfx950 twice the rate of the 16x16x32
 // form).  Gate/up runs 8 wavefronts per workgroup (512 weight rows), one
-// workgroup per CU; down runs 4 (256 rows), two per CU.  Each wavefront
+// workgroup per CU; down runs 4 (256 rows), two per CU, or 8 (256 or 512
+// rows) depending on the batch size (see the shape selection).  Each wavefront
 // owns 64 weight rows (two packed row blocks) for all 128 tokens: 4 x 2
 // accumulator tiles.  Because no two wavefronts share weight rows, the
 // weights need no LDS: every wavefront streams its own packed fragments
@@ -64,10 +65,11 @@ constexpr int kXcds = 8;
 // and the MFMA operand reads (32 rows of one K half) free of bank conflicts.
 __device__ __forceinline__ int swz(int c) { return c + 8 * (c & 1); }
 
-// Gate/up: 8 wavefronts (128 x 512 tiles), one workgroup per CU.  Down:
-// 4 wavefronts (128 x 256), two per CU -- its 8 column tiles then deal
-// evenly over the CUs where 4 wide ones would leave a half-empty last round
-// (N = 4096: down 159 us against 164; gate/up 256 against 267 with 4).
+// Gate/up: 8 wavefronts (128 x 512 tiles), one workgroup per CU.  Down
+// from 2049 to 6144 tokens: 4 wavefronts (128 x 256), two per CU -- its 8
+// column tiles then deal evenly over the CUs where 4 wide ones would leave a
+// half-empty last round (N = 4096: down 159 us against 164; gate/up 256
+// against 267 with 4); the other batch sizes take other shapes (below).
 template <bool GATEUP, int FB_, int WAVES_ = (GATEUP ? 8 : 4), int TB_ = 4>
 struct TileShape {
   static constexpr int FB = FB_;  // packed 32-row blocks per wavefront
@@ -371,20 +373,32 @@ int64_t tiled_grid(int64_t N) {
 // tiles runs on a fraction of the CUs; narrower tiles make that tail
 // shorter.  Gate/up: 512 weight rows (8 wavefronts x two blocks) by
 // default, 128 rows (4 wavefronts x one block, two workgroups per CU) for
-// 193-512 tokens, 256 rows (8 x one) for 513-2048.  Down: 256 rows (4 x two)
-// by default, 128 rows (4 x one) up to 512 tokens.  Measured (layer of seed
+// 193-512 tokens, 256 rows (8 x one) for 513-2048.  Down: 128 rows (4 x
+// one) up to 512 tokens, 256 rows (8 x one) for 513-2048, 256 rows (4 x
+// two) for 2049-6144, 512 rows (8 x two) above.  Measured (layer of seed
 // 4, first N tokens; gate/up 512 / 128 / 256 rows, us): N = 160: 92 / 97 /
 // -; 256: 132 / 112 / -; 320: - / 112 / 117; 512: - / 119 / 121; 640: - /
 // 130 / 126; 1024: - / 140 / 133; earlier, 4096: 245 / - / 261.  Down 256 /
 // 128 rows: N = 128: 61 / 52; 320: 71 / 61; 512: 77 / 69; 640: 74 / 75;
-// 2048: 104 / 108.
+// 2048: 104 / 108.  Down by N (us, same box, mean of two runs for the
+// 256-row form; 256 rows as 4 x two / 256 rows as 8 x one / 512 rows as 8 x
+// two): N = 1024: 83.1 / 78.6 / 83.8; 2048: 112.3 / 104.5 / 115.8; 4096:
+// 157.3 / 160.3 / 165.7; 6144: 210.6 / 217.6 / 209.9; 8192: 277.6 / 299.0 /
+// 264.8; 16384: 497.2 / 541.0 / 470.8.  With eight wavefronts a workgroup
+// has a CU to itself and its token tile feeds twice the weight rows.
 enum class GateupTiles { kWide, kNarrow4, kNarrow8 };
 GateupTiles gateup_tiles(int64_t N) {
   if (N > 192 && N <= 512) return GateupTiles::kNarrow4;
   if (N > 512 && N <= 2048) return GateupTiles::kNarrow8;
   return GateupTiles::kWide;
 }
-bool narrow_down_tiles(int64_t N) { return N <= 512; }
+enum class DownTiles { kNarrow4, kNarrow8, kMid, kWide8 };
+DownTiles down_tiles(int64_t N) {
+  if (N <= 512) return DownTiles::kNarrow4;
+  if (N <= 2048) return DownTiles::kNarrow8;
+  if (N <= 6144) return DownTiles::kMid;
+  return DownTiles::kWide8;
+}
 
 template <bool GATEUP, int FB, int WAVES = (GATEUP ? 8 : 4), int TB = 4, bool FP8 = false,
           typename Out>
@@ -418,8 +432,16 @@ hipError_t launch_gateup_tiled(const uint16_t* X, const uint16_t* Wgu, const int
 
 hipError_t launch_down_tiled(const uint16_t* H, const uint16_t* Wd, const int32_t* offsets,
                              const int32_t* row2slot, float* Y, int64_t N, hipStream_t stream) {
-  return narrow_down_tiles(N) ? launch_tiled<false, 1, 4>(H, Wd, offsets, row2slot, Y, N, stream)
-                              : launch_tiled<false, 2>(H, Wd, offsets, row2slot, Y, N, stream);
+  switch (down_tiles(N)) {
+    case DownTiles::kNarrow4:
+      return launch_tiled<false, 1, 4>(H, Wd, offsets, row2slot, Y, N, stream);
+    case DownTiles::kNarrow8:
+      return launch_tiled<false, 1, 8>(H, Wd, offsets, row2slot, Y, N, stream);
+    case DownTiles::kWide8:
+      return launch_tiled<false, 2, 8>(H, Wd, offsets, row2slot, Y, N, stream);
+    default:
+      return launch_tiled<false, 2>(H, Wd, offsets, row2slot, Y, N, stream);
+  }
 }
 
 hipError_t launch_gateup_tiled_fp8(const uint16_t* Xq, const uint8_t* Wq, const float* Ws,

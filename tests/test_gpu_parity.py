@@ -300,10 +300,10 @@ def test_verification_batches(moe, c):
     check_out(_np(out), expected_outputs(inp, r, np.arange(N), alt))
 
 
-@pytest.mark.parametrize("N", [17, 300, 4096])
+@pytest.mark.parametrize("N", [17, 300, 1000, 4096, 6145])
 def test_writes_stay_in_bounds(moe, N):
     """Canaries after the output rows and after the workspace's documented
-    size are left untouched (decode path, narrow and wide grouped tiles)."""
+    size are left untouched (decode path and every grouped tile shape)."""
     inp, dev = _layer_case(N, 700 + N)
     _step(f"canaries N={N}")
     out_all = torch.full((N + 8, 2048), 12345.0, dtype=torch.float32, device="cuda")
