@@ -346,6 +346,11 @@ def device_info():
     p = torch.cuda.get_device_properties(0)
     info = dict(name=p.name, arch=getattr(p, "gcnArchName", None), cus=p.multi_processor_count,
                 memory_gib=round(p.total_memory / 2**30, 1), smi=None)
+    # Under rocprofv3 a child process inherits the profiler's preloaded
+    # library, which opens the GPU before rocm-smi's interpreter starts; skip
+    # the query there (the profile does not need it).
+    if any(k.startswith("ROCPROF") for k in os.environ):
+        return info
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showtemp", "--json"],
                            capture_output=True, text=True, timeout=20)
