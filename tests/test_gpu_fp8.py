@@ -176,6 +176,41 @@ def test_fp8_forward_parity_decode_n64(moe):
     _check_fp8_forward(moe, inp, dev, q, inp["X"].shape[0])
 
 
+def test_fp8_forward_skewed_sampled(moe):
+    """The FP8 layer at the largest configuration (16,384 tokens, skewed bias:
+    most slots on experts 0-7, which then run up to ~100 m-tiles each on the
+    grouped kernels in FP8 mode), on sampled tokens: the GPU's selections
+    checked against the oracle's (near ties accepted as for the bf16 layer),
+    the output against oracle.fp8 on those tokens and selections."""
+    from biased_sigmoid_top_amd import _lib
+    from oracle import fp8
+    w_ = synth.WORKLOADS["skewed_n16384"]
+    layer = cached_layer(w_["N"], w_["seed"], w_["skew"])
+    inp = oracle_inputs(layer)
+    N = inp["X"].shape[0]
+    print("[fp8] oracle block quantisation of the skewed workload's experts", flush=True)
+    q = oracle_fp8_experts(inp)
+    r = oracle.route(inp["X"], inp["W_r"], inp["bias"])
+    _step("pack_fp8_gateup / pack_fp8_down (skewed workload)")
+    gq = moe.pack_fp8_gateup(layer["W_gate"].cuda(), layer["W_up"].cuda())
+    dq = moe.pack_fp8_down(layer["W_down"].cuda())
+    X = torch.from_numpy(inp["X"]).to(torch.bfloat16).cuda()
+    ws = moe.alloc_workspace(N)
+    _step(f"forward_fp8 skewed_n16384 N={N}")
+    out = _np(moe.forward_fp8(X, layer["W_r"].cuda(), layer["bias"].cuda(), gq, dq, workspace=ws))
+    idx = _np(moe.workspace_view(ws, N, _lib.WS_IDX, torch.int32, (N, 4)))
+    w = _np(moe.workspace_view(ws, N, _lib.WS_W, torch.float32, (N, 4))).astype(np.float64)
+    assert np.all(np.isfinite(out))
+    rng = np.random.default_rng(1)
+    near = np.nonzero(r.margin <= 1e-4)[0]
+    tokens = np.unique(np.concatenate([rng.choice(N, 384, replace=False), near, [0, 1, N - 2, N - 1]]))
+    check_route(idx, w, r, tokens=tokens)
+    expect = fp8.moe_apply_fp8(inp["X"][tokens], idx[tokens], w[tokens], q).out
+    ratio = float(np.max(np.abs(out[tokens] - expect))) / float(np.sqrt(np.mean(expect ** 2)))
+    print(f"  sampled {len(tokens)} tokens, max|err| / RMS = {ratio:.4f}", flush=True)
+    assert ratio <= OUT_GATE_FP8, ratio
+
+
 @pytest.mark.parametrize("N", [1, 17, 33, 95, 96, 97, 160, 255, 256, 257, 700, 2049, 4096])
 def test_fp8_forward_ragged(moe, N):
     """Streaming kernels up to 256 tokens, grouped kernels in FP8 mode above."""
