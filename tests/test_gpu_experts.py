@@ -71,8 +71,9 @@ def _experts(moe, dev, fp8, X, idx, w, ws):
 
 
 @pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
-@pytest.mark.parametrize("N", [64, 700])
+@pytest.mark.parametrize("N", [64, 700, 5000])
 def test_experts_equal_the_layer_on_its_own_routing(moe, N, fp8):
+    """N = 5000 ends in a partial 16-token histogram block."""
     from biased_sigmoid_top_amd import _lib
     inp, dev = _case(moe)
     _, X = _x(N, 2100 + N)
