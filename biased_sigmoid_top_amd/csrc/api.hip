@@ -1,5 +1,6 @@
 // C ABI of the MoE layer: argument checks, workspace layout and the launch
 // sequence route -> dispatch -> gate/up -> down -> combine on one stream.
+#include <initializer_list>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -101,16 +102,29 @@ lfm_moe_status check_layer_args(const void* x, size_t x_bytes, const uint16_t* W
   return LFM_MOE_OK;
 }
 
-lfm_moe_status check_ws(void* ws, size_t ws_bytes, int64_t N, Span out) {
+// The caller workspace: present, aligned, large enough, and apart from the
+// output and from every input tensor (its regions are written while the
+// inputs are still being read).
+lfm_moe_status check_ws(void* ws, size_t ws_bytes, int64_t N, Span out,
+                        std::initializer_list<Span> inputs) {
   if (!ws) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "null workspace");
   if (misaligned(ws, kAlign)) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
   if (ws_bytes < workspace_bytes(N))
     return fail(LFM_MOE_ERR_WORKSPACE_TOO_SMALL,
                 "workspace of " + std::to_string(ws_bytes) + " bytes, need " +
                     std::to_string(workspace_bytes(N)));
-  if (overlap(Span{ws, ws_bytes}, out)) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "workspace overlaps the output");
+  const Span w{ws, ws_bytes};
+  if (overlap(w, out)) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "workspace overlaps the output");
+  for (const Span& s : inputs)
+    if (overlap(w, s)) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "workspace overlaps an input");
   return LFM_MOE_OK;
 }
+
+// Spans of the bf16 layer's weights and of the FP8 experts.
+Span gateup_span(const void* p) { return {p, sizeof(uint16_t) * kExperts * 2 * kFF * kHidden}; }
+Span down_span(const void* p) { return {p, sizeof(uint16_t) * kExperts * kHidden * kFF}; }
+Span router_span(const void* p) { return {p, p ? sizeof(uint16_t) * kExperts * kHidden : 0}; }
+Span bias_span(const void* p) { return {p, p ? sizeof(float) * kExperts : 0}; }
 
 // Checks of the caller-given routing of the expert-path entry points: the
 // selections and weights are read once (at the start of the call) and may
@@ -503,7 +517,11 @@ lfm_moe_status lfm_moe_forward_fp8_ws(const uint16_t* X, const uint16_t* W_r, co
   lfm_moe_status st = check_fp8_args(X, W_r, bias, W_gateup_fp8, scales_gateup, W_down_fp8,
                                      scales_down, out, N);
   if (st != LFM_MOE_OK || N == 0) return st;
-  if ((st = check_ws(ws, ws_bytes, N, Span{out, act_bytes(N, 4)})) != LFM_MOE_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, N, Span{out, act_bytes(N, 4)},
+                     {{X, act_bytes(N, 2)}, router_span(W_r), bias_span(bias), {W_gateup_fp8, kFp8GateupBytes},
+                      {scales_gateup, kFp8GateupScaleBytes}, {W_down_fp8, kFp8DownBytes},
+                      {scales_down, kFp8DownScaleBytes}})) != LFM_MOE_OK)
+    return st;
   return run_fp8(X, W_r, bias, nullptr, nullptr, W_gateup_fp8, scales_gateup, W_down_fp8, scales_down,
                  out, N, ws, stream);
 }
@@ -517,7 +535,10 @@ lfm_moe_status lfm_moe_experts_fp8_ws(const uint16_t* X, const int32_t* idx, con
                                      scales_down, out, N, false);
   if (st != LFM_MOE_OK || N == 0) return st;
   const Span o{out, act_bytes(N, 4)};
-  if ((st = check_ws(ws, ws_bytes, N, o)) != LFM_MOE_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, N, o,
+                     {{X, act_bytes(N, 2)}, {W_gateup_fp8, kFp8GateupBytes}, {scales_gateup, kFp8GateupScaleBytes},
+                      {W_down_fp8, kFp8DownBytes}, {scales_down, kFp8DownScaleBytes}})) != LFM_MOE_OK)
+    return st;
   if ((st = check_routing_args(idx, w, N, o, ws, ws_bytes)) != LFM_MOE_OK) return st;
   return run_fp8(X, nullptr, nullptr, idx, w, W_gateup_fp8, scales_gateup, W_down_fp8, scales_down,
                  out, N, ws, stream);
@@ -565,7 +586,10 @@ lfm_moe_status lfm_moe_forward_ws(const uint16_t* X, const uint16_t* W_r, const 
   lfm_moe_status st = check_layer_args(X, act_bytes(N, 2), W_r, bias, W_gateup, W_down, out,
                                        act_bytes(N, 4), N, false);
   if (st != LFM_MOE_OK || N == 0) return st;
-  if ((st = check_ws(ws, ws_bytes, N, Span{out, act_bytes(N, 4)})) != LFM_MOE_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, N, Span{out, act_bytes(N, 4)},
+                     {{X, act_bytes(N, 2)}, router_span(W_r), bias_span(bias), gateup_span(W_gateup),
+                      down_span(W_down)})) != LFM_MOE_OK)
+    return st;
   StageTimer timer(stream);
   return run_layer(X, W_r, bias, nullptr, nullptr, W_gateup, W_down, nullptr, out, N, ws, stream, timer);
 }
@@ -592,7 +616,9 @@ lfm_moe_status lfm_moe_experts_ws(const uint16_t* X, const int32_t* idx, const f
                                        act_bytes(N, 4), N, false, false);
   if (st != LFM_MOE_OK || N == 0) return st;
   const Span o{out, act_bytes(N, 4)};
-  if ((st = check_ws(ws, ws_bytes, N, o)) != LFM_MOE_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, N, o, {{X, act_bytes(N, 2)}, gateup_span(W_gateup), down_span(W_down)})) !=
+      LFM_MOE_OK)
+    return st;
   if ((st = check_routing_args(idx, w, N, o, ws, ws_bytes)) != LFM_MOE_OK) return st;
   StageTimer timer(stream);
   return run_layer(X, nullptr, nullptr, idx, w, W_gateup, W_down, nullptr, out, N, ws, stream, timer);
@@ -605,7 +631,9 @@ lfm_moe_status lfm_moe_block_forward_ws(float* x_inout, const uint16_t* W_r, con
   lfm_moe_status st = check_layer_args(x_inout, act_bytes(N, 4), W_r, bias, W_gateup, W_down,
                                        x_inout, act_bytes(N, 4), N, true);
   if (st != LFM_MOE_OK || N == 0) return st;
-  if ((st = check_ws(ws, ws_bytes, N, Span{x_inout, act_bytes(N, 4)})) != LFM_MOE_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, N, Span{x_inout, act_bytes(N, 4)},
+                     {router_span(W_r), bias_span(bias), gateup_span(W_gateup), down_span(W_down)})) != LFM_MOE_OK)
+    return st;
   uint16_t* X = region<uint16_t>(ws, N, LFM_MOE_WS_X);
   StageTimer timer(stream);
   hipError_t e = launch_rmsnorm(x_inout, X, N, stream);

@@ -100,6 +100,12 @@ def test_forward_ws_checks(lib):
     assert f(*a, 100, None, need, None) == _lib.ERR_INVALID_ARGUMENT
     assert f(*a, 100, ws + 16, need, None) == _lib.ERR_INVALID_ARGUMENT
     assert f(*a, 100, a[5], need, None) == _lib.ERR_INVALID_ARGUMENT  # overlaps out
+    for i in range(5):                                 # starts 256 bytes before an input
+        assert f(*a, 100, a[i] - 256, need, None) == _lib.ERR_INVALID_ARGUMENT
+        assert b"workspace overlaps an input" in lib.lfm_moe_last_error()
+    blk = lib.lfm_moe_block_forward_ws
+    assert blk(a[0], a[1], a[2], a[3], a[4], 100, a[3] + 4096, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert b"workspace overlaps an input" in lib.lfm_moe_last_error()
     assert f(*a, 0, None, 0, None) == _lib.OK
 
 
@@ -152,6 +158,9 @@ def test_fp8_argument_checks(lib):
     assert fw(*a, 8, ws, need - 1, None) == _lib.ERR_WORKSPACE_TOO_SMALL
     assert fw(*a, 8, a[7] - 256, need, None) == _lib.ERR_INVALID_ARGUMENT   # overlaps out
     assert fw(*a, _lib.FP8_MAX_TOKENS + 1, ws, 1 << 40, None) == _lib.ERR_INVALID_ARGUMENT
+    for i in range(7):                                      # starts 256 bytes before an input
+        assert fw(*a, 8, a[i] - 256, need, None) == _lib.ERR_INVALID_ARGUMENT
+        assert b"workspace overlaps an input" in lib.lfm_moe_last_error()
     g, d = lib.lfm_moe_pack_fp8_gateup, lib.lfm_moe_pack_fp8_down
     assert g(a[0], a[1], a[2], None, None) == _lib.ERR_INVALID_ARGUMENT
     assert g(a[0], a[1], a[0] + 512, a[3], None) == _lib.ERR_INVALID_ARGUMENT   # codes over W_gate
@@ -185,6 +194,9 @@ def test_experts_argument_checks(lib):
     b[5] = a[1] + 256                                                      # out over the selections
     assert f(*b, N, ws, need, None) == _lib.ERR_INVALID_ARGUMENT
     assert b"routing" in lib.lfm_moe_last_error()
+    for i in (0, 3, 4):                                                    # X, W_gateup, W_down
+        assert f(*a, N, a[i] - 256, need, None) == _lib.ERR_INVALID_ARGUMENT
+        assert b"workspace overlaps an input" in lib.lfm_moe_last_error()
     b = list(a)
     b[2] = ws + 1024                                                       # weights inside the workspace
     assert f(*b, N, ws, need, None) == _lib.ERR_INVALID_ARGUMENT
