@@ -172,7 +172,9 @@ size_t lfm_moe_workspace_offset(int64_t N, int region);
 
 /*
  * lfm_moe_forward with a caller-owned workspace `ws` of `ws_bytes` bytes
- * (device memory, 256-byte aligned, at least lfm_moe_workspace_bytes(N)).
+ * (device memory, 256-byte aligned, at least lfm_moe_workspace_bytes(N),
+ * overlapping neither the output nor any input tensor: every _ws entry
+ * point returns LFM_MOE_ERR_INVALID_ARGUMENT otherwise).
  * The workspace holds the intermediate results listed in lfm_moe_ws_region
  * after the call completes.  Batches of up to 96 tokens take the
  * decode-shaped path, whose expert kernels group their own tokens and leave
