@@ -163,6 +163,45 @@ def test_invalid_routing_is_replaced_by_the_documented_rule(moe, N, fp8):
     assert torch.isfinite(out).all().item()
 
 
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("N", [64, 700])
+def test_experts_graph_replays_match_eager(moe, N, fp8):
+    """The expert path records no allocation, memset or host synchronisation
+    either: captured in a HIP graph, three replays (with eager calls and
+    synchronisations between them) equal the eager result bit for bit."""
+    inp, dev = _case(moe)
+    _, X = _x(N, 2900 + N)
+    idx = torch.from_numpy(np.stack([np.random.default_rng(N).choice(64, 4, replace=False)
+                                     for _ in range(N)]).astype(np.int32)).cuda()
+    w = torch.full((N, 4), 0.25, device="cuda")
+    ws = moe.alloc_workspace(N)
+    _step(f"graph capture experts{'_fp8' if fp8 else ''}_ws N={N}")
+    eager = _experts(moe, dev, fp8, X, idx, w, ws).clone()
+
+    def run(out):
+        if fp8:
+            moe.experts_fp8(X, idx, w, dev["gateup_fp8"], dev["down_fp8"], out=out, workspace=ws)
+        else:
+            moe.experts(X, idx, w, dev["W_gateup"], dev["W_down"], out=out, workspace=ws)
+
+    out = torch.empty_like(eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(out)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(out)
+    for i in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i} differs from the eager call"
+        run(torch.empty_like(eager))
+        torch.cuda.synchronize()
+
+
 def test_experts_with_no_tokens_is_a_no_op(moe):
     _, dev = _case(moe)
     X = torch.empty(0, 2048, dtype=torch.bfloat16, device="cuda")
