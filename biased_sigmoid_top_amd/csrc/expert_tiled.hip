@@ -100,7 +100,7 @@ struct TileShape {
 // A the bf16 values of the token rows' E4M3 codes and As the rows' scales per
 // 128-wide K group.  Each group of four stages (128 K) is accumulated on its
 // own and added into the result times weight scale x token scale.
-template <bool GATEUP, int FB_, int WAVES_, int TB_, bool FP8 = false>
+template <bool GATEUP, int FB_, int WAVES_, int TB_, bool FP8 = false, bool NTW = false>
 __global__ __launch_bounds__((TileShape<GATEUP, FB_, WAVES_, TB_>::kThreads),
                              (TileShape<GATEUP, FB_, WAVES_, TB_>::kPerCu))
 void expert_tiled_kernel(
@@ -178,7 +178,7 @@ void expert_tiled_kernel(
     for (int f = 0; f < FB; ++f)
 #pragma unroll
       for (int j = 0; j < kWK; ++j)
-        wv[f][j] = buf_ld<false>(wr, wlane, wbase + f * kBlockBytes + (sc * kWK + j) * kFragBytes);
+        wv[f][j] = buf_ld<NTW>(wr, wlane, wbase + f * kBlockBytes + (sc * kWK + j) * kFragBytes);
   };
   constexpr int kPairs = T::kStages / 2;
   uint4 stg[T::kChunks];
@@ -386,6 +386,13 @@ int64_t tiled_grid(int64_t N) {
 // 157.3 / 160.3 / 165.7; 6144: 210.6 / 217.6 / 209.9; 8192: 277.6 / 299.0 /
 // 264.8; 16384: 497.2 / 541.0 / 470.8.  With eight wavefronts a workgroup
 // has a CU to itself and its token tile feeds twice the weight rows.
+// Weight loads: up to kOneTouchTokens tokens most experts have a single
+// m-tile, so each weight byte is read once and the loads are non-temporal
+// (layer us, same box, plain / non-temporal: N = 160: 149.5-152.9 /
+// 141.8-144.3; 320: 174.1-177.9 / 164.5-168.5; 640: 219-220 both); above,
+// the m-tiles of an expert share its weight tiles through the L2 and
+// non-temporal loads cost (N = 2048: 333 / 362-368; 4096: 465-476 / 532-535).
+constexpr int64_t kOneTouchTokens = 512;
 enum class GateupTiles { kWide, kNarrow4, kNarrow8 };
 GateupTiles gateup_tiles(int64_t N) {
   if (N > 192 && N <= 512) return GateupTiles::kNarrow4;
@@ -401,14 +408,14 @@ DownTiles down_tiles(int64_t N) {
 }
 
 template <bool GATEUP, int FB, int WAVES = (GATEUP ? 8 : 4), int TB = 4, bool FP8 = false,
-          typename Out>
+          bool NTW = false, typename Out>
 hipError_t launch_tiled(const uint16_t* A, const void* W, const int32_t* offsets,
                         const int32_t* row2slot, Out* out, int64_t N, hipStream_t stream,
                         const float* Ws = nullptr, const float* As = nullptr) {
   uint16_t* H = nullptr;
   float* Y = nullptr;
   if constexpr (GATEUP) H = out; else Y = out;
-  hipLaunchKernelGGL((expert_tiled_kernel<GATEUP, FB, WAVES, TB, FP8>),
+  hipLaunchKernelGGL((expert_tiled_kernel<GATEUP, FB, WAVES, TB, FP8, NTW>),
                      dim3(tiled_grid<GATEUP, FB, WAVES, TB>(N)),
                      dim3(TileShape<GATEUP, FB, WAVES, TB>::kThreads), 0, stream, A, W, offsets,
                      row2slot, H, Y, Ws, As);
@@ -422,11 +429,12 @@ hipError_t launch_gateup_tiled(const uint16_t* X, const uint16_t* Wgu, const int
                                hipStream_t stream) {
   switch (gateup_tiles(N)) {
     case GateupTiles::kNarrow4:
-      return launch_tiled<true, 1, 4>(X, Wgu, offsets, row2slot, H, N, stream);
+      return launch_tiled<true, 1, 4, 4, false, true>(X, Wgu, offsets, row2slot, H, N, stream);
     case GateupTiles::kNarrow8:
       return launch_tiled<true, 1>(X, Wgu, offsets, row2slot, H, N, stream);
     default:
-      return launch_tiled<true, 2>(X, Wgu, offsets, row2slot, H, N, stream);
+      return N <= kOneTouchTokens ? launch_tiled<true, 2, 8, 4, false, true>(X, Wgu, offsets, row2slot, H, N, stream)
+                                  : launch_tiled<true, 2>(X, Wgu, offsets, row2slot, H, N, stream);
   }
 }
 
@@ -434,7 +442,7 @@ hipError_t launch_down_tiled(const uint16_t* H, const uint16_t* Wd, const int32_
                              const int32_t* row2slot, float* Y, int64_t N, hipStream_t stream) {
   switch (down_tiles(N)) {
     case DownTiles::kNarrow4:
-      return launch_tiled<false, 1, 4>(H, Wd, offsets, row2slot, Y, N, stream);
+      return launch_tiled<false, 1, 4, 4, false, true>(H, Wd, offsets, row2slot, Y, N, stream);
     case DownTiles::kNarrow8:
       return launch_tiled<false, 1, 8>(H, Wd, offsets, row2slot, Y, N, stream);
     case DownTiles::kWide8:
