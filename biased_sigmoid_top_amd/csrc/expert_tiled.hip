@@ -392,6 +392,9 @@ int64_t tiled_grid(int64_t N) {
 // 141.8-144.3; 320: 174.1-177.9 / 164.5-168.5; 640: 219-220 both); above,
 // the m-tiles of an expert share its weight tiles through the L2 and
 // non-temporal loads cost (N = 2048: 333 / 362-368; 4096: 465-476 / 532-535).
+// The FP8 grouped kernels (from 257 tokens) follow the same rule (FP8 layer
+// us: N = 300: 141.1-141.6 / 138.0-138.9; 400: 156.1-156.3 / 152.3-152.4;
+// 512: 166.4-167.0 / 165.5-165.9).
 constexpr int64_t kOneTouchTokens = 512;
 enum class GateupTiles { kWide, kNarrow4, kNarrow8 };
 GateupTiles gateup_tiles(int64_t N) {
@@ -455,13 +458,15 @@ hipError_t launch_down_tiled(const uint16_t* H, const uint16_t* Wd, const int32_
 hipError_t launch_gateup_tiled_fp8(const uint16_t* Xq, const uint8_t* Wq, const float* Ws,
                                    const float* Xs, const int32_t* offsets, const int32_t* row2slot,
                                    uint16_t* H, int64_t N, hipStream_t stream) {
-  return launch_tiled<true, 1, 8, 4, true>(Xq, Wq, offsets, row2slot, H, N, stream, Ws, Xs);
+  return N <= kOneTouchTokens ? launch_tiled<true, 1, 8, 4, true, true>(Xq, Wq, offsets, row2slot, H, N, stream, Ws, Xs)
+                              : launch_tiled<true, 1, 8, 4, true>(Xq, Wq, offsets, row2slot, H, N, stream, Ws, Xs);
 }
 
 hipError_t launch_down_tiled_fp8(const uint16_t* Hq, const uint8_t* Wq, const float* Ws,
                                  const float* Hs, const int32_t* offsets, const int32_t* row2slot,
                                  float* Y, int64_t N, hipStream_t stream) {
-  return launch_tiled<false, 1, 4, 4, true>(Hq, Wq, offsets, row2slot, Y, N, stream, Ws, Hs);
+  return N <= kOneTouchTokens ? launch_tiled<false, 1, 4, 4, true, true>(Hq, Wq, offsets, row2slot, Y, N, stream, Ws, Hs)
+                              : launch_tiled<false, 1, 4, 4, true>(Hq, Wq, offsets, row2slot, Y, N, stream, Ws, Hs);
 }
 
 }  // namespace lfm
