@@ -21,7 +21,7 @@ from parity import (check_route, device_inputs, expected_outputs, oracle_fp8_exp
 
 pytestmark = pytest.mark.gpu
 
-OUT_GATE_FP8 = 5e-2
+OUT_GATE_FP8 = 2e-2
 
 _STATE = {}
 
@@ -92,10 +92,8 @@ def _check_fp8_forward(moe, inp, dev, q, N):
       codes of H are a rounding decision taken from H's bf16 values, so the
       comparison is made on the same H): fp32 accumulation error only;
     * out against the combine of the GPU's Y and w;
-    * out against the FP8 oracle end to end within 5e-2 * RMS: a hidden
-      value one bf16 ulp away from the oracle's can land on the neighbouring
-      FP8 code, a step of up to 1/8 of the value, and a few such flips per
-      batch move single outputs by up to ~2.5e-2 * RMS on this workload.
+    * out against the FP8 oracle end to end within 2e-2 * RMS, the bar of
+      the bf16 layer.
     """
     from biased_sigmoid_top_amd import _lib
     from oracle import fp8
@@ -176,12 +174,12 @@ def test_fp8_forward_parity_decode_n64(moe):
     _check_fp8_forward(moe, inp, dev, q, inp["X"].shape[0])
 
 
-def test_fp8_forward_skewed_sampled(moe):
+def test_fp8_forward_skewed_all_tokens(moe):
     """The FP8 layer at the largest configuration (16,384 tokens, skewed bias:
     most slots on experts 0-7, which then run up to ~100 m-tiles each on the
-    grouped kernels in FP8 mode), on sampled tokens: the GPU's selections
+    grouped kernels in FP8 mode), on every token: the GPU's selections
     checked against the oracle's (near ties accepted as for the bf16 layer),
-    the output against oracle.fp8 on those tokens and selections."""
+    the output against oracle.fp8 on the GPU's checked selections."""
     from biased_sigmoid_top_amd import _lib
     from oracle import fp8
     w_ = synth.WORKLOADS["skewed_n16384"]
@@ -201,13 +199,11 @@ def test_fp8_forward_skewed_sampled(moe):
     idx = _np(moe.workspace_view(ws, N, _lib.WS_IDX, torch.int32, (N, 4)))
     w = _np(moe.workspace_view(ws, N, _lib.WS_W, torch.float32, (N, 4))).astype(np.float64)
     assert np.all(np.isfinite(out))
-    rng = np.random.default_rng(1)
-    near = np.nonzero(r.margin <= 1e-4)[0]
-    tokens = np.unique(np.concatenate([rng.choice(N, 384, replace=False), near, [0, 1, N - 2, N - 1]]))
-    check_route(idx, w, r, tokens=tokens)
-    expect = fp8.moe_apply_fp8(inp["X"][tokens], idx[tokens], w[tokens], q).out
-    ratio = float(np.max(np.abs(out[tokens] - expect))) / float(np.sqrt(np.mean(expect ** 2)))
-    print(f"  sampled {len(tokens)} tokens, max|err| / RMS = {ratio:.4f}", flush=True)
+    alt = check_route(idx, w, r)
+    expect = fp8.moe_apply_fp8(inp["X"], idx, w, q).out
+    ratio = float(np.max(np.abs(out - expect))) / float(np.sqrt(np.mean(expect ** 2)))
+    print(f"  all {N} tokens ({len(alt)} near ties with another accepted set), "
+          f"max|err| / RMS = {ratio:.4f}", flush=True)
     assert ratio <= OUT_GATE_FP8, ratio
 
 

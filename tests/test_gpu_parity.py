@@ -111,19 +111,20 @@ def test_forward_parity_all_tokens(moe, name):
     print(f"  max|err| / RMS = {ratio:.4f}", flush=True)
 
 
-def test_forward_parity_skewed_sampled(moe):
+def test_forward_parity_skewed_all_tokens(moe):
+    """The largest workload (16,384 tokens, skewed bias: most slots on
+    experts 0-7, up to ~100 m-tiles per expert and the widest down tile) on
+    every token."""
     inp, dev, r = case("skewed_n16384")
     N = inp["X"].shape[0]
     _step(f"forward skewed_n16384 N={N}")
     out = moe.forward(dev["X"], dev["W_r"], dev["bias"], dev["W_gateup"], dev["W_down"])
     idx, w = moe.route(dev["X"], dev["W_r"], dev["bias"])
-    rng = np.random.default_rng(0)
-    near = np.nonzero(r.margin <= 1e-4)[0]
-    tokens = np.unique(np.concatenate([rng.choice(N, 384, replace=False), near,
-                                       [0, 1, N - 2, N - 1]]))
-    alt = check_route(_np(idx), _np(w), r, tokens=tokens)
-    ratio = check_out(_np(out)[tokens], expected_outputs(inp, r, tokens, alt))
-    print(f"  sampled {len(tokens)} tokens, max|err| / RMS = {ratio:.4f}", flush=True)
+    alt = check_route(_np(idx), _np(w), r)
+    tokens = np.arange(N)
+    ratio = check_out(_np(out), expected_outputs(inp, r, tokens, alt))
+    print(f"  all {N} tokens ({len(alt)} near ties with another accepted set), "
+          f"max|err| / RMS = {ratio:.4f}", flush=True)
 
 
 @pytest.mark.parametrize("name", ["tiny_n32", "decode_n64", "prefill_n4096"])
@@ -252,7 +253,7 @@ def _layer_case(N, seed_z, bias_override=None):
     return inp, dev
 
 
-@pytest.mark.parametrize("N", [1, 2, 17, 63, 65, 96, 97, 193, 257, 511, 513, 1000, 2049])
+@pytest.mark.parametrize("N", [1, 2, 17, 63, 65, 96, 97, 193, 257, 511, 513, 1000, 2049, 6145])
 def test_ragged_token_counts(moe, N):
     inp, dev = _layer_case(N, 100 + N)
     r = oracle.route(inp["X"], inp["W_r"], inp["bias"])

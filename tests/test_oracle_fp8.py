@@ -152,3 +152,57 @@ def test_fp8_layer_is_close_to_the_bf16_layer(seed):
     b = oracle.moe_apply(X, idx, w, Wg, Wu, Wd).out
     rel = np.sqrt(np.mean((a - b) ** 2)) / np.sqrt(np.mean(b ** 2))
     assert 1e-3 < rel < 0.1
+
+
+def _grid_values(rng, n):
+    """n random E4M3 normal values built from the format's definition,
+    +-(1 + m/8) * 2^e with e in [-6, 7] (all below 448, exact in fp32)."""
+    m = rng.integers(0, 8, n)
+    e = rng.integers(-6, 8, n)
+    sgn = rng.choice([-1.0, 1.0], n)
+    return sgn * (1.0 + m / 8.0) * np.exp2(e)
+
+
+def test_down_step_quantises_hidden_rows_and_weights_exactly():
+    """fp8.expert_down_fp8 on hand-checked values.  Every group or block
+    maximum is 448 * 2^-k, so its scale 2^-k and 448 / amax are exact; each
+    off-grid value is listed with the E4M3 value the format's spacing rounds
+    it to (round to nearest; no value sits near a midpoint).  The products
+    and sums of these dyadic values are exact in float64, so the down step
+    must equal the hand-dequantised product bit for bit.  A down step that
+    skipped the quantisation of H, used another group size, or dropped a
+    scale would give a different result."""
+    # (raw value, dequantised value) per group; group = 128 columns.
+    H_cases = {
+        (0, 0): [(448.0, 448.0), (1.03, 1.0), (2.3, 2.25), (-5.1, -5.0), (300.0, 288.0),
+                 (0.0101, 5 * 2.0 ** -9)],                      # scale 1; 0.0101 is subnormal
+        (0, 1): [(56.0, 56.0), (1.03, 1.0), (3.3, 3.25), (-0.7, -0.6875)],   # 56 = 448 / 8
+        (1, 0): [(-7.0, -7.0), (0.1, 0.1015625), (1.0, 1.0)],              # 7 = 448 / 64
+        (1, 1): [],                                                          # all zero: scale 0
+        (2, 0): [(224.0, 224.0), (0.33, 0.34375)],                           # 224 = 448 / 2
+        (2, 1): [(-28.0, -28.0), (2.2, 2.25)],                               # 28 = 448 / 16
+    }
+    H = np.zeros((3, 256))
+    H_deq = np.zeros((3, 256))
+    for (row, grp), vals in H_cases.items():
+        for i, (raw, deq) in enumerate(vals):
+            col = grp * 128 + 7 * i + 3
+            H[row, col] = raw
+            H_deq[row, col] = deq
+    rng = np.random.default_rng(3)
+    W = np.zeros((128, 256))
+    W[:, :128] = _grid_values(rng, 128 * 128).reshape(128, 128)          # block scale 1
+    W[:, 128:] = 0.25 * _grid_values(rng, 128 * 128).reshape(128, 128)  # block scale 1/4
+    W[0, 0] = 448.0
+    W[5, 200] = 112.0                                                    # 448 / 4
+    W_deq = W.copy()
+    W[1, 10], W_deq[1, 10] = 1.03, 1.0         # scale 1: 1.03 -> 1.0
+    W[9, 131], W_deq[9, 131] = 0.3, 0.3125     # scale 1/4: 1.2 -> 1.25
+    codes, scales = fp8.quantize_blocks(W)
+    q = {"down_codes": codes[None], "down_scales": scales[None]}
+    got = fp8.expert_down_fp8(H, q, 0)
+    want = H_deq @ W_deq.T
+    np.testing.assert_array_equal(got, want)
+    # The quantisation matters: the unquantised product is another result.
+    assert not np.array_equal(got, H @ W_deq.T)
+    assert not np.array_equal(got, H_deq @ W.T)

@@ -194,3 +194,41 @@ def test_rmsnorm_closed_forms():
     np.testing.assert_allclose(np.mean(y * y, 1), ms / (ms + 1e-6), rtol=1e-12)
     # Scale invariance up to the epsilon term.
     np.testing.assert_allclose(oracle.rmsnorm(10 * z), y, rtol=1e-6)
+
+
+def test_weights_for_set_closed_forms():
+    """oracle.weights_for_set against the page's facts and the closed form:
+    on the illustrative token E enters the weights with its unbiased 0.40
+    (section "The router has two different scores"), the weights are the
+    selected unbiased scores over their sum plus 1e-6, so they sum to
+    S / (S + 1e-6) < 1, and they equal the router's own weights for the set
+    it selects, in any order of the set."""
+    fx, s, b, names = _illustrative()
+    ids = {n: v["expert"] for n, v in fx["candidates"].items()}
+    # Literal values: A 0.90, B 0.80, C 0.70, E 0.40 (E's score from the page).
+    got = oracle.weights_for_set(s, [ids["A"], ids["B"], ids["C"], ids["E"]])
+    den = 0.90 + 0.80 + 0.70 + 0.40 + 1e-6
+    np.testing.assert_allclose(got, [0.90 / den, 0.80 / den, 0.70 / den, 0.40 / den], rtol=0, atol=1e-15)
+    assert got[3] == pytest.approx(0.40 / 2.800001, abs=1e-15)   # not 0.60 / ...
+    # Without the bias the set has D (0.55) in E's place.
+    got_d = oracle.weights_for_set(s, [ids["A"], ids["B"], ids["C"], ids["D"]])
+    np.testing.assert_allclose(got_d, np.array([0.90, 0.80, 0.70, 0.55]) / (2.95 + 1e-6), rtol=0,
+                               atol=1e-15)
+    # The set's order permutes the weights and nothing else.
+    perm = oracle.weights_for_set(s, [ids["E"], ids["C"], ids["A"], ids["B"]])
+    np.testing.assert_allclose(perm, got[[3, 2, 0, 1]], rtol=0, atol=1e-16)
+    # Closed form of the sum on random tokens, and agreement with the router.
+    rng = np.random.default_rng(5)
+    l = rng.normal(0, 0.9, size=(64, 64))
+    bias = rng.uniform(-0.25, 0.25, size=64)
+    r = oracle.route_from_logits(l, bias)
+    for t in range(64):
+        S = [int(e) for e in r.idx[t]]
+        w = oracle.weights_for_set(r.s[t], S)
+        tot = float(np.sum(r.s[t, S]))
+        assert w.sum() < 1.0
+        assert 1.0 - w.sum() == pytest.approx(1e-6 / (tot + 1e-6), rel=1e-6)
+        np.testing.assert_allclose(w, r.w[t], rtol=0, atol=1e-16)
+        # A wrong set gives different weights (the function uses the set it is given).
+        other = S[:3] + [next(e for e in range(64) if e not in S)]
+        assert not np.allclose(oracle.weights_for_set(r.s[t], other), w, atol=1e-9)
