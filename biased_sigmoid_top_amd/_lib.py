@@ -36,6 +36,10 @@ SIGNATURES = {
     "lfm_moe_last_error": (ctypes.c_char_p, []),
     "lfm_moe_rmsnorm": (ctypes.c_int, [_P, _P, _I64, _P]),
     "lfm_moe_route": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _P]),
+    "lfm_moe_route_workspace_bytes": (_SZ, [_I64]),
+    "lfm_moe_route_ws": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _P, _SZ, _P]),
+    "lfm_moe_pack_gateup_stacked": (ctypes.c_int, [_P, _P, _P]),
+    "lfm_moe_pack_fp8_gateup_stacked": (ctypes.c_int, [_P, _P, _P, _P]),
     "lfm_moe_pack_gateup": (ctypes.c_int, [_P, _P, _P, _P]),
     "lfm_moe_pack_down": (ctypes.c_int, [_P, _P, _P]),
     "lfm_moe_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _P]),

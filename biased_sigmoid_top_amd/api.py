@@ -50,6 +50,18 @@ def pack_gateup(W_gate, W_up, out=None, stream=None):
     return out
 
 
+def pack_gateup_stacked(W_gateup, out=None, stream=None):
+    """Packs one stacked [64, 3072, 2048] gate/up tensor (rows 0..1535 of an
+    expert are its gate rows, 1536..3071 its up rows) into the fragment
+    layout; the same bytes as pack_gateup on the two halves."""
+    pw = _req(W_gateup, "W_gateup", torch.bfloat16, (EXPERTS, 2 * FF, HIDDEN))
+    if out is None:
+        out = torch.empty(EXPERTS * 2 * FF * HIDDEN, dtype=torch.bfloat16, device=W_gateup.device)
+    po = _req(out, "W_gateup_packed", torch.bfloat16, (EXPERTS * 2 * FF * HIDDEN,))
+    _lib.call("lfm_moe_pack_gateup_stacked", pw, po, _stream(stream))
+    return out
+
+
 def pack_down(W_down, out=None, stream=None):
     """Packs the [64, 2048, 1536] down matrices into the fragment layout."""
     pd = _req(W_down, "W_down", torch.bfloat16, (EXPERTS, HIDDEN, FF))
@@ -98,7 +110,14 @@ def rmsnorm(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> to
     return out
 
 
-def route(X, W_r, bias, idx=None, w=None, stream=None):
+def route_workspace_bytes(N: int) -> int:
+    return int(_lib.load().lfm_moe_route_workspace_bytes(N))
+
+
+def route(X, W_r, bias, idx=None, w=None, workspace=None, stream=None):
+    """Selections [N, 4] int32 and weights [N, 4] fp32.  With ``workspace``
+    (a byte tensor of at least route_workspace_bytes(N)) lfm_moe_route_ws is
+    used."""
     N = X.shape[0]
     pX = _req(X, "X", torch.bfloat16, (N, HIDDEN))
     pW = _req(W_r, "W_r", torch.bfloat16, (EXPERTS, HIDDEN))
@@ -109,7 +128,11 @@ def route(X, W_r, bias, idx=None, w=None, stream=None):
         w = torch.empty(N, TOP_K, dtype=torch.float32, device=X.device)
     pi = _req(idx, "idx", torch.int32, (N, TOP_K))
     pw = _req(w, "w", torch.float32, (N, TOP_K))
-    _lib.call("lfm_moe_route", pX, pW, pb, pi, pw, N, _stream(stream))
+    if workspace is None:
+        _lib.call("lfm_moe_route", pX, pW, pb, pi, pw, N, _stream(stream))
+    else:
+        _lib.call("lfm_moe_route_ws", pX, pW, pb, pi, pw, N, workspace.data_ptr(),
+                  workspace.numel() * workspace.element_size(), _stream(stream))
     return idx, w
 
 
@@ -125,6 +148,16 @@ def pack_fp8_gateup(W_gate, W_up, stream=None):
     codes = torch.empty(EXPERTS * 2 * FF * HIDDEN, dtype=torch.uint8, device=W_gate.device)
     scales = torch.empty(FP8_GATEUP_SCALES, dtype=torch.float32, device=W_gate.device)
     _lib.call("lfm_moe_pack_fp8_gateup", pg, pu, codes.data_ptr(), scales.data_ptr(), _stream(stream))
+    return codes, scales
+
+
+def pack_fp8_gateup_stacked(W_gateup, stream=None):
+    """FP8 block quantisation of one stacked [64, 3072, 2048] gate/up tensor:
+    the same (codes, scales) as pack_fp8_gateup on its two halves."""
+    pw = _req(W_gateup, "W_gateup", torch.bfloat16, (EXPERTS, 2 * FF, HIDDEN))
+    codes = torch.empty(EXPERTS * 2 * FF * HIDDEN, dtype=torch.uint8, device=W_gateup.device)
+    scales = torch.empty(FP8_GATEUP_SCALES, dtype=torch.float32, device=W_gateup.device)
+    _lib.call("lfm_moe_pack_fp8_gateup_stacked", pw, codes.data_ptr(), scales.data_ptr(), _stream(stream))
     return codes, scales
 
 
@@ -161,6 +194,25 @@ def forward_fp8(X, W_r, bias, gateup_fp8, down_fp8, out=None, workspace=None, st
     return out
 
 
+def _temporaries(out, workspace, N, device, stream):
+    """The output and workspace of an expert-path call, allocated here when
+    not given.  The caching allocator hands out memory for the current
+    stream; when the call runs on another stream, the tensors are marked as
+    in use there, so that their memory is not reused before that stream has
+    passed the call."""
+    made = []
+    if out is None:
+        out = torch.empty(N, HIDDEN, dtype=torch.float32, device=device)
+        made.append(out)
+    if workspace is None:
+        workspace = alloc_workspace(N, device)
+        made.append(workspace)
+    if stream is not None:
+        for t in made:
+            t.record_stream(stream)
+    return out, workspace
+
+
 def _routing(idx, w, N):
     return (_req(idx, "idx", torch.int32, (N, TOP_K)), _req(w, "w", torch.float32, (N, TOP_K)))
 
@@ -173,11 +225,8 @@ def experts(X, idx, w, W_gateup, W_down, out=None, workspace=None, stream=None):
     pi, pw = _routing(idx, w, N)
     pg = _req(W_gateup, "W_gateup (packed)", torch.bfloat16, (EXPERTS * 2 * FF * HIDDEN,))
     pd = _req(W_down, "W_down (packed)", torch.bfloat16, (EXPERTS * HIDDEN * FF,))
-    if out is None:
-        out = torch.empty(N, HIDDEN, dtype=torch.float32, device=X.device)
+    out, workspace = _temporaries(out, workspace, N, X.device, stream)
     po = _req(out, "out", torch.float32, (N, HIDDEN))
-    if workspace is None:
-        workspace = alloc_workspace(N, X.device)
     _lib.call("lfm_moe_experts_ws", pX, pi, pw, pg, pd, po, N, workspace.data_ptr(),
               workspace.numel() * workspace.element_size(), _stream(stream))
     return out
@@ -192,11 +241,8 @@ def experts_fp8(X, idx, w, gateup_fp8, down_fp8, out=None, workspace=None, strea
     gs = _req(gateup_fp8[1], "scales_gateup", torch.float32, FP8_GATEUP_SCALES)
     dc = _req(down_fp8[0], "W_down_fp8", torch.uint8, (EXPERTS * HIDDEN * FF,))
     ds = _req(down_fp8[1], "scales_down", torch.float32, FP8_DOWN_SCALES)
-    if out is None:
-        out = torch.empty(N, HIDDEN, dtype=torch.float32, device=X.device)
+    out, workspace = _temporaries(out, workspace, N, X.device, stream)
     po = _req(out, "out", torch.float32, (N, HIDDEN))
-    if workspace is None:
-        workspace = alloc_workspace(N, X.device)
     _lib.call("lfm_moe_experts_fp8_ws", pX, pi, pw, gc, gs, dc, ds, po, N, workspace.data_ptr(),
               workspace.numel() * workspace.element_size(), _stream(stream))
     return out

@@ -1,4 +1,8 @@
-"""Builds liblfm_moe.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree."""
+"""Builds liblfm_moe.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+
+Each source is compiled to an object on its own (in parallel), then the
+objects are linked into the shared library.
+"""
 
 from __future__ import annotations
 
@@ -7,16 +11,18 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblfm_moe.so")
+OBJ_DIR = os.path.join(ROOT, "_build", "obj")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-O3", "-std=c++17", "-fPIC",
     f"--offload-arch={ARCH}",
     # Packed fp32 instructions stay off (hipcc's host pass warns that it
     # does not know the feature; the warning is harmless).
@@ -32,20 +38,30 @@ def hipcc() -> str:
     return exe
 
 
-def build(verbose: bool = False) -> str:
-    """Compiles every HIP source into liblfm_moe.so and returns its path."""
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops" not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{out}")
     if verbose and out.strip():
         print(out, flush=True)
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compiles every HIP source into liblfm_moe.so and returns its path."""
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    objs = [os.path.join(OBJ_DIR, os.path.basename(s) + ".o") for s in srcs]
+    cc = hipcc()
+    jobs = jobs or min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(jobs) as pool:
+        list(pool.map(lambda so: _run([cc, *HIPCC_FLAGS, f"-I{INCLUDE}", "-c", so[0], "-o", so[1]],
+                                      verbose), zip(srcs, objs)))
+    tmp = LIB + ".tmp"
+    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

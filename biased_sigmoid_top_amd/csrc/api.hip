@@ -144,37 +144,44 @@ lfm_moe_status check_routing_args(const int32_t* idx, const float* w, int64_t N,
   return LFM_MOE_OK;
 }
 
-// Library-owned workspace, one per device, grown on demand.
+// Library-owned workspaces, one per device and purpose (the layer's, and
+// the router's partial logits for lfm_moe_route), grown on demand.
 constexpr int kMaxDevices = 64;
+enum WsKind { kLayerWs = 0, kRouteWs = 1, kWsKinds = 2 };
 std::mutex g_ws_mu;
-void* g_ws[kMaxDevices] = {};
-size_t g_ws_bytes[kMaxDevices] = {};
+void* g_ws[kWsKinds][kMaxDevices] = {};
+size_t g_ws_bytes[kWsKinds][kMaxDevices] = {};
 
-lfm_moe_status internal_ws(int64_t N, void** ws, size_t* bytes) {
+lfm_moe_status internal_ws(WsKind kind, size_t need, void** ws, size_t* bytes) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   if (dev < 0 || dev >= kMaxDevices) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "device ordinal out of range");
-  const size_t need = workspace_bytes(N);
   std::lock_guard<std::mutex> lock(g_ws_mu);
-  if (g_ws_bytes[dev] < need) {
-    if (g_ws[dev]) {
-      e = hipFree(g_ws[dev]);  // hipFree waits for work that may still use it
-      g_ws[dev] = nullptr;
-      g_ws_bytes[dev] = 0;
+  void*& buf = g_ws[kind][dev];
+  size_t& have = g_ws_bytes[kind][dev];
+  if (have < need) {
+    if (buf) {
+      e = hipFree(buf);  // hipFree waits for work that may still use it
+      buf = nullptr;
+      have = 0;
       if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
     }
-    e = hipMalloc(&g_ws[dev], need);
+    e = hipMalloc(&buf, need);
     if (e != hipSuccess) {
-      g_ws[dev] = nullptr;
+      buf = nullptr;
       (void)hipGetLastError();
       return fail(LFM_MOE_ERR_OUT_OF_MEMORY, "hipMalloc of " + std::to_string(need) + " workspace bytes failed");
     }
-    g_ws_bytes[dev] = need;
+    have = need;
   }
-  *ws = g_ws[dev];
-  *bytes = g_ws_bytes[dev];
+  *ws = buf;
+  *bytes = have;
   return LFM_MOE_OK;
+}
+
+lfm_moe_status internal_ws(int64_t N, void** ws, size_t* bytes) {
+  return internal_ws(kLayerWs, workspace_bytes(N), ws, bytes);
 }
 
 // Per-kernel timing for measurements (lfm_moe_timing_*).
@@ -458,7 +465,21 @@ lfm_moe_status lfm_moe_pack_gateup(const uint16_t* W_gate, const uint16_t* W_up,
   const Span o{W_gateup, 2 * half};
   if (overlap(o, Span{W_gate, half}) || overlap(o, Span{W_up, half}))
     return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "output overlaps an input");
-  hipError_t e = launch_pack_gateup(W_gate, W_up, W_gateup, stream);
+  hipError_t e = launch_pack_gateup(W_gate, W_up, static_cast<size_t>(kFF) * kHidden, W_gateup, stream);
+  return e == hipSuccess ? LFM_MOE_OK : hip_fail(e, "pack kernel launch");
+}
+
+lfm_moe_status lfm_moe_pack_gateup_stacked(const uint16_t* W_gateup, uint16_t* W_gateup_packed,
+                                           hipStream_t stream) {
+  g_last_error.clear();
+  if (!W_gateup || !W_gateup_packed) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if (misaligned(W_gateup) || misaligned(W_gateup_packed))
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  const size_t bytes = sizeof(uint16_t) * kExperts * 2 * kFF * kHidden;
+  if (overlap(Span{W_gateup, bytes}, Span{W_gateup_packed, bytes}))
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "output overlaps the input");
+  const size_t half = static_cast<size_t>(kFF) * kHidden;
+  hipError_t e = launch_pack_gateup(W_gateup, W_gateup + half, 2 * half, W_gateup_packed, stream);
   return e == hipSuccess ? LFM_MOE_OK : hip_fail(e, "pack kernel launch");
 }
 
@@ -489,7 +510,25 @@ lfm_moe_status lfm_moe_pack_fp8_gateup(const uint16_t* W_gate, const uint16_t* W
     if (overlap(o, Span{W_gate, half}) || overlap(o, Span{W_up, half}))
       return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "output overlaps an input");
   if (overlap(outs[0], outs[1])) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "codes overlap scales");
-  hipError_t e = launch_pack_fp8_gateup(W_gate, W_up, W_gateup_fp8, scales_gateup, stream);
+  hipError_t e = launch_pack_fp8_gateup(W_gate, W_up, static_cast<size_t>(kFF) * kHidden, W_gateup_fp8,
+                                        scales_gateup, stream);
+  return e == hipSuccess ? LFM_MOE_OK : hip_fail(e, "fp8 pack kernel launch");
+}
+
+lfm_moe_status lfm_moe_pack_fp8_gateup_stacked(const uint16_t* W_gateup, uint8_t* W_gateup_fp8,
+                                               float* scales_gateup, hipStream_t stream) {
+  g_last_error.clear();
+  if (!W_gateup || !W_gateup_fp8 || !scales_gateup)
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if (misaligned(W_gateup) || misaligned(W_gateup_fp8) || misaligned(scales_gateup))
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  const Span in{W_gateup, sizeof(uint16_t) * kExperts * 2 * kFF * kHidden};
+  const Span outs[] = {{W_gateup_fp8, kFp8GateupBytes}, {scales_gateup, kFp8GateupScaleBytes}};
+  for (const Span& o : outs)
+    if (overlap(o, in)) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "output overlaps the input");
+  if (overlap(outs[0], outs[1])) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "codes overlap scales");
+  const size_t half = static_cast<size_t>(kFF) * kHidden;
+  hipError_t e = launch_pack_fp8_gateup(W_gateup, W_gateup + half, 2 * half, W_gateup_fp8, scales_gateup, stream);
   return e == hipSuccess ? LFM_MOE_OK : hip_fail(e, "fp8 pack kernel launch");
 }
 
@@ -559,24 +598,76 @@ lfm_moe_status lfm_moe_forward_fp8(const uint16_t* X, const uint16_t* W_r, const
                  out, N, ws, stream);
 }
 
-lfm_moe_status lfm_moe_route(const uint16_t* X, const uint16_t* W_r, const float* bias,
-                             int32_t* idx, float* w, int64_t N, hipStream_t stream) {
-  g_last_error.clear();
+}  // extern "C"
+
+namespace {
+
+// Checks of the router entry points' tensors.
+lfm_moe_status check_route_args(const uint16_t* X, const uint16_t* W_r, const float* bias,
+                                const int32_t* idx, const float* w, int64_t N) {
   if (N < 0 || N > LFM_MOE_MAX_TOKENS) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "N out of range");
   if (N == 0) return LFM_MOE_OK;
   if (!X || !W_r || !bias || !idx || !w) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "null tensor pointer");
   if (misaligned(X) || misaligned(W_r) || misaligned(bias) || misaligned(idx) || misaligned(w))
     return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
   const size_t sel = static_cast<size_t>(N) * kTopK * 4;
-  if (overlap(Span{idx, sel}, Span{w, sel})) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "idx overlaps w");
-  void* ws = nullptr;
-  size_t bytes = 0;
-  lfm_moe_status st = internal_ws(N, &ws, &bytes);
-  if (st != LFM_MOE_OK) return st;
-  hipError_t e = launch_route(X, W_r, bias, idx, w, nullptr,
-                              region<float>(ws, N, LFM_MOE_WS_ROUTER_PARTIAL), static_cast<int>(N),
+  const Span outs[] = {{idx, sel}, {w, sel}};
+  if (overlap(outs[0], outs[1])) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "idx overlaps w");
+  const Span ins[] = {{X, act_bytes(N, 2)}, router_span(W_r), bias_span(bias)};
+  for (const Span& o : outs)
+    for (const Span& i : ins)
+      if (overlap(o, i)) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "output overlaps an input");
+  return LFM_MOE_OK;
+}
+
+lfm_moe_status run_route(const uint16_t* X, const uint16_t* W_r, const float* bias, int32_t* idx,
+                         float* w, int64_t N, void* ws, hipStream_t stream) {
+  hipError_t e = launch_route(X, W_r, bias, idx, w, nullptr, static_cast<float*>(ws), static_cast<int>(N),
                               stream);
   return e == hipSuccess ? LFM_MOE_OK : hip_fail(e, "route kernel launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lfm_moe_route_workspace_bytes(int64_t N) {
+  if (N < 0 || N > LFM_MOE_MAX_TOKENS) return 0;
+  return route_partial_bytes(N);
+}
+
+lfm_moe_status lfm_moe_route_ws(const uint16_t* X, const uint16_t* W_r, const float* bias,
+                                int32_t* idx, float* w, int64_t N, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  g_last_error.clear();
+  lfm_moe_status st = check_route_args(X, W_r, bias, idx, w, N);
+  if (st != LFM_MOE_OK || N == 0) return st;
+  const size_t need = route_partial_bytes(N);
+  if (need > 0) {
+    if (!ws) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "null workspace");
+    if (misaligned(ws, kAlign)) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    if (ws_bytes < need)
+      return fail(LFM_MOE_ERR_WORKSPACE_TOO_SMALL,
+                  "workspace of " + std::to_string(ws_bytes) + " bytes, need " + std::to_string(need));
+    const Span wsp{ws, ws_bytes};
+    const size_t sel = static_cast<size_t>(N) * kTopK * 4;
+    const Span others[] = {{X, act_bytes(N, 2)}, router_span(W_r), bias_span(bias), {idx, sel}, {w, sel}};
+    for (const Span& o : others)
+      if (overlap(wsp, o)) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "workspace overlaps a tensor argument");
+  }
+  return run_route(X, W_r, bias, idx, w, N, ws, stream);
+}
+
+lfm_moe_status lfm_moe_route(const uint16_t* X, const uint16_t* W_r, const float* bias,
+                             int32_t* idx, float* w, int64_t N, hipStream_t stream) {
+  g_last_error.clear();
+  lfm_moe_status st = check_route_args(X, W_r, bias, idx, w, N);
+  if (st != LFM_MOE_OK || N == 0) return st;
+  void* ws = nullptr;
+  size_t bytes = 0;
+  const size_t need = route_partial_bytes(N);
+  if (need > 0 && (st = internal_ws(kRouteWs, need, &ws, &bytes)) != LFM_MOE_OK) return st;
+  return run_route(X, W_r, bias, idx, w, N, ws, stream);
 }
 
 lfm_moe_status lfm_moe_forward_ws(const uint16_t* X, const uint16_t* W_r, const float* bias,
@@ -658,16 +749,18 @@ lfm_moe_status lfm_moe_block_forward(float* x_inout, const uint16_t* W_r, const 
 void lfm_moe_release(void) {
   std::lock_guard<std::mutex> lock(g_ws_mu);
   bool any = false;
-  for (int d = 0; d < kMaxDevices; ++d) any = any || g_ws[d] != nullptr;
+  for (int k = 0; k < kWsKinds; ++k)
+    for (int d = 0; d < kMaxDevices; ++d) any = any || g_ws[k][d] != nullptr;
   if (!any) return;  // nothing to free: no HIP call at all
   int cur = 0;
   if (hipGetDevice(&cur) != hipSuccess) return;
-  for (int d = 0; d < kMaxDevices; ++d) {
-    if (!g_ws[d]) continue;
-    if (hipSetDevice(d) == hipSuccess) (void)hipFree(g_ws[d]);
-    g_ws[d] = nullptr;
-    g_ws_bytes[d] = 0;
-  }
+  for (int k = 0; k < kWsKinds; ++k)
+    for (int d = 0; d < kMaxDevices; ++d) {
+      if (!g_ws[k][d]) continue;
+      if (hipSetDevice(d) == hipSuccess) (void)hipFree(g_ws[k][d]);
+      g_ws[k][d] = nullptr;
+      g_ws_bytes[k][d] = 0;
+    }
   (void)hipSetDevice(cur);
 }
 

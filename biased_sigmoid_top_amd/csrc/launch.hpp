@@ -13,12 +13,13 @@ int route_block_tokens(int64_t N);
 // Upper bound of the number of m-tiles of tile_rows rows over all experts.
 int64_t max_mtiles(int64_t N, int tile_rows);
 
-hipError_t launch_pack_gateup(const uint16_t* Wg, const uint16_t* Wu, uint16_t* out,
+// Expert e's gate and up matrices start at Wg + e * estride, Wu + e * estride.
+hipError_t launch_pack_gateup(const uint16_t* Wg, const uint16_t* Wu, size_t estride, uint16_t* out,
                               hipStream_t stream);
 hipError_t launch_pack_down(const uint16_t* Wd, uint16_t* out, hipStream_t stream);
 
 // FP8 (E4M3) block quantisation + packing of the expert weights.
-hipError_t launch_pack_fp8_gateup(const uint16_t* Wg, const uint16_t* Wu, uint8_t* out,
+hipError_t launch_pack_fp8_gateup(const uint16_t* Wg, const uint16_t* Wu, size_t estride, uint8_t* out,
                                   float* scales, hipStream_t stream);
 hipError_t launch_pack_fp8_down(const uint16_t* Wd, uint8_t* out, float* scales,
                                 hipStream_t stream);

@@ -29,8 +29,12 @@ namespace {
 constexpr int kPackThreads = 256;
 
 // One thread moves one 16-byte piece (8 consecutive columns of one row).
+// Expert e's gate and up matrices start at Wg + e * estride and
+// Wu + e * estride (estride = 1536 * 2048 for two [64, 1536, 2048] tensors,
+// 2 * 1536 * 2048 for one [64, 3072, 2048] tensor of gate rows then up rows).
 __global__ __launch_bounds__(kPackThreads) void pack_gateup_kernel(
-    const uint16_t* __restrict__ Wg, const uint16_t* __restrict__ Wu, uint16_t* __restrict__ out) {
+    const uint16_t* __restrict__ Wg, const uint16_t* __restrict__ Wu, size_t estride,
+    uint16_t* __restrict__ out) {
   const size_t piece = static_cast<size_t>(blockIdx.x) * kPackThreads + threadIdx.x;
   const int lane = static_cast<int>(piece % kWave);
   const size_t frag = piece / kWave;
@@ -41,7 +45,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_gateup_kernel(
   const int i = lane % 32;
   const int row = b * 16 + (i % 16);
   const int col = ks * 16 + (lane / 32) * 8;
-  const uint16_t* src = (i < 16 ? Wg : Wu) + (e * kFF + row) * static_cast<size_t>(kHidden) + col;
+  const uint16_t* src = (i < 16 ? Wg : Wu) + e * estride + row * static_cast<size_t>(kHidden) + col;
   *reinterpret_cast<uint4*>(out + piece * 8) = ld16(src);
 }
 
@@ -62,11 +66,11 @@ __global__ __launch_bounds__(kPackThreads) void pack_down_kernel(const uint16_t*
 
 }  // namespace
 
-hipError_t launch_pack_gateup(const uint16_t* Wg, const uint16_t* Wu, uint16_t* out,
+hipError_t launch_pack_gateup(const uint16_t* Wg, const uint16_t* Wu, size_t estride, uint16_t* out,
                               hipStream_t stream) {
   const size_t pieces = static_cast<size_t>(kExperts) * 2 * kFF * kHidden / 8;
   hipLaunchKernelGGL(pack_gateup_kernel, dim3(pieces / kPackThreads), dim3(kPackThreads), 0,
-                     stream, Wg, Wu, out);
+                     stream, Wg, Wu, estride, out);
   return hipGetLastError();
 }
 

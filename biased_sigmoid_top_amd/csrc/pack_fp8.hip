@@ -87,16 +87,17 @@ __device__ __forceinline__ uint32_t frag_byte(int i, int c) {
 }
 
 // Block (e, m, rb, kb): m = 0 gate, 1 up; rb < 12 row blocks, kb < 16 column blocks.
+// Expert e's matrices start at Wg + e * estride and Wu + e * estride.
 __global__ __launch_bounds__(kQThreads) void pack_fp8_gateup_kernel(
-    const uint16_t* __restrict__ Wg, const uint16_t* __restrict__ Wu, uint8_t* __restrict__ out,
-    float* __restrict__ scales) {
+    const uint16_t* __restrict__ Wg, const uint16_t* __restrict__ Wu, size_t estride,
+    uint8_t* __restrict__ out, float* __restrict__ scales) {
   constexpr int kRB = kFF / kQBlock, kKB = kHidden / kQBlock;
   const int kb = blockIdx.x % kKB;
   const int rb = (blockIdx.x / kKB) % kRB;
   const int m = (blockIdx.x / (kKB * kRB)) % 2;
   const int e = blockIdx.x / (kKB * kRB * 2);
-  const uint16_t* W = (m == 0 ? Wg : Wu) + (static_cast<size_t>(e) * kFF + rb * kQBlock) * kHidden +
-                      kb * kQBlock;
+  const uint16_t* W = (m == 0 ? Wg : Wu) + static_cast<size_t>(e) * estride +
+                      static_cast<size_t>(rb * kQBlock) * kHidden + kb * kQBlock;
   quantize_block(W, kHidden, out, scales + blockIdx.x, [=](int r, int c) {
     const int R = rb * kQBlock + r, C = kb * kQBlock + c;
     const size_t frag = (static_cast<size_t>(e) * kGateupBlocks + R / 16) * (kHidden / 32) + C / 32;
@@ -121,11 +122,11 @@ __global__ __launch_bounds__(kQThreads) void pack_fp8_down_kernel(
 
 }  // namespace
 
-hipError_t launch_pack_fp8_gateup(const uint16_t* Wg, const uint16_t* Wu, uint8_t* out,
+hipError_t launch_pack_fp8_gateup(const uint16_t* Wg, const uint16_t* Wu, size_t estride, uint8_t* out,
                                   float* scales, hipStream_t stream) {
   const int blocks = kExperts * 2 * (kFF / kQBlock) * (kHidden / kQBlock);
-  hipLaunchKernelGGL(pack_fp8_gateup_kernel, dim3(blocks), dim3(kQThreads), 0, stream, Wg, Wu, out,
-                     scales);
+  hipLaunchKernelGGL(pack_fp8_gateup_kernel, dim3(blocks), dim3(kQThreads), 0, stream, Wg, Wu, estride,
+                     out, scales);
   return hipGetLastError();
 }
 

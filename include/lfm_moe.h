@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define LFM_MOE_ABI_VERSION 4
+#define LFM_MOE_ABI_VERSION 5
 #define LFM_MOE_HIDDEN 2048
 #define LFM_MOE_EXPERTS 64
 #define LFM_MOE_TOPK 4
@@ -93,11 +93,29 @@ lfm_moe_status lfm_moe_rmsnorm(const float* x, uint16_t* X, int64_t N, hipStream
  *         score s + bias, equal scores ordered by lower expert id
  *   w:    [N, 4] fp32 (written): w[t, j] = s[idx[t, j]] / (sum_j s + 1e-6)
  * The logits are summed from 16 partial products over 128-wide K slices,
- * in a fixed order, in the library-owned workspace of the current device
- * (grown on demand as for lfm_moe_forward).
+ * in a fixed order.  Up to 2048 tokens the partials pass through a
+ * workspace of lfm_moe_route_workspace_bytes(N) bytes (none above): the
+ * library-owned one of the current device (grown on demand, kept until
+ * lfm_moe_release(); separate from the layer's), so calls to lfm_moe_route
+ * that overlap in time on one device race on it -- use lfm_moe_route_ws
+ * with distinct workspaces for those.
  */
 lfm_moe_status lfm_moe_route(const uint16_t* X, const uint16_t* W_r, const float* bias,
                              int32_t* idx, float* w, int64_t N, hipStream_t stream);
+
+/* Bytes of workspace lfm_moe_route_ws needs for N tokens (0 above 2048 tokens). */
+size_t lfm_moe_route_workspace_bytes(int64_t N);
+
+/*
+ * lfm_moe_route with a caller-owned workspace `ws` of `ws_bytes` bytes
+ * (device memory, 256-byte aligned, at least lfm_moe_route_workspace_bytes(N),
+ * overlapping no tensor argument; may be NULL when that size is 0).  The
+ * same selections and weights as lfm_moe_route, bit for bit.  Concurrent
+ * calls need distinct workspaces.
+ */
+lfm_moe_status lfm_moe_route_ws(const uint16_t* X, const uint16_t* W_r, const float* bias,
+                                int32_t* idx, float* w, int64_t N, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
 
 /*
  * Expert weight packing (guide, section "The router has two different
@@ -119,10 +137,17 @@ lfm_moe_status lfm_moe_route(const uint16_t* X, const uint16_t* W_r, const float
  *   -> W_down_packed [64 * 2048 * 1536] bf16 (written): fragment
  *   (e * 64 + b) * 96 + ks holds rows 32 b .. 32 b + 31 of W_down of
  *   expert e, columns ks*16 .. ks*16+15 (b < 64, ks < 96).
+ * lfm_moe_pack_gateup_stacked: the same packed output from one
+ *   W_gateup [64, 3072, 2048] bf16 tensor (read) whose rows 0..1535 of
+ *   expert e are W_gate[e] and rows 1536..3071 are W_up[e] -- the stacked
+ *   gate/up layout of the layer's definition; bit-identical to
+ *   lfm_moe_pack_gateup on the two halves.
  * Outputs must not overlap the inputs.  A pure permutation: bit exact.
  */
 lfm_moe_status lfm_moe_pack_gateup(const uint16_t* W_gate, const uint16_t* W_up,
                                    uint16_t* W_gateup, hipStream_t stream);
+lfm_moe_status lfm_moe_pack_gateup_stacked(const uint16_t* W_gateup, uint16_t* W_gateup_packed,
+                                           hipStream_t stream);
 lfm_moe_status lfm_moe_pack_down(const uint16_t* W_down, uint16_t* W_down_packed,
                                  hipStream_t stream);
 
@@ -131,8 +156,13 @@ lfm_moe_status lfm_moe_pack_down(const uint16_t* W_down, uint16_t* W_down_packed
  *   X:        [N, 2048] bf16 normalised hidden states (read)
  *   W_r:      [64, 2048] bf16, bias: [64] fp32 (read), as for lfm_moe_route
  *   W_gateup: packed gate/up weights of all 64 experts, as written by
- *             lfm_moe_pack_gateup (read)
- *   W_down:   packed down weights, as written by lfm_moe_pack_down (read)
+ *             lfm_moe_pack_gateup or lfm_moe_pack_gateup_stacked (read).
+ *             The layer takes its expert weights only in this packed form:
+ *             a [64, 3072, 2048] stacked gate/up tensor (or separate
+ *             [64, 1536, 2048] gate and up tensors) is packed once, and
+ *             packing changes no value.
+ *   W_down:   packed down weights, as written by lfm_moe_pack_down from the
+ *             [64, 2048, 1536] tensor (read)
  *   out:      [N, 2048] fp32 (written; must not overlap any input)
  * Expert hidden activations are rounded to bf16 before the down
  * projection; every accumulation is fp32.  Uses a workspace that the
@@ -248,6 +278,9 @@ lfm_moe_status lfm_moe_block_forward_ws(float* x_inout, const uint16_t* W_r, con
  *   (e * 96 + b) * 64 + kp holds rows 16 b .. 16 b + 15 of W_gate as its
  *   rows 0..15 and the same rows of W_up as its rows 16..31, columns
  *   32 kp .. 32 kp + 31.
+ * lfm_moe_pack_fp8_gateup_stacked: the same codes and scales from one
+ *   stacked W_gateup [64, 3072, 2048] bf16 tensor (rows 0..1535 gate,
+ *   1536..3071 up of each expert).
  * lfm_moe_pack_fp8_down: W_down [64, 2048, 1536] bf16 (read) ->
  *   W_down_fp8 [64 * 2048 * 1536] bytes, scales_down [64][16][12] fp32
  *   (written); fragment (e * 64 + b) * 48 + kp holds rows 32 b .. 32 b + 31,
@@ -278,6 +311,8 @@ lfm_moe_status lfm_moe_block_forward_ws(float* x_inout, const uint16_t* W_r, con
 lfm_moe_status lfm_moe_pack_fp8_gateup(const uint16_t* W_gate, const uint16_t* W_up,
                                        uint8_t* W_gateup_fp8, float* scales_gateup,
                                        hipStream_t stream);
+lfm_moe_status lfm_moe_pack_fp8_gateup_stacked(const uint16_t* W_gateup, uint8_t* W_gateup_fp8,
+                                               float* scales_gateup, hipStream_t stream);
 lfm_moe_status lfm_moe_pack_fp8_down(const uint16_t* W_down, uint8_t* W_down_fp8,
                                      float* scales_down, hipStream_t stream);
 lfm_moe_status lfm_moe_forward_fp8(const uint16_t* X, const uint16_t* W_r, const float* bias,
@@ -293,7 +328,8 @@ lfm_moe_status lfm_moe_experts_fp8_ws(const uint16_t* X, const int32_t* idx, con
                                       const uint8_t* W_down_fp8, const float* scales_down, float* out,
                                       int64_t N, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Frees the library-owned workspaces (call with no work of this library in flight). */
+/* Frees the library-owned workspaces, the layer's and the router's (call with no work of
+ * this library in flight). */
 void lfm_moe_release(void);
 
 /*

@@ -72,6 +72,17 @@ int main() {
   EXPECT(lfm_moe_route(X, Wr, b, fake<int32_t>(8), fake<float>(8, 64), N, nullptr) == LFM_MOE_ERR_INVALID_ARGUMENT);
   EXPECT(lfm_moe_route(X, Wr, b, nullptr, fake<float>(9), N, nullptr) == LFM_MOE_ERR_INVALID_ARGUMENT);
   EXPECT(lfm_moe_route(X, Wr, b, fake<int32_t>(8), fake<float>(9), 0, nullptr) == LFM_MOE_OK);
+  const size_t rneed = lfm_moe_route_workspace_bytes(N);
+  EXPECT(rneed == 4u * 16 * 16 * 64 * 4 && lfm_moe_route_workspace_bytes(4096) == 0);
+  EXPECT(lfm_moe_route_ws(X, Wr, b, fake<int32_t>(8), fake<float>(9), N, nullptr, rneed, nullptr) ==
+         LFM_MOE_ERR_INVALID_ARGUMENT);
+  EXPECT(lfm_moe_route_ws(X, Wr, b, fake<int32_t>(8), fake<float>(9), N, ws, rneed - 4, nullptr) ==
+         LFM_MOE_ERR_WORKSPACE_TOO_SMALL);
+  EXPECT(lfm_moe_route_ws(X, Wr, b, fake<int32_t>(8), fake<float>(9), N, fake<void>(0, 256), rneed, nullptr) ==
+         LFM_MOE_ERR_INVALID_ARGUMENT && has_message());
+  EXPECT(lfm_moe_route_ws(X, Wr, b, fake<int32_t>(8), fake<float>(9), 0, nullptr, 0, nullptr) == LFM_MOE_OK);
+  EXPECT(lfm_moe_pack_gateup_stacked(Wgu, fake<uint16_t>(3, 1024), nullptr) == LFM_MOE_ERR_INVALID_ARGUMENT);
+  EXPECT(lfm_moe_pack_fp8_gateup_stacked(Wgu, fake<uint8_t>(10), nullptr, nullptr) == LFM_MOE_ERR_INVALID_ARGUMENT);
   EXPECT(lfm_moe_rmsnorm(nullptr, fake<uint16_t>(9), N, nullptr) == LFM_MOE_ERR_INVALID_ARGUMENT);
   EXPECT(lfm_moe_rmsnorm(x, fake<uint16_t>(9), -5, nullptr) == LFM_MOE_ERR_INVALID_ARGUMENT);
   EXPECT(lfm_moe_pack_gateup(Wgu, nullptr, fake<uint16_t>(10), nullptr) == LFM_MOE_ERR_INVALID_ARGUMENT);

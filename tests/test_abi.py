@@ -123,6 +123,36 @@ def test_route_rmsnorm_block_checks(lib):
     assert lib.lfm_moe_block_forward_ws(a[0], a[1], a[2], a[3], a[4], 4, None, 0, None) == _lib.ERR_INVALID_ARGUMENT
 
 
+def test_route_ws_checks(lib):
+    """lfm_moe_route_ws: the router workspace is the partial logits of up to
+    2048 tokens (none above), checked like the layer's."""
+    # X, W_r, bias, idx, w
+    a = [_addr(i) for i in range(5)]
+    ws = _addr(7)
+    rb = lib.lfm_moe_route_workspace_bytes
+    assert rb(64) == 4 * 16 * 16 * 64 * 4 and rb(2048) == 128 * 16 * 16 * 64 * 4
+    assert rb(2049) == 0 and rb(16384) == 0 and rb(-1) == 0 and rb(0) == 0
+    f = lib.lfm_moe_route_ws
+    need = rb(100)
+    assert f(*a, 0, None, 0, None) == _lib.OK
+    assert f(*a, -1, ws, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert f(*a, 100, None, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert f(*a, 100, ws + 16, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert f(*a, 100, ws, need - 1, None) == _lib.ERR_WORKSPACE_TOO_SMALL
+    for i in range(5):                                   # workspace over any tensor argument
+        assert f(*a, 100, a[i] - 256, need, None) == _lib.ERR_INVALID_ARGUMENT
+        assert b"workspace overlaps" in lib.lfm_moe_last_error()
+    b = list(a)
+    b[3] = a[0] + 64                                     # selections written over X
+    assert f(*b, 100, ws, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.lfm_moe_route(*b, 100, None) == _lib.ERR_INVALID_ARGUMENT
+    # Above 2048 tokens no workspace is needed, so none is checked.
+    for i in range(5):
+        c = list(a)
+        c[i] = None
+        assert f(*c, 4096, None, 0, None) == _lib.ERR_INVALID_ARGUMENT
+
+
 def test_pack_checks(lib):
     a = [_addr(i) for i in range(3)]
     assert lib.lfm_moe_pack_gateup(a[0], None, a[2], None) == _lib.ERR_INVALID_ARGUMENT
@@ -130,6 +160,14 @@ def test_pack_checks(lib):
     assert lib.lfm_moe_pack_gateup(a[0] + 2, a[1], a[2], None) == _lib.ERR_INVALID_ARGUMENT
     assert lib.lfm_moe_pack_down(a[0], a[0], None) == _lib.ERR_INVALID_ARGUMENT
     assert lib.lfm_moe_pack_down(None, a[1], None) == _lib.ERR_INVALID_ARGUMENT
+    st = lib.lfm_moe_pack_gateup_stacked
+    assert st(a[0], None, None) == _lib.ERR_INVALID_ARGUMENT
+    assert st(a[0] + 8, a[1], None) == _lib.ERR_INVALID_ARGUMENT
+    assert st(a[0], a[0] + 2 * 64 * 3072 * 2048 - 16, None) == _lib.ERR_INVALID_ARGUMENT  # last 16 bytes
+    s8 = lib.lfm_moe_pack_fp8_gateup_stacked
+    assert s8(a[0], a[1], None, None) == _lib.ERR_INVALID_ARGUMENT
+    assert s8(a[0], a[0] + 1024, a[2], None) == _lib.ERR_INVALID_ARGUMENT                  # codes over input
+    assert s8(a[0], a[1], a[1] + 256, None) == _lib.ERR_INVALID_ARGUMENT                   # scales over codes
 
 
 def test_fp8_argument_checks(lib):

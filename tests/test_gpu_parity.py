@@ -74,6 +74,69 @@ def test_weight_packing_is_the_documented_permutation(moe):
     assert torch.equal(got_d.view(torch.int16), ref_d.contiguous().view(torch.int16))
 
 
+def test_stacked_gateup_packs_to_the_same_bytes(moe):
+    """The stacked [64, 3072, 2048] gate/up tensor of the layer's definition
+    (rows 0..1535 gate, 1536..3071 up) packs to the same bytes as the two
+    halves, bf16 and FP8, and the layer on those bytes is the same call bit
+    for bit."""
+    w = synth.WORKLOADS["decode_n64"]
+    layer = cached_layer(w["N"], w["seed"], w["skew"])
+    inp, dev, r = case("decode_n64")
+    stacked = torch.cat([layer["W_gate"], layer["W_up"]], dim=1).contiguous()
+    assert stacked.shape == (64, 3072, 2048)
+    _step("pack_gateup_stacked / pack_fp8_gateup_stacked")
+    Ws = stacked.cuda()
+    packed = moe.pack_gateup_stacked(Ws)
+    codes, scales = moe.pack_fp8_gateup_stacked(Ws)
+    del Ws
+    assert torch.equal(packed.view(torch.int16), dev["W_gateup"].view(torch.int16))
+    c2, s2 = moe.pack_fp8_gateup(layer["W_gate"].cuda(), layer["W_up"].cuda())
+    assert torch.equal(codes, c2) and torch.equal(scales, s2)
+    del c2, s2, codes, scales
+    args = (dev["X"], dev["W_r"], dev["bias"])
+    a = moe.forward(*args, packed, dev["W_down"])
+    b = moe.forward(*args, dev["W_gateup"], dev["W_down"])
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("N", [64, 2048, 4096])
+def test_route_ws_equals_route(moe, N):
+    """lfm_moe_route_ws on a poisoned caller workspace gives the selections
+    and weights of lfm_moe_route bit for bit (split router up to 2048 tokens,
+    no workspace above)."""
+    inp, dev = _layer_case(N, 1400 + N)
+    nbytes = moe.route_workspace_bytes(N)
+    ws = torch.full((max(nbytes, 256),), 0xFF, dtype=torch.uint8, device="cuda") if nbytes else None
+    _step(f"route_ws N={N} ({nbytes} workspace bytes)")
+    i1, w1 = moe.route(dev["X"], dev["W_r"], dev["bias"], workspace=ws)
+    i2, w2 = moe.route(dev["X"], dev["W_r"], dev["bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2) and torch.equal(w1, w2)
+    r = oracle.route(inp["X"], inp["W_r"], inp["bias"])
+    check_route(_np(i1), _np(w1), r)
+
+
+def test_route_ws_on_two_streams(moe):
+    """Two router calls on two streams with their own workspaces, issued so
+    that they overlap, give the results of the calls made one at a time."""
+    cases = [_layer_case(64, 1500), _layer_case(1000, 1501)]
+    alone = [tuple(t.clone() for t in moe.route(d["X"], d["W_r"], d["bias"])) for _, d in cases]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    _step("route_ws on two streams")
+    for rep in range(3):
+        outs = []
+        for (inp, dev), st in zip(cases, streams):
+            N = inp["X"].shape[0]
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                ws = torch.empty(moe.route_workspace_bytes(N), dtype=torch.uint8, device="cuda")
+                outs.append(moe.route(dev["X"], dev["W_r"], dev["bias"], workspace=ws, stream=st))
+        torch.cuda.synchronize()
+        for (i, w), (ia, wa) in zip(outs, alone):
+            assert torch.equal(i, ia) and torch.equal(w, wa), f"repetition {rep}"
+
+
 @pytest.mark.parametrize("name", ["tiny_n32", "prefill_n4096"])
 def test_rmsnorm_parity(moe, name):
     w = synth.WORKLOADS[name]
@@ -327,6 +390,9 @@ def test_out_of_memory_is_reported(moe):
     lib = _lib.load()
     N = (1 << 24)                      # LFM_MOE_MAX_TOKENS: ~0.8 TB of workspace
     assert moe.workspace_bytes(N) > 400 * (1 << 30)
+    # More than the device holds, so the allocation must fail and the fake
+    # pointers below can never reach a kernel launch.
+    assert moe.workspace_bytes(N) > torch.cuda.mem_get_info()[1]
     fake = [0x7F00_0000_0000 + i * (1 << 36) for i in range(6)]
     _step("out-of-memory path")
     st = lib.lfm_moe_forward(*fake[:5], fake[5], N, None)
@@ -405,36 +471,91 @@ _STACK = {}
 
 
 def _stack_block(l):
+    """Oracle-side arrays and device weights of stack block l (one block at a
+    time: the previous block's are dropped)."""
     if l not in _STACK:
+        _STACK.clear()
         print(f"[case] generating stack block {l}", flush=True)
         p = synth.stack_block_params(synth.STACK["seed"], l)
         inp = dict(W_r=p["W_r"].float().numpy(), bias=p["bias"].numpy(),
                    W_gate=p["W_gate"].float().numpy(), W_up=p["W_up"].float().numpy(),
                    W_down=p["W_down"].float().numpy())
         dev = device_weights(p)
+        del p
         _STACK[l] = (inp, dev)
     return _STACK[l]
 
 
-def test_stack_blocks_teacher_forced(moe):
-    """Blocks 0..2 of the 38-block stack at N = 512: the oracle's own residual
-    stream x_l goes into the HIP block, whose x_{l+1} - x_l must match the
-    oracle's MoE output for that block."""
+class _StackRun:
+    """State carried from block to block: the oracle's residual stream, the
+    HIP stack's own (free-running) stream and per-token bookkeeping."""
+    next_block = 0
+    failed = False
+    x = None          # oracle x_l, float64 [N, 2048]
+    x_free = None     # the HIP stack's x_l from its own previous blocks (device)
+    near = None       # tokens with an oracle margin <= 1e-4 at some block
+    differs = None    # tokens whose HIP selection (free-running) differed from the oracle's at some block
+    worst = 0.0
+
+
+@pytest.mark.parametrize("l", range(synth.STACK["blocks"]))
+def test_stack_blocks_teacher_forced(moe, l):
+    """Block l of the 38-block stack at N = 512 (guide, section "The exact
+    checkpoint": normalise, feed-forward network, residual), teacher-forced:
+    the oracle's own residual stream x_l goes into the HIP block, whose
+    x_{l+1} - x_l must match the oracle's MoE output for that block to the
+    layer's bar.  Alongside, the HIP stack runs on its own stream from x_0;
+    after the last block its end-to-end drift from the oracle's x_38 is
+    reported, over the tokens that had no near tie (margin <= 1e-4) at any
+    block."""
+    from biased_sigmoid_top_amd import _lib
+    st = _StackRun
+    if st.failed or st.next_block != l:
+        pytest.skip("an earlier stack block failed or did not run")
+    st.failed = True
     N = synth.STACK["N"]
-    x = synth.stack_residual(N, synth.STACK["seed"]).numpy().astype(np.float64)
-    for l in range(3):
-        inp, dev = _stack_block(l)
-        X = oracle.block_input(x)
-        r = oracle.route(X, inp["W_r"], inp["bias"])
-        _step(f"block_forward block {l} N={N}")
-        x_dev = torch.from_numpy(x.astype(np.float32)).cuda()
-        x_in = x_dev.clone()
-        moe.block_forward(x_dev, dev["W_r"], dev["bias"], dev["W_gateup"], dev["W_down"])
-        delta = _np(x_dev).astype(np.float64) - _np(x_in).astype(np.float64)
-        # The HIP block normalises x itself: check its selection separately.
-        Xd = torch.from_numpy(X).to(torch.bfloat16).cuda()
-        idx, w = moe.route(Xd, dev["W_r"], dev["bias"])
-        alt = check_route(_np(idx), _np(w), r)
-        full = dict(inp, X=X)
-        check_out(delta, expected_outputs(full, r, np.arange(N), alt))
-        x = x + oracle.moe_apply(X, r.idx, r.w, inp["W_gate"], inp["W_up"], inp["W_down"]).out
+    if l == 0:
+        st.x = synth.stack_residual(N, synth.STACK["seed"]).numpy().astype(np.float64)
+        st.x_free = torch.from_numpy(st.x.astype(np.float32)).cuda()
+        st.near = np.zeros(N, dtype=bool)
+        st.differs = np.zeros(N, dtype=bool)
+        st.worst = 0.0
+    inp, dev = _stack_block(l)
+    X = oracle.block_input(st.x)
+    r = oracle.route(X, inp["W_r"], inp["bias"])
+    _step(f"block_forward block {l} N={N}")
+    x_dev = torch.from_numpy(st.x.astype(np.float32)).cuda()
+    x_in = x_dev.clone()
+    moe.block_forward(x_dev, dev["W_r"], dev["bias"], dev["W_gateup"], dev["W_down"])
+    delta = _np(x_dev).astype(np.float64) - _np(x_in).astype(np.float64)
+    # The HIP block normalises x itself: check its selection separately.
+    Xd = torch.from_numpy(X).to(torch.bfloat16).cuda()
+    idx, w = moe.route(Xd, dev["W_r"], dev["bias"])
+    alt = check_route(_np(idx), _np(w), r)
+    full = dict(inp, X=X)
+    ratio = check_out(delta, expected_outputs(full, r, np.arange(N), alt))
+    st.worst = max(st.worst, ratio)
+    # The HIP stack's own stream through this block.
+    ws = moe.alloc_workspace(N)
+    moe.block_forward(st.x_free, dev["W_r"], dev["bias"], dev["W_gateup"], dev["W_down"], workspace=ws)
+    sel_free = np.sort(_np(moe.workspace_view(ws, N, _lib.WS_IDX, torch.int32, (N, 4))), 1)
+    st.differs |= np.any(sel_free != np.sort(r.idx, 1), axis=1)
+    st.near |= r.margin <= 1e-4
+    st.x = st.x + oracle.moe_apply(X, r.idx, r.w, inp["W_gate"], inp["W_up"], inp["W_down"]).out
+    print(f"  teacher-forced max|err| / RMS = {ratio:.4f}", flush=True)
+    st.next_block = l + 1
+    st.failed = False
+    if l == synth.STACK["blocks"] - 1:
+        x0 = synth.stack_residual(N, synth.STACK["seed"]).numpy().astype(np.float64)
+        xf = _np(st.x_free).astype(np.float64)
+        assert np.all(np.isfinite(xf))
+        keep = ~st.near
+        moe_rms = float(np.sqrt(np.mean((st.x - x0)[keep] ** 2)))
+        err = np.abs(xf - st.x)[keep].max(axis=1)
+        print(f"  stack end to end over {int(keep.sum())} of {N} tokens (no near tie at any block): "
+              f"max|x_38(HIP) - x_38(oracle)| / RMS(sum of the 38 MoE outputs) = {err.max() / moe_rms:.4f}, "
+              f"median over tokens {np.median(err) / moe_rms:.4f}; tokens whose free-running selection "
+              f"differed from the oracle's at some block: {int(st.differs.sum())} "
+              f"({int((st.differs & keep).sum())} of them without an oracle near tie); "
+              f"worst teacher-forced block {st.worst:.4f}", flush=True)
+        assert np.median(err) / moe_rms < 2e-2
