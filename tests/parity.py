@@ -149,3 +149,45 @@ def oracle_fp8_experts(inp: dict, workers: int = 8) -> dict:
         q[name + "_scales"] = np.stack([s for _, s in qs])
     return q
 
+
+def fp8_output_check(out: np.ndarray, idx: np.ndarray, w: np.ndarray, H_gpu: np.ndarray,
+                     X: np.ndarray, q: dict) -> dict:
+    """Output parity of the FP8 layer for the GPU's selections idx and weights
+    w (slot order t * 4 + j everywhere).
+
+    The E4M3 codes of a hidden row are an integer decision taken from its
+    bf16 values, which come from fp32 sums on the GPU and from float64 on the
+    oracle; where the two round H to neighbouring bf16 values, a code can
+    land on the neighbouring E4M3 value (and a group maximum moves its whole
+    group's scale).  So the output is gated against the oracle's down step
+    and combine applied to the GPU's own H (both sides decide the codes from
+    the same values), within OUT_GATE * RMS; the fully independent oracle
+    result is also compared, and must pass the same gate whenever no code
+    differs.  Returns the ratios and the number of differing codes."""
+    from oracle import fp8
+    N = idx.shape[0]
+    flat = idx.reshape(-1)
+    xc, xs = fp8.quantize_groups(X)
+    Xq = fp8.dequantize_groups(xc, xs)
+    H_ref = np.zeros_like(H_gpu)
+    Y_same = np.zeros((4 * N, X.shape[1]))
+    for e in np.unique(flat):
+        rows = np.nonzero(flat == e)[0]
+        H_ref[rows] = fp8.expert_hidden_fp8(Xq[rows // 4], q, int(e))
+        Y_same[rows] = fp8.expert_down_fp8(H_gpu[rows], q, int(e))
+    out_same = (w[:, :, None] * Y_same.reshape(N, 4, -1)).sum(axis=1)
+    ref = fp8.moe_apply_fp8(X, idx, w, q).out
+    gc, gs = fp8.quantize_groups(H_gpu)
+    rc, rs = fp8.quantize_groups(H_ref)
+    code_flips = int(np.sum(gc != rc))
+    scale_flips = int(np.sum(gs != rs))
+    rms_same = float(np.sqrt(np.mean(out_same ** 2)))
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    res = dict(same_codes=float(np.max(np.abs(out - out_same))) / rms_same,
+               end_to_end=float(np.max(np.abs(out - ref))) / rms,
+               h_differs=int(np.sum(H_gpu != H_ref)), code_flips=code_flips, scale_flips=scale_flips)
+    assert np.all(np.isfinite(out)), "non-finite outputs"
+    assert res["same_codes"] <= OUT_GATE, res
+    if code_flips == 0 and scale_flips == 0:
+        assert res["end_to_end"] <= OUT_GATE, res
+    return res

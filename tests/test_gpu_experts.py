@@ -18,11 +18,10 @@ import torch
 import oracle
 import synth
 from conftest import cached_layer
-from parity import check_out, device_inputs, oracle_fp8_experts, oracle_inputs, sanitize_routing
+from parity import (check_out, device_inputs, fp8_output_check, oracle_fp8_experts, oracle_inputs,
+                    sanitize_routing)
 
 pytestmark = pytest.mark.gpu
-
-OUT_GATE_FP8 = 5e-2  # the FP8 layer's end-to-end bar (a hidden value's code can flip)
 
 _STATE = {}
 
@@ -116,8 +115,9 @@ def test_experts_on_the_oracle_routing(moe, N):
 
 @pytest.mark.parametrize("N", [64, 700])
 def test_experts_fp8_on_the_oracle_routing(moe, N):
-    """FP8 experts against oracle.fp8.moe_apply_fp8 on the oracle's routing."""
-    from oracle import fp8
+    """FP8 experts against oracle.fp8 on the oracle's routing (the bar of
+    parity.fp8_output_check)."""
+    from biased_sigmoid_top_amd import _lib
     inp, dev = _case(moe)
     if "q" not in _STATE:
         print("[fp8] oracle block quantisation of 64 x 3 expert matrices", flush=True)
@@ -129,13 +129,13 @@ def test_experts_fp8_on_the_oracle_routing(moe, N):
     idx = torch.from_numpy(np.ascontiguousarray(r.idx, dtype=np.int32)).cuda()
     w = torch.from_numpy(w32).cuda()
     _step(f"experts_fp8_ws on oracle routing N={N}")
-    out = _np(moe.experts_fp8(X, idx, w, dev["gateup_fp8"], dev["down_fp8"]))
-    expect = fp8.moe_apply_fp8(Xo, r.idx, w32.astype(np.float64), q).out
-    rms = float(np.sqrt(np.mean(expect ** 2)))
-    ratio = float(np.max(np.abs(out.astype(np.float64) - expect))) / rms
-    print(f"  max|err|/RMS {ratio:.4f} over all {N} tokens", flush=True)
-    assert np.all(np.isfinite(out))
-    assert ratio <= OUT_GATE_FP8, ratio
+    ws = moe.alloc_workspace(N)
+    out = _np(moe.experts_fp8(X, idx, w, dev["gateup_fp8"], dev["down_fp8"], workspace=ws)).astype(np.float64)
+    H = _np(moe.workspace_view(ws, N, _lib.WS_H, torch.bfloat16, (4 * N, 1536)).float()).astype(np.float64)
+    res = fp8_output_check(out, r.idx, w32.astype(np.float64), H, Xo, q)
+    print(f"  all {N} tokens: out vs FP8 oracle on the GPU's H {res['same_codes']:.2e}, end to end "
+          f"{res['end_to_end']:.4f} ({res['code_flips']} H codes and {res['scale_flips']} group scales differ)",
+          flush=True)
 
 
 @pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
