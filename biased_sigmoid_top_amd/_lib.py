@@ -25,6 +25,8 @@ ERR_HIP = 4
 DECODE_MAX_TOKENS = 96
 FP8_MAX_TOKENS = 1 << 24
 FP8_STREAM_TOKENS = 256
+NOALLOC_MAX_TOKENS = 256
+NOALLOC_SCRATCH_BYTES = 14 << 20
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -46,6 +48,7 @@ SIGNATURES = {
     "lfm_moe_workspace_bytes": (_SZ, [_I64]),
     "lfm_moe_workspace_offset": (_SZ, [_I64, ctypes.c_int]),
     "lfm_moe_forward_ws": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _P, _SZ, _P]),
+    "lfm_moe_forward_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _P]),
     "lfm_moe_experts_ws": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _P, _SZ, _P]),
     "lfm_moe_block_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _P]),
     "lfm_moe_block_forward_ws": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _P, _SZ, _P]),

@@ -184,6 +184,32 @@ lfm_moe_status internal_ws(int64_t N, void** ws, size_t* bytes) {
   return internal_ws(kLayerWs, workspace_bytes(N), ws, bytes);
 }
 
+// Workspace of lfm_moe_forward_noalloc: a static device array, one per GPU,
+// held until the process ends.  In host code its name is only a stand-in
+// for the symbol; the kernels get its device address, looked up once per
+// device with hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[LFM_MOE_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+lfm_moe_status scratch_address(void** p) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "device ordinal out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr) return fail(LFM_MOE_ERR_HIP, "hipGetSymbolAddress(scratch) gave no address");
+    g_scratch[dev] = ptr;
+  }
+  *p = g_scratch[dev];
+  return LFM_MOE_OK;
+}
+
 // Per-kernel timing for measurements (lfm_moe_timing_*).
 constexpr int kStages = LFM_MOE_STAGES;
 constexpr int kMaxMarks = kStages + 1;
@@ -695,6 +721,27 @@ lfm_moe_status lfm_moe_forward(const uint16_t* X, const uint16_t* W_r, const flo
   void* ws = nullptr;
   size_t bytes = 0;
   if ((st = internal_ws(N, &ws, &bytes)) != LFM_MOE_OK) return st;
+  StageTimer timer(stream);
+  return run_layer(X, W_r, bias, nullptr, nullptr, W_gateup, W_down, nullptr, out, N, ws, stream, timer);
+}
+
+lfm_moe_status lfm_moe_forward_noalloc(const uint16_t* X, const uint16_t* W_r, const float* bias,
+                                       const uint16_t* W_gateup, const uint16_t* W_down, float* out,
+                                       int64_t N, hipStream_t stream) {
+  g_last_error.clear();
+  lfm_moe_status st = check_layer_args(X, act_bytes(N, 2), W_r, bias, W_gateup, W_down, out,
+                                       act_bytes(N, 4), N, false);
+  if (st != LFM_MOE_OK || N == 0) return st;
+  if (N > LFM_MOE_NOALLOC_MAX_TOKENS)
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT,
+                "N = " + std::to_string(N) + " exceeds LFM_MOE_NOALLOC_MAX_TOKENS (" +
+                    std::to_string(LFM_MOE_NOALLOC_MAX_TOKENS) + "); use lfm_moe_forward_ws");
+  if (workspace_bytes(N) > sizeof(scratch))
+    return fail(LFM_MOE_ERR_WORKSPACE_TOO_SMALL,
+                "the static workspace holds " + std::to_string(sizeof(scratch)) + " bytes, N = " +
+                    std::to_string(N) + " needs " + std::to_string(workspace_bytes(N)));
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != LFM_MOE_OK) return st;
   StageTimer timer(stream);
   return run_layer(X, W_r, bias, nullptr, nullptr, W_gateup, W_down, nullptr, out, N, ws, stream, timer);
 }

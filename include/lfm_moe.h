@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define LFM_MOE_ABI_VERSION 5
+#define LFM_MOE_ABI_VERSION 6
 #define LFM_MOE_HIDDEN 2048
 #define LFM_MOE_EXPERTS 64
 #define LFM_MOE_TOPK 4
@@ -327,6 +327,27 @@ lfm_moe_status lfm_moe_experts_fp8_ws(const uint16_t* X, const int32_t* idx, con
                                       const uint8_t* W_gateup_fp8, const float* scales_gateup,
                                       const uint8_t* W_down_fp8, const float* scales_down, float* out,
                                       int64_t N, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * lfm_moe_forward that allocates nothing, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc.  Same arguments, kernels and result (bit
+ * for bit) as lfm_moe_forward, for 0 <= N <= LFM_MOE_NOALLOC_MAX_TOKENS; a
+ * larger N returns LFM_MOE_ERR_INVALID_ARGUMENT before any HIP call.  Its
+ * workspace is a static device array of LFM_MOE_NOALLOC_SCRATCH_BYTES bytes
+ * that every GPU the library runs on holds until the process ends; no call
+ * makes hipMalloc, hipFree or any other allocation (the array's device
+ * address is looked up once per device, at the first call on it).  Every
+ * call on one GPU uses that GPU's one array and leaves the last call's
+ * intermediates in it, so calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race and give wrong
+ * results: serialise them, or use lfm_moe_forward_ws.
+ */
+#define LFM_MOE_NOALLOC_MAX_TOKENS 256
+#define LFM_MOE_NOALLOC_SCRATCH_BYTES (14u << 20)
+lfm_moe_status lfm_moe_forward_noalloc(const uint16_t* X, const uint16_t* W_r, const float* bias,
+                                       const uint16_t* W_gateup, const uint16_t* W_down,
+                                       float* out, int64_t N, hipStream_t stream);
 
 /* Frees the library-owned workspaces, the layer's and the router's (call with no work of
  * this library in flight). */

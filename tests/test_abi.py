@@ -153,6 +153,30 @@ def test_route_ws_checks(lib):
         assert f(*c, 4096, None, 0, None) == _lib.ERR_INVALID_ARGUMENT
 
 
+def test_noalloc_forward_checks(lib):
+    """lfm_moe_forward_noalloc rejects a batch past its static workspace
+    before any HIP call, checks its tensors like lfm_moe_forward, and its
+    array holds the workspace of the largest batch it takes."""
+    a = [_addr(i) for i in range(6)]
+    f = lib.lfm_moe_forward_noalloc
+    assert lib.lfm_moe_workspace_bytes(_lib.NOALLOC_MAX_TOKENS) <= _lib.NOALLOC_SCRATCH_BYTES
+    assert f(*a, 0, None) == _lib.OK
+    assert f(*a, _lib.NOALLOC_MAX_TOKENS + 1, None) == _lib.ERR_INVALID_ARGUMENT
+    assert b"NOALLOC_MAX_TOKENS" in lib.lfm_moe_last_error()
+    assert f(*a, -1, None) == _lib.ERR_INVALID_ARGUMENT
+    for i in range(6):
+        b = list(a)
+        b[i] = None
+        assert f(*b, 8, None) == _lib.ERR_INVALID_ARGUMENT
+    b = list(a)
+    b[5] = a[0] + 1024
+    assert f(*b, 8, None) == _lib.ERR_INVALID_ARGUMENT
+    with open(_lib.HEADER) as fh:
+        text = fh.read()
+    assert f"#define LFM_MOE_NOALLOC_MAX_TOKENS {_lib.NOALLOC_MAX_TOKENS}" in text
+    assert "#define LFM_MOE_NOALLOC_SCRATCH_BYTES (14u << 20)" in text
+
+
 def test_pack_checks(lib):
     a = [_addr(i) for i in range(3)]
     assert lib.lfm_moe_pack_gateup(a[0], None, a[2], None) == _lib.ERR_INVALID_ARGUMENT
