@@ -245,12 +245,12 @@ def summarize_fp8(p, wall_ms, per_kernel, label, note):
     if hbm:
         roof = dict(bound="hbm", kernel=kernel, achieved=gu_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=gu_gbs / HBM_PEAK_GBS, traffic=measured_traffic(p["name"], "gateup_fp8"),
-                    bytes_per_launch=fp8_gateup_bytes(A, N), avg_launch_ms=gu_ms,
+                    bytes_per_launch=fp8_gateup_bytes(A, N), avg_launch_ms=gu_ms, timing=EVENT_TIMING,
                     down_gbs=fp8_down_bytes(A, N) / (dn_ms * 1e-3) / 1e9)
     else:
         roof = dict(bound="mfma", kernel=kernel, achieved=gu_tflops, peak=BF16_PEAK_TFLOPS,
                     unit="TFLOP/s", frac=gu_tflops / BF16_PEAK_TFLOPS, traffic=None,
-                    flops_per_launch=gateup_flops(N), avg_launch_ms=gu_ms)
+                    flops_per_launch=gateup_flops(N), avg_launch_ms=gu_ms, timing=EVENT_TIMING)
     return dict(config=label, N=N, dtype="fp8-e4m3 experts (bf16 router, fp32 accumulation)",
                 active_experts=A, max_tokens_per_expert=max(p["counts"]), ms_per_step=wall_ms,
                 tokens_per_s=N / s, gbs=gbs, hbm_frac=gbs / HBM_PEAK_GBS, tflops=tflops,
@@ -306,11 +306,18 @@ def roofline(h, workload):
         return dict(bound="hbm", kernel=kernel, achieved=h["gateup_gbs"],
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=h["gateup_gbs"] / HBM_PEAK_GBS,
                     traffic=measured_traffic(workload), bytes_per_launch=gateup_bytes(A, N),
-                    avg_launch_ms=ms)
+                    avg_launch_ms=ms, timing=EVENT_TIMING)
     return dict(bound="mfma", kernel="gateup_tiled", achieved=h["gateup_tflops"],
                 peak=BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=h["gateup_tflops"] / BF16_PEAK_TFLOPS,
                 traffic=measured_traffic(workload), flops_per_launch=gateup_flops(N),
-                avg_launch_ms=ms)
+                avg_launch_ms=ms, timing=EVENT_TIMING)
+
+
+# How avg_launch_ms is measured (stated in every roofline object).
+EVENT_TIMING = ("hipEvents recorded by the library on the launch stream before the layer's first "
+                "kernel and after each kernel, over a second pass of the timed steps: a kernel's "
+                "interval includes the dispatch gap before it (about 1-4 us), so it reads a little "
+                "above the kernel-only duration in the rocprofv3 traces under profiles/")
 
 
 def cpu_baseline(p, budget_s):
@@ -375,74 +382,6 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": n, "copies": 3}))
 
 
-def vendor_gemm(steps=20, warmup=5):
-    """Context, not the product: the vendor BLAS (torch.bmm / torch.matmul on
-    ROCm) on uniform shapes with the FLOPs of the 4,096-token expert GEMMs --
-    64 experts x 256 rows, and the same rows against one dense weight matrix.
-    Nothing here touches the layer's kernels."""
-    import torch
-    g = torch.Generator(device="cuda")
-    g.manual_seed(0)
-    out = {}
-
-    def timed(fn):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        for _ in range(steps):
-            fn()
-        e.record()
-        torch.cuda.synchronize()
-        return s.elapsed_time(e) / steps * 1e3
-
-    for name, (n_out, k) in {"gateup": (2 * FF, D), "down": (D, FF)}.items():
-        a = torch.randn(E, 256, k, device="cuda", dtype=torch.bfloat16, generator=g)
-        # Right operands materialised as [E, K, n_out] (contiguous, never a transposed view).
-        b = torch.randn(E, k, n_out, device="cuda", dtype=torch.bfloat16, generator=g)
-        flop = 2 * E * 256 * n_out * k
-        us = timed(lambda: torch.bmm(a, b))
-        out[f"{name}_bmm_64x256"] = {"us": round(us, 1), "tflops": round(flop / us / 1e6, 1)}
-        a2, b2 = a.reshape(E * 256, k), b[0].contiguous()
-        us = timed(lambda: torch.matmul(a2, b2))
-        out[f"{name}_dense_16384"] = {"us": round(us, 1), "tflops": round(flop / us / 1e6, 1)}
-        del a, b, a2, b2
-
-    # This library's expert kernels on the same uniform shape: 4,096 tokens
-    # routed so that every expert gets exactly 256 slots (token t takes
-    # experts 4t .. 4t + 3 modulo 64), through lfm_moe_experts_ws, per-kernel
-    # times from the library's stage events.
-    import biased_sigmoid_top_amd as moe
-    N = 4096
-    Wg = (0.02 * torch.randn(E, FF, D, device="cuda", generator=g)).to(torch.bfloat16)
-    Wu = (0.02 * torch.randn(E, FF, D, device="cuda", generator=g)).to(torch.bfloat16)
-    Wd = (0.02 * torch.randn(E, D, FF, device="cuda", generator=g)).to(torch.bfloat16)
-    Wgu, Wdp = moe.pack_gateup(Wg, Wu), moe.pack_down(Wd)
-    del Wg, Wu, Wd
-    X = torch.randn(N, D, device="cuda", generator=g).to(torch.bfloat16)
-    t = torch.arange(N, device="cuda", dtype=torch.int32)
-    idx = ((4 * t[:, None] + torch.arange(4, device="cuda", dtype=torch.int32)) % E).contiguous()
-    w = torch.full((N, 4), 0.25, device="cuda")
-    res = torch.empty(N, D, device="cuda")
-    ws = moe.alloc_workspace(N)
-    for _ in range(warmup):
-        moe.experts(X, idx, w, Wgu, Wdp, out=res, workspace=ws)
-    torch.cuda.synchronize()
-    moe.timing_enable(True)
-    for _ in range(steps):
-        moe.experts(X, idx, w, Wgu, Wdp, out=res, workspace=ws)
-    torch.cuda.synchronize()
-    st = moe.timing_read()
-    moe.timing_enable(False)
-    for name, n_out, k in (("gateup", 2 * FF, D), ("down", D, FF)):
-        ms, n = st[name]
-        us = ms / max(n, 1) * 1e3
-        flop = 2 * E * 256 * n_out * k
-        out[f"{name}_ours_uniform_64x256"] = {"us": round(us, 1), "tflops": round(flop / us / 1e6, 1)}
-    print(json.dumps({"vendor_gemm": out, "steps": steps, "dtype": "bf16"}))
-
-
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -454,8 +393,8 @@ def parse_args(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the oracle baseline (0 leaves it out)")
     ap.add_argument("--copy-probe", action="store_true", help="only run a plain 1 GiB copy")
-    ap.add_argument("--vendor-gemm", action="store_true",
-                    help="only time the vendor BLAS on uniform shapes with the FLOPs of the 4,096-token expert GEMMs")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="leave out the skewed 16,384-token layer and the 38-block stack (measured by default)")
     ap.add_argument("--workload", default="decode_n64", help="headline workload")
     ap.add_argument("--configs", action="store_true",
                     help="also measure every configuration (C0-C4, the 38-block stack included; "
@@ -477,9 +416,6 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
-        return
-    if args.vendor_gemm:
-        vendor_gemm()
         return
 
     import biased_sigmoid_top_amd  # noqa: F401  (fails loudly without the built library)
@@ -517,9 +453,22 @@ def main():
     line = build_line(args, h, head["seed"], second, cpu)
     line["fp8"] = fp8
     line["device"] = dev_info
-    if args.configs:
-        del head
+    del head
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        p3 = prepare("skewed_n16384", args.copies)
+        steps3 = max(5, args.steps // 10)
+        log(f"timing skewed_n16384: {steps3} steps")
+        w3, k3 = time_steps(p3, steps3, max(2, args.warmup // 10))
+        s3 = summarize(p3, w3, k3)
+        line["skewed"] = dict(config_entry("C3", s3), workload="skewed_n16384",
+                              roofline=roofline(s3, "skewed_n16384"))
+        log(json.dumps(line["skewed"]))
+        del p3
         torch.cuda.empty_cache()
+        line["stack"] = measure_stack(max(3, args.steps // 4), 1)
+        log(json.dumps(line["stack"]))
+    if args.configs:
         line["configs"] = measure_configs(args)
     print(json.dumps(line), flush=True)
 
@@ -652,6 +601,19 @@ def measure_stack(steps, warmup):
     ms_graph = (time.perf_counter() - t0) * 1e3 / steps
     assert torch.equal(x, eager_x), "graph replay differs from the eager stack"
     del graph
+    # Per-kernel times of the blocks (library events), for the roofline of
+    # the dominant kernel: gate/up, HBM-bound at 512 tokens.
+    moe.timing_enable(True)
+    stack_pass()
+    torch.cuda.synchronize()
+    st_ms = moe.timing_read()
+    moe.timing_enable(False)
+    kernel_ms = {k: (v / n if n else 0.0) for k, (v, n) in st_ms.items()}
+    gu_bytes = sum(gateup_bytes(a, N) for a in active) / nb
+    gu_ms = kernel_ms["gateup"]
+    roof = dict(bound="hbm", kernel="gateup_tiled", achieved=gu_bytes / (gu_ms * 1e-3) / 1e9,
+                peak=HBM_PEAK_GBS, unit="GB/s", frac=gu_bytes / (gu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                traffic=None, bytes_per_launch=gu_bytes, avg_launch_ms=gu_ms, timing=EVENT_TIMING)
     bytes_ = sum(a * EXPERT_BYTES + ROUTER_BYTES for a in active) + nb * N * D * 4 * 2
     flops = nb * N * FLOP_PER_TOKEN
     s = ms * 1e-3
@@ -662,6 +624,7 @@ def measure_stack(steps, warmup):
              mfma_frac=flops / s / 1e12 / BF16_PEAK_TFLOPS, bound="hbm",
              roofline_frac=bytes_ / s / 1e9 / HBM_PEAK_GBS,
              ms_per_step_graph=ms_graph, tokens_per_s_graph=N / (ms_graph * 1e-3),
+             kernel_ms=kernel_ms, roofline=roof,
              note="one step = the whole stack (a copy of x0, then 38 block calls); "
                   "the _graph figures replay the same step captured in one HIP graph")
     del blocks
