@@ -566,8 +566,7 @@ def measure_stack(steps, warmup):
 
     def stack_pass():
         x.copy_(x0)
-        for blk in blocks:
-            moe.block_forward(x, *blk, workspace=ws)
+        moe.stack_forward(x, blocks, workspace=ws)
 
     for _ in range(warmup):
         stack_pass()
@@ -625,8 +624,10 @@ def measure_stack(steps, warmup):
              roofline_frac=bytes_ / s / 1e9 / HBM_PEAK_GBS,
              ms_per_step_graph=ms_graph, tokens_per_s_graph=N / (ms_graph * 1e-3),
              kernel_ms=kernel_ms, roofline=roof,
-             note="one step = the whole stack (a copy of x0, then 38 block calls); "
-                  "the _graph figures replay the same step captured in one HIP graph")
+             note="one step = the whole stack (a copy of x0, then one lfm_moe_stack_forward_ws call "
+                  "over the 38 blocks: one normalisation launch, the later blocks' inputs normalised by "
+                  "the previous block's combine); the _graph figures replay the same step captured in "
+                  "one HIP graph")
     del blocks
     torch.cuda.empty_cache()
     return e

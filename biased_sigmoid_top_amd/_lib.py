@@ -52,6 +52,7 @@ SIGNATURES = {
     "lfm_moe_experts_ws": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _P, _SZ, _P]),
     "lfm_moe_block_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _P]),
     "lfm_moe_block_forward_ws": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _P, _SZ, _P]),
+    "lfm_moe_stack_forward_ws": (ctypes.c_int, [_P, _P, ctypes.c_int, _I64, _P, _SZ, _P]),
     "lfm_moe_pack_fp8_gateup": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "lfm_moe_pack_fp8_down": (ctypes.c_int, [_P, _P, _P, _P]),
     "lfm_moe_forward_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _P]),
@@ -61,6 +62,11 @@ SIGNATURES = {
     "lfm_moe_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "lfm_moe_timing_read": (ctypes.c_int, [_P, _P]),
 }
+
+class BlockWeights(ctypes.Structure):
+    """lfm_moe_block_weights: one block's device weight pointers."""
+    _fields_ = [("W_r", _P), ("bias", _P), ("W_gateup", _P), ("W_down", _P)]
+
 
 STAGES = ("rmsnorm", "route", "dispatch", "gateup", "down", "combine")
 

@@ -277,6 +277,23 @@ def block_forward(x, W_r, bias, W_gateup, W_down, workspace=None, stream=None):
     return x
 
 
+def stack_forward(x, blocks, workspace=None, stream=None):
+    """x <- x + MoE_l(bf16(RMSNorm(x))) for each (W_r, bias, W_gateup, W_down)
+    of ``blocks`` in order, in place; returns x.  Without ``workspace`` one of
+    workspace_bytes(N) is allocated for the call."""
+    import ctypes
+    N = x.shape[0]
+    px = _req(x, "x", torch.float32, (N, HIDDEN))
+    arr = (_lib.BlockWeights * max(1, len(blocks)))()
+    for i, blk in enumerate(blocks):
+        arr[i] = _lib.BlockWeights(*_weights(*blk))
+    if workspace is None:
+        workspace = alloc_workspace(N, device=x.device)
+    _lib.call("lfm_moe_stack_forward_ws", px, ctypes.addressof(arr), len(blocks), N, workspace.data_ptr(),
+              workspace.numel() * workspace.element_size(), _stream(stream))
+    return x
+
+
 def release() -> None:
     _lib.load().lfm_moe_release()
 

@@ -311,10 +311,13 @@ hipError_t route_or_ingest(const uint16_t* X, const uint16_t* W_r, const float* 
 
 // route -> [dispatch] -> gate/up -> down -> combine.  Arguments already
 // checked.  With idx_in and w_in the router is replaced by a copy of them.
+// With X_next (then resid == out) the combine also stores the next block's
+// input bf16(RMSNorm(out)) there.
 lfm_moe_status run_layer(const uint16_t* X, const uint16_t* W_r, const float* bias,
                          const int32_t* idx_in, const float* w_in,
                          const uint16_t* W_gateup, const uint16_t* W_down, const float* resid,
-                         float* out, int64_t N, void* ws, hipStream_t stream, StageTimer& timer) {
+                         float* out, int64_t N, void* ws, hipStream_t stream, StageTimer& timer,
+                         uint16_t* X_next = nullptr) {
   int32_t* idx = region<int32_t>(ws, N, LFM_MOE_WS_IDX);
   float* w = region<float>(ws, N, LFM_MOE_WS_W);
   int32_t* blockcounts = region<int32_t>(ws, N, LFM_MOE_WS_BLOCKCOUNTS);
@@ -348,8 +351,9 @@ lfm_moe_status run_layer(const uint16_t* X, const uint16_t* W_r, const float* bi
       return hip_fail(e, "down kernel launch");
     timer.after(4);
   }
-  if ((e = launch_combine(Y, w, resid, out, N, stream)) != hipSuccess)
-    return hip_fail(e, "combine kernel launch");
+  e = X_next != nullptr ? launch_combine_norm(Y, w, out, X_next, N, stream)
+                       : launch_combine(Y, w, resid, out, N, stream);
+  if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   timer.after(5);
   return LFM_MOE_OK;
 }
@@ -778,6 +782,38 @@ lfm_moe_status lfm_moe_block_forward_ws(float* x_inout, const uint16_t* W_r, con
   if (e != hipSuccess) return hip_fail(e, "rmsnorm kernel launch");
   timer.after(0);
   return run_layer(X, W_r, bias, nullptr, nullptr, W_gateup, W_down, x_inout, x_inout, N, ws, stream, timer);
+}
+
+lfm_moe_status lfm_moe_stack_forward_ws(float* x_inout, const lfm_moe_block_weights* blocks, int n_blocks,
+                                        int64_t N, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  if (n_blocks < 0) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "n_blocks must be >= 0");
+  if (n_blocks > 0 && blocks == nullptr) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "null block array");
+  // Every block's arguments are checked before anything is launched.
+  lfm_moe_status st = LFM_MOE_OK;
+  for (int l = 0; l < n_blocks && st == LFM_MOE_OK; ++l) {
+    const lfm_moe_block_weights& b = blocks[l];
+    st = check_layer_args(x_inout, act_bytes(N, 4), b.W_r, b.bias, b.W_gateup, b.W_down, x_inout,
+                          act_bytes(N, 4), N, true);
+    if (st == LFM_MOE_OK && N > 0)
+      st = check_ws(ws, ws_bytes, N, Span{x_inout, act_bytes(N, 4)},
+                    {router_span(b.W_r), bias_span(b.bias), gateup_span(b.W_gateup), down_span(b.W_down)});
+  }
+  if (st != LFM_MOE_OK || N == 0 || n_blocks == 0) return st;
+  uint16_t* X = region<uint16_t>(ws, N, LFM_MOE_WS_X);
+  hipError_t e;
+  for (int l = 0; l < n_blocks; ++l) {
+    StageTimer timer(stream);
+    if (l == 0) {
+      if ((e = launch_rmsnorm(x_inout, X, N, stream)) != hipSuccess) return hip_fail(e, "rmsnorm kernel launch");
+      timer.after(0);
+    }
+    const lfm_moe_block_weights& b = blocks[l];
+    if ((st = run_layer(X, b.W_r, b.bias, nullptr, nullptr, b.W_gateup, b.W_down, x_inout, x_inout, N, ws,
+                        stream, timer, l + 1 < n_blocks ? X : nullptr)) != LFM_MOE_OK)
+      return st;
+  }
+  return LFM_MOE_OK;
 }
 
 lfm_moe_status lfm_moe_block_forward(float* x_inout, const uint16_t* W_r, const float* bias,

@@ -10,7 +10,11 @@
 //
 // The combine reads the four expert rows of a token (stored in slot order)
 // and accumulates them in the fixed order j = 0..3 in fp32 (no atomics), so
-// the result is the same on every run.
+// the result is the same on every run.  In a stack of blocks the combine of
+// block l also normalises the row it has just formed and stores the bf16
+// input of block l + 1 (combine_norm_kernel), so no separate normalisation
+// launch runs between blocks; it takes the same steps as rmsnorm_kernel
+// over the same values, so the two give the same bits.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -20,12 +24,10 @@ namespace {
 
 constexpr int kRowThreads = 256;  // one token row of 2048 values per workgroup
 
-// out[t] = (resid[t] +) sum_j w[t, j] * Y[t*4 + j]; resid may alias out.
-// Y rows are in slot order, so a token's four rows are contiguous.
-__global__ __launch_bounds__(kRowThreads) void combine_kernel(const float* __restrict__ Y,
-                                                              const float* __restrict__ w,
-                                                              const float* resid, float* out) {
-  const size_t t = blockIdx.x;
+// Thread `tid`'s part of row t: sum_j w[t, j] * Y[t*4 + j] (+ resid[t]) over
+// columns (h * kRowThreads + tid) * 4 .. + 3, h = 0, 1.
+__device__ __forceinline__ void combine_row(const float* __restrict__ Y, const float* __restrict__ w,
+                                            const float* resid, size_t t, float4 (&v)[2]) {
   const float4 wt = *reinterpret_cast<const float4*>(w + t * kTopK);
   const float* y0 = Y + t * kTopK * kHidden;
   const float* y1 = y0 + kHidden;
@@ -43,7 +45,6 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(const float* __res
     acc.y = fmaf(wt.w, d.y, fmaf(wt.z, c.y, fmaf(wt.y, b.y, wt.x * a.y)));
     acc.z = fmaf(wt.w, d.z, fmaf(wt.z, c.z, fmaf(wt.y, b.z, wt.x * a.z)));
     acc.w = fmaf(wt.w, d.w, fmaf(wt.z, c.w, fmaf(wt.y, b.w, wt.x * a.w)));
-    float* dst = out + t * kHidden + col;
     if (resid != nullptr) {
       const float4 x = *reinterpret_cast<const float4*>(resid + t * kHidden + col);
       acc.x = x.x + acc.x;
@@ -51,21 +52,19 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(const float* __res
       acc.z = x.z + acc.z;
       acc.w = x.w + acc.w;
     }
-    *reinterpret_cast<float4*>(dst) = acc;
+    v[h] = acc;
   }
 }
 
-// X[t] = bf16(x[t] / sqrt(mean(x[t]^2) + eps)), unit weight.
-__global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const float* __restrict__ x,
-                                                              uint16_t* __restrict__ X) {
-  __shared__ float wave_ss[kRowThreads / kWave];
-  const size_t t = blockIdx.x;
-  const float* row = x + t * kHidden;
-  float4 v[2];
+// X[t] = bf16(v / sqrt(mean(v^2) + eps)) (unit weight) for the row whose
+// columns (h * kRowThreads + tid) * 4 .. + 3 thread tid holds in v[h]; the
+// sum of squares in a fixed order (per thread, then the wavefront's
+// butterfly, then the four wavefronts in pairs).
+__device__ __forceinline__ void norm_row(const float4 (&v)[2], size_t t, float* wave_ss,
+                                         uint16_t* __restrict__ X) {
   float ss = 0.0f;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    v[h] = *reinterpret_cast<const float4*>(row + (h * kRowThreads + threadIdx.x) * 4);
     ss = fmaf(v[h].x, v[h].x, ss);
     ss = fmaf(v[h].y, v[h].y, ss);
     ss = fmaf(v[h].z, v[h].z, ss);
@@ -86,11 +85,57 @@ __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const float* __res
   }
 }
 
+__device__ __forceinline__ void store_row(const float4 (&v)[2], size_t t, float* out) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    *reinterpret_cast<float4*>(out + t * kHidden + (h * kRowThreads + threadIdx.x) * 4) = v[h];
+}
+
+// out[t] = (resid[t] +) sum_j w[t, j] * Y[t*4 + j]; resid may alias out.
+// Y rows are in slot order, so a token's four rows are contiguous.
+__global__ __launch_bounds__(kRowThreads) void combine_kernel(const float* __restrict__ Y,
+                                                              const float* __restrict__ w,
+                                                              const float* resid, float* out) {
+  float4 v[2];
+  combine_row(Y, w, resid, blockIdx.x, v);
+  store_row(v, blockIdx.x, out);
+}
+
+// The same with the residual (x <- x + sum_j ...), then the next block's
+// input Xn[t] = bf16(RMSNorm(x[t])) from the new row.
+__global__ __launch_bounds__(kRowThreads) void combine_norm_kernel(const float* __restrict__ Y,
+                                                                   const float* __restrict__ w, float* x,
+                                                                   uint16_t* __restrict__ Xn) {
+  __shared__ float wave_ss[kRowThreads / kWave];
+  float4 v[2];
+  combine_row(Y, w, x, blockIdx.x, v);
+  store_row(v, blockIdx.x, x);
+  norm_row(v, blockIdx.x, wave_ss, Xn);
+}
+
+// X[t] = bf16(x[t] / sqrt(mean(x[t]^2) + eps)), unit weight.
+__global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const float* __restrict__ x,
+                                                              uint16_t* __restrict__ X) {
+  __shared__ float wave_ss[kRowThreads / kWave];
+  const size_t t = blockIdx.x;
+  const float* row = x + t * kHidden;
+  float4 v[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) v[h] = *reinterpret_cast<const float4*>(row + (h * kRowThreads + threadIdx.x) * 4);
+  norm_row(v, t, wave_ss, X);
+}
+
 }  // namespace
 
 hipError_t launch_combine(const float* Y, const float* w, const float* resid, float* out,
                           int64_t N, hipStream_t stream) {
   hipLaunchKernelGGL(combine_kernel, dim3(N), dim3(kRowThreads), 0, stream, Y, w, resid, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_norm(const float* Y, const float* w, float* x, uint16_t* Xn, int64_t N,
+                               hipStream_t stream) {
+  hipLaunchKernelGGL(combine_norm_kernel, dim3(N), dim3(kRowThreads), 0, stream, Y, w, x, Xn);
   return hipGetLastError();
 }
 

@@ -73,5 +73,9 @@ hipError_t launch_down_tiled(const uint16_t* H, const uint16_t* Wd, const int32_
 
 hipError_t launch_combine(const float* Y, const float* w, const float* resid, float* out,
                           int64_t N, hipStream_t stream);
+// x <- x + sum_j w Y (as launch_combine with resid = out = x), then
+// Xn = bf16(RMSNorm(x)) of the new rows, bit for bit launch_rmsnorm's.
+hipError_t launch_combine_norm(const float* Y, const float* w, float* x, uint16_t* Xn, int64_t N,
+                               hipStream_t stream);
 
 }  // namespace lfm

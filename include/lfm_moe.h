@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define LFM_MOE_ABI_VERSION 6
+#define LFM_MOE_ABI_VERSION 7
 #define LFM_MOE_HIDDEN 2048
 #define LFM_MOE_EXPERTS 64
 #define LFM_MOE_TOPK 4
@@ -254,6 +254,30 @@ lfm_moe_status lfm_moe_block_forward(float* x_inout, const uint16_t* W_r, const 
                                      int64_t N, hipStream_t stream);
 lfm_moe_status lfm_moe_block_forward_ws(float* x_inout, const uint16_t* W_r, const float* bias,
                                         const uint16_t* W_gateup, const uint16_t* W_down,
+                                        int64_t N, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * A stack of MoE blocks (guide, section "The exact checkpoint": every block
+ * normalises, applies its feed-forward network and adds the residual):
+ *   for l = 0 .. n_blocks - 1:
+ *     x_inout[t] <- x_inout[t] + MoE_l(bf16(RMSNorm(x_inout[t])))
+ * blocks: host array of n_blocks entries, block l's device weights (each as
+ * for lfm_moe_block_forward; blocks may share weights); read during the
+ * call only.  x_inout, N, ws, ws_bytes, stream as for
+ * lfm_moe_block_forward_ws.  The result equals n_blocks calls of
+ * lfm_moe_block_forward_ws bit for bit, with one launch fewer per block
+ * after the first: the combine of block l stores block l + 1's normalised
+ * input itself.  Every block's arguments are checked before anything is
+ * launched.  n_blocks == 0 or N == 0 is a no-op.
+ */
+typedef struct lfm_moe_block_weights {
+  const uint16_t* W_r;       /* [64, 2048] bf16 */
+  const float* bias;         /* [64] fp32 */
+  const uint16_t* W_gateup;  /* lfm_moe_pack_gateup / _stacked output */
+  const uint16_t* W_down;    /* lfm_moe_pack_down output */
+} lfm_moe_block_weights;
+
+lfm_moe_status lfm_moe_stack_forward_ws(float* x_inout, const lfm_moe_block_weights* blocks, int n_blocks,
                                         int64_t N, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*

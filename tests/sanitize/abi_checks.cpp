@@ -69,6 +69,15 @@ int main() {
   EXPECT(lfm_moe_block_forward(x, Wr, b, Wgu, Wd, 0, nullptr) == LFM_MOE_OK);
   EXPECT(lfm_moe_block_forward(nullptr, Wr, b, Wgu, Wd, N, nullptr) == LFM_MOE_ERR_INVALID_ARGUMENT);
   EXPECT(lfm_moe_block_forward_ws(x, Wr, b, Wgu, Wd, N, ws, 0, nullptr) == LFM_MOE_ERR_WORKSPACE_TOO_SMALL);
+  {
+    const lfm_moe_block_weights blocks[2] = {{Wr, b, Wgu, Wd}, {Wr, b, Wgu, nullptr}};
+    EXPECT(lfm_moe_stack_forward_ws(x, blocks, 2, N, ws, need, nullptr) == LFM_MOE_ERR_INVALID_ARGUMENT);
+    EXPECT(lfm_moe_stack_forward_ws(x, blocks, -1, N, ws, need, nullptr) == LFM_MOE_ERR_INVALID_ARGUMENT);
+    EXPECT(lfm_moe_stack_forward_ws(x, nullptr, 1, N, ws, need, nullptr) == LFM_MOE_ERR_INVALID_ARGUMENT);
+    EXPECT(lfm_moe_stack_forward_ws(x, blocks, 1, N, ws, 0, nullptr) == LFM_MOE_ERR_WORKSPACE_TOO_SMALL);
+    EXPECT(lfm_moe_stack_forward_ws(x, blocks, 2, 0, nullptr, 0, nullptr) == LFM_MOE_OK);
+    EXPECT(lfm_moe_stack_forward_ws(x, blocks, 0, N, ws, need, nullptr) == LFM_MOE_OK);
+  }
   EXPECT(lfm_moe_route(X, Wr, b, fake<int32_t>(8), fake<float>(8, 64), N, nullptr) == LFM_MOE_ERR_INVALID_ARGUMENT);
   EXPECT(lfm_moe_route(X, Wr, b, nullptr, fake<float>(9), N, nullptr) == LFM_MOE_ERR_INVALID_ARGUMENT);
   EXPECT(lfm_moe_route(X, Wr, b, fake<int32_t>(8), fake<float>(9), 0, nullptr) == LFM_MOE_OK);

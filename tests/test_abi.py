@@ -123,6 +123,29 @@ def test_route_rmsnorm_block_checks(lib):
     assert lib.lfm_moe_block_forward_ws(a[0], a[1], a[2], a[3], a[4], 4, None, 0, None) == _lib.ERR_INVALID_ARGUMENT
 
 
+def test_stack_forward_checks(lib):
+    """lfm_moe_stack_forward_ws checks every block before launching anything
+    (each call here fails or is a no-op before any HIP call)."""
+    import ctypes
+    a = [_addr(i) for i in range(5)]
+    need = lib.lfm_moe_workspace_bytes(100)
+    ws = _addr(7)
+    good = _lib.BlockWeights(a[1], a[2], a[3], a[4])
+    blocks = (_lib.BlockWeights * 3)(good, good, _lib.BlockWeights(a[1], a[2], a[3], None))
+    f = lib.lfm_moe_stack_forward_ws
+    p = ctypes.addressof(blocks)
+    assert f(a[0], p, 3, 100, ws, need, None) == _lib.ERR_INVALID_ARGUMENT  # block 2 has no W_down
+    assert b"null tensor pointer" in lib.lfm_moe_last_error()
+    assert f(a[0], p, -1, 100, ws, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert f(a[0], None, 2, 100, ws, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert f(a[0], p, 2, 100, ws, need - 1, None) == _lib.ERR_WORKSPACE_TOO_SMALL
+    assert f(a[0], p, 2, 100, a[3] + 4096, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert b"workspace overlaps an input" in lib.lfm_moe_last_error()
+    assert f(a[0], p, 3, 0, None, 0, None) == _lib.OK   # N == 0
+    assert f(a[0], p, 0, 100, ws, need, None) == _lib.OK  # no blocks
+    assert f(a[0], None, 0, 100, None, 0, None) == _lib.OK
+
+
 def test_route_ws_checks(lib):
     """lfm_moe_route_ws: the router workspace is the partial logits of up to
     2048 tokens (none above), checked like the layer's."""

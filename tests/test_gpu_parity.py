@@ -467,6 +467,57 @@ def test_zero_tokens_is_a_no_op(moe):
     assert torch.all(sentinel == 7.0)
 
 
+@pytest.mark.parametrize("N", [64, 512])
+def test_stack_forward_equals_chained_blocks(moe, N):
+    """lfm_moe_stack_forward_ws over the first three stack blocks equals three
+    lfm_moe_block_forward_ws calls bit for bit (the combine of blocks 0 and 1
+    stores the next block's normalised input itself), with one normalisation
+    launch per call instead of one per block; a HIP graph of the stack call
+    replays to the same bits.  N = 64 takes the streaming path, 512 the
+    grouped one."""
+    seed = synth.STACK["seed"]
+    if "stack3" not in _CASES:
+        print("[case] generating stack blocks 0-2", flush=True)
+        blocks = []
+        for l in range(3):
+            d = device_weights(synth.stack_block_params(seed, l))
+            blocks.append((d["W_r"], d["bias"], d["W_gateup"], d["W_down"]))
+        _CASES["stack3"] = blocks
+    blocks = _CASES["stack3"]
+    x0 = synth.stack_residual(N, seed).cuda()
+    ws = moe.alloc_workspace(N)
+    _step(f"three block_forward_ws calls N={N}")
+    xb = x0.clone()
+    for blk in blocks:
+        moe.block_forward(xb, *blk, workspace=ws)
+    _step(f"stack_forward_ws of three blocks N={N}")
+    moe.timing_enable(True)
+    xs = moe.stack_forward(x0.clone(), blocks, workspace=ws)
+    t = moe.timing_read()
+    moe.timing_enable(False)
+    torch.cuda.synchronize()
+    assert torch.equal(xs, xb), "the stack call differs from chained block calls"
+    assert t["rmsnorm"][1] == 1 and t["combine"][1] == 3 and t["gateup"][1] == 3, t
+    _step(f"graph of stack_forward_ws N={N}")
+    x = x0.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        moe.stack_forward(x, blocks, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.stack_forward(x, blocks, workspace=ws)
+    for i in range(3):
+        x.copy_(x0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(x, xb), f"replay {i} differs"
+        moe.forward(*(torch.zeros(4, 2048, dtype=torch.bfloat16, device="cuda"),) + blocks[0])
+        torch.cuda.synchronize()
+    del g
+
+
 _STACK = {}
 
 
