@@ -53,6 +53,10 @@ SIGNATURES = {
     "lfm_moe_block_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _P]),
     "lfm_moe_block_forward_ws": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _P, _SZ, _P]),
     "lfm_moe_stack_forward_ws": (ctypes.c_int, [_P, _P, ctypes.c_int, _I64, _P, _SZ, _P]),
+    "lfm_moe_stage_dispatch": (ctypes.c_int, [_P, _P, _I64, _P, _SZ, _P]),
+    "lfm_moe_stage_gateup": (ctypes.c_int, [_P, _P, _I64, _P, _SZ, _P]),
+    "lfm_moe_stage_down": (ctypes.c_int, [_P, _I64, _P, _SZ, _P]),
+    "lfm_moe_stage_combine": (ctypes.c_int, [_P, _P, _I64, _P, _SZ, _P]),
     "lfm_moe_pack_fp8_gateup": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "lfm_moe_pack_fp8_down": (ctypes.c_int, [_P, _P, _P, _P]),
     "lfm_moe_forward_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _P]),

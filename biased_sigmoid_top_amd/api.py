@@ -277,6 +277,42 @@ def block_forward(x, W_r, bias, W_gateup, W_down, workspace=None, stream=None):
     return x
 
 
+def _ws_args(workspace):
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def stage_dispatch(idx, w, workspace, stream=None):
+    """Routing copy + dispatch into the workspace regions (lfm_moe_stage_dispatch)."""
+    N = idx.shape[0]
+    pi = _req(idx, "idx", torch.int32, (N, TOP_K))
+    pw = _req(w, "w", torch.float32, (N, TOP_K))
+    _lib.call("lfm_moe_stage_dispatch", pi, pw, N, *_ws_args(workspace), _stream(stream))
+
+
+def stage_gateup(X, W_gateup, workspace, stream=None):
+    """X and the workspace's grouping -> H region (lfm_moe_stage_gateup)."""
+    N = X.shape[0]
+    pX = _req(X, "X", torch.bfloat16, (N, HIDDEN))
+    pg = _req(W_gateup, "W_gateup (packed)", torch.bfloat16, (EXPERTS * 2 * FF * HIDDEN,))
+    _lib.call("lfm_moe_stage_gateup", pX, pg, N, *_ws_args(workspace), _stream(stream))
+
+
+def stage_down(W_down, N, workspace, stream=None):
+    """H region -> Y region (lfm_moe_stage_down)."""
+    pd = _req(W_down, "W_down (packed)", torch.bfloat16, (EXPERTS * HIDDEN * FF,))
+    _lib.call("lfm_moe_stage_down", pd, N, *_ws_args(workspace), _stream(stream))
+
+
+def stage_combine(N, workspace, out=None, resid=None, stream=None):
+    """Y and W regions -> out [N, 2048] fp32 (lfm_moe_stage_combine)."""
+    if out is None:
+        out = torch.empty(N, HIDDEN, dtype=torch.float32, device=workspace.device)
+    po = _req(out, "out", torch.float32, (N, HIDDEN))
+    pr = _req(resid, "resid", torch.float32, (N, HIDDEN)) if resid is not None else None
+    _lib.call("lfm_moe_stage_combine", pr, po, N, *_ws_args(workspace), _stream(stream))
+    return out
+
+
 def stack_forward(x, blocks, workspace=None, stream=None):
     """x <- x + MoE_l(bf16(RMSNorm(x))) for each (W_r, bias, W_gateup, W_down)
     of ``blocks`` in order, in place; returns x.  Without ``workspace`` one of

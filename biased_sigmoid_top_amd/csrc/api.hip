@@ -144,6 +144,22 @@ lfm_moe_status check_routing_args(const int32_t* idx, const float* w, int64_t N,
   return LFM_MOE_OK;
 }
 
+// Checks of the stage entry points: tensors present and aligned, the
+// workspace as for the layer and apart from them.
+lfm_moe_status check_stage(int64_t N, void* ws, size_t ws_bytes, Span out, std::initializer_list<Span> ins) {
+  if (N < 0) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "N must be >= 0");
+  if (N > LFM_MOE_MAX_TOKENS) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "N exceeds LFM_MOE_MAX_TOKENS");
+  if (N == 0) return LFM_MOE_OK;
+  for (const Span& s : ins)
+    if (!s.p) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "null tensor pointer");
+    else if (misaligned(s.p)) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  if (out.bytes != 0) {
+    if (!out.p) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "null tensor pointer");
+    if (misaligned(out.p)) return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  }
+  return check_ws(ws, ws_bytes, N, out, ins);
+}
+
 // Library-owned workspaces, one per device and purpose (the layer's, and
 // the router's partial logits for lfm_moe_route), grown on demand.
 constexpr int kMaxDevices = 64;
@@ -782,6 +798,69 @@ lfm_moe_status lfm_moe_block_forward_ws(float* x_inout, const uint16_t* W_r, con
   if (e != hipSuccess) return hip_fail(e, "rmsnorm kernel launch");
   timer.after(0);
   return run_layer(X, W_r, bias, nullptr, nullptr, W_gateup, W_down, x_inout, x_inout, N, ws, stream, timer);
+}
+
+// Stage entry points: the layer's own kernels one stage at a time on the
+// regions of a caller workspace.
+lfm_moe_status lfm_moe_stage_dispatch(const int32_t* idx, const float* w, int64_t N, void* ws, size_t ws_bytes,
+                                      hipStream_t stream) {
+  g_last_error.clear();
+  const size_t sel = static_cast<size_t>(N < 0 ? 0 : N) * kTopK * 4;
+  lfm_moe_status st = check_stage(N, ws, ws_bytes, Span{nullptr, 0}, {{idx, sel}, {w, sel}});
+  if (st != LFM_MOE_OK || N == 0) return st;
+  const int n = static_cast<int>(N);
+  int32_t* idx_ws = region<int32_t>(ws, N, LFM_MOE_WS_IDX);
+  int32_t* blockcounts = region<int32_t>(ws, N, LFM_MOE_WS_BLOCKCOUNTS);
+  hipError_t e = launch_ingest_routing(idx, w, idx_ws, region<float>(ws, N, LFM_MOE_WS_W), blockcounts, n, stream);
+  if (e != hipSuccess) return hip_fail(e, "routing copy kernel launch");
+  e = launch_dispatch(idx_ws, blockcounts, region<int32_t>(ws, N, LFM_MOE_WS_OFFSETS),
+                      region<int32_t>(ws, N, LFM_MOE_WS_ROW2SLOT), n, stream);
+  if (e != hipSuccess) return hip_fail(e, "dispatch kernel launch");
+  return LFM_MOE_OK;
+}
+
+lfm_moe_status lfm_moe_stage_gateup(const uint16_t* X, const uint16_t* W_gateup, int64_t N, void* ws,
+                                    size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  lfm_moe_status st = check_stage(N, ws, ws_bytes, Span{nullptr, 0}, {{X, act_bytes(N, 2)}, gateup_span(W_gateup)});
+  if (st != LFM_MOE_OK || N == 0) return st;
+  uint16_t* H = region<uint16_t>(ws, N, LFM_MOE_WS_H);
+  const hipError_t e =
+      use_decode_path(N)
+          ? launch_gateup_decode(X, W_gateup, region<int32_t>(ws, N, LFM_MOE_WS_IDX), H, static_cast<int>(N), stream)
+          : launch_gateup_tiled(X, W_gateup, region<int32_t>(ws, N, LFM_MOE_WS_OFFSETS),
+                                region<int32_t>(ws, N, LFM_MOE_WS_ROW2SLOT), H, N, stream);
+  return e == hipSuccess ? LFM_MOE_OK : hip_fail(e, "gate/up kernel launch");
+}
+
+lfm_moe_status lfm_moe_stage_down(const uint16_t* W_down, int64_t N, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  g_last_error.clear();
+  lfm_moe_status st = check_stage(N, ws, ws_bytes, Span{nullptr, 0}, {down_span(W_down)});
+  if (st != LFM_MOE_OK || N == 0) return st;
+  const uint16_t* H = region<uint16_t>(ws, N, LFM_MOE_WS_H);
+  float* Y = region<float>(ws, N, LFM_MOE_WS_Y);
+  const hipError_t e =
+      use_decode_path(N)
+          ? launch_down_decode(H, W_down, region<int32_t>(ws, N, LFM_MOE_WS_IDX), Y, static_cast<int>(N), stream)
+          : launch_down_tiled(H, W_down, region<int32_t>(ws, N, LFM_MOE_WS_OFFSETS),
+                              region<int32_t>(ws, N, LFM_MOE_WS_ROW2SLOT), Y, N, stream);
+  return e == hipSuccess ? LFM_MOE_OK : hip_fail(e, "down kernel launch");
+}
+
+lfm_moe_status lfm_moe_stage_combine(const float* resid, float* out, int64_t N, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+  g_last_error.clear();
+  const size_t ob = act_bytes(N, 4);
+  lfm_moe_status st = resid != nullptr
+                          ? check_stage(N, ws, ws_bytes, Span{out, ob}, {{resid, ob}})
+                          : check_stage(N, ws, ws_bytes, Span{out, ob}, {});
+  if (st != LFM_MOE_OK || N == 0) return st;
+  if (resid != nullptr && resid != out && overlap(Span{resid, ob}, Span{out, ob}))
+    return fail(LFM_MOE_ERR_INVALID_ARGUMENT, "resid overlaps out without being it");
+  const hipError_t e = launch_combine(region<float>(ws, N, LFM_MOE_WS_Y), region<float>(ws, N, LFM_MOE_WS_W),
+                                      resid, out, N, stream);
+  return e == hipSuccess ? LFM_MOE_OK : hip_fail(e, "combine kernel launch");
 }
 
 lfm_moe_status lfm_moe_stack_forward_ws(float* x_inout, const lfm_moe_block_weights* blocks, int n_blocks,

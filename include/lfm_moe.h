@@ -242,6 +242,47 @@ lfm_moe_status lfm_moe_experts_ws(const uint16_t* X, const int32_t* idx, const f
                                   hipStream_t stream);
 
 /*
+ * Stage entry points (for tests that check one stage at a time): the
+ * layer's own kernels for one stage, on the regions of a caller workspace
+ * of at least lfm_moe_workspace_bytes(N) bytes (guide, section "What to
+ * verify in a deployment": route, group the tokens by expert, run each
+ * expert on its group, combine the weighted outputs; section "The router
+ * has two different scores" for what the router hands over).  Called in
+ * the order dispatch, gate/up, down, combine on one workspace, they give
+ * lfm_moe_experts_ws's result bit for bit (the same kernels on the same
+ * regions).  Between calls a test may overwrite the H region (bf16
+ * [4N, 1536], slot order) or the Y region (fp32 [4N, 2048], slot order)
+ * with values of its own, to check the next stage alone; the IDX, W,
+ * BLOCKCOUNTS, OFFSETS and ROW2SLOT regions must hold what
+ * lfm_moe_stage_dispatch (or a layer call with the same N) stored there.
+ * Asynchronous on stream; arguments checked before any HIP call; N == 0 is
+ * a no-op; 0 <= N <= LFM_MOE_MAX_TOKENS.
+ *
+ * lfm_moe_stage_dispatch: idx [N, 4] int32, w [N, 4] fp32 (read; replaced
+ *   by the rule of lfm_moe_experts_ws where invalid) -> IDX and W regions
+ *   (the routing used), BLOCKCOUNTS, OFFSETS [65] (expert e's grouped rows
+ *   are OFFSETS[e] .. OFFSETS[e+1]-1) and ROW2SLOT [4N] (grouped row ->
+ *   slot t*4 + j; within an expert, slots in token order).
+ * lfm_moe_stage_gateup: X [N, 2048] bf16, W_gateup (pack output) -> H
+ *   region: H[t*4 + j] = bf16(silu(X_t Wg_e^T) * (X_t Wu_e^T)), e = IDX[t, j].
+ * lfm_moe_stage_down: W_down (pack output), H region -> Y region:
+ *   Y[t*4 + j] = H[t*4 + j] Wd_e^T (fp32).
+ * lfm_moe_stage_combine: Y and W regions -> out [N, 2048] fp32:
+ *   out[t] = (resid[t] +) sum_j W[t, j] Y[t*4 + j] in the order j = 0..3.
+ *   resid may be NULL, or equal to out (in place); it may not otherwise
+ *   overlap out.
+ * Tensors may not overlap the workspace.
+ */
+lfm_moe_status lfm_moe_stage_dispatch(const int32_t* idx, const float* w, int64_t N, void* ws, size_t ws_bytes,
+                                      hipStream_t stream);
+lfm_moe_status lfm_moe_stage_gateup(const uint16_t* X, const uint16_t* W_gateup, int64_t N, void* ws,
+                                    size_t ws_bytes, hipStream_t stream);
+lfm_moe_status lfm_moe_stage_down(const uint16_t* W_down, int64_t N, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+lfm_moe_status lfm_moe_stage_combine(const float* resid, float* out, int64_t N, void* ws, size_t ws_bytes,
+                                     hipStream_t stream);
+
+/*
  * One block's feed-forward half (guide, section "The exact checkpoint":
  * normalise, feed-forward network, residual):
  *   x_inout[t] <- x_inout[t] + MoE(bf16(RMSNorm(x_inout[t])))

@@ -146,6 +146,29 @@ def test_stack_forward_checks(lib):
     assert f(a[0], None, 0, 100, None, 0, None) == _lib.OK
 
 
+def test_stage_checks(lib):
+    """The stage entry points check their tensors and the workspace before
+    any HIP call."""
+    a = [_addr(i) for i in range(5)]
+    need = lib.lfm_moe_workspace_bytes(100)
+    ws = _addr(7)
+    assert lib.lfm_moe_stage_dispatch(a[0], a[1], 100, ws, need - 1, None) == _lib.ERR_WORKSPACE_TOO_SMALL
+    assert lib.lfm_moe_stage_dispatch(None, a[1], 100, ws, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.lfm_moe_stage_dispatch(a[0], a[1] + 4, 100, ws, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.lfm_moe_stage_dispatch(a[0], a[1], -1, ws, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.lfm_moe_stage_dispatch(a[0], a[1], 0, None, 0, None) == _lib.OK
+    assert lib.lfm_moe_stage_gateup(a[0], a[3], 100, a[3] + 4096, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert b"workspace overlaps an input" in lib.lfm_moe_last_error()
+    assert lib.lfm_moe_stage_gateup(a[0], None, 100, ws, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.lfm_moe_stage_down(a[4], 100, None, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.lfm_moe_stage_down(a[4], 100, ws + 16, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.lfm_moe_stage_combine(None, None, 100, ws, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.lfm_moe_stage_combine(None, ws + 256, 100, ws, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert b"workspace overlaps the output" in lib.lfm_moe_last_error()
+    assert lib.lfm_moe_stage_combine(a[0] + 64, a[0], 100, ws, need, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.lfm_moe_stage_combine(a[0], a[0], 0, None, 0, None) == _lib.OK
+
+
 def test_route_ws_checks(lib):
     """lfm_moe_route_ws: the router workspace is the partial logits of up to
     2048 tokens (none above), checked like the layer's."""
