@@ -396,6 +396,8 @@ def parse_args(argv=None):
     ap.add_argument("--no-extra", action="store_true",
                     help="leave out the skewed 16,384-token layer and the 38-block stack (measured by default)")
     ap.add_argument("--workload", default="decode_n64", help="headline workload")
+    ap.add_argument("--stack-only", action="store_true",
+                    help="only measure the 38-block stack (for profiling it on its own); prints its entry")
     ap.add_argument("--configs", action="store_true",
                     help="also measure every configuration (C0-C4, the 38-block stack included; "
                          "several minutes) and add them, with the verification-batch series V1-V64, to the line under 'configs'")
@@ -419,6 +421,10 @@ def main():
         return
 
     import biased_sigmoid_top_amd  # noqa: F401  (fails loudly without the built library)
+
+    if args.stack_only:
+        print(json.dumps(measure_stack(max(3, args.steps // 4), 1)), flush=True)
+        return
 
     head = prepare(args.workload, args.copies)
     log(f"timing {args.workload}: {args.steps} steps after {args.warmup} warm-up")
