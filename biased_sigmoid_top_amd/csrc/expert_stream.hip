@@ -350,7 +350,7 @@ __device__ __forceinline__ uint32_t fp8_block_bytes(int e, int b) {
   return static_cast<uint32_t>((e * kBlocks + b) * kPairs) * kFp8FragBytes;
 }
 
-template <bool GATEUP, int GPW>
+template <bool GATEUP, int GPW, int RING>
 __device__ __forceinline__ void stream_units_fp8(const uint16_t* __restrict__ B,
                                                  const uint8_t* __restrict__ Wq,
                                                  const float* __restrict__ Ws,
@@ -365,7 +365,9 @@ __device__ __forceinline__ void stream_units_fp8(const uint16_t* __restrict__ B,
   my_share<kUnitsPerExpert>(S.G, begin, end);
   if (begin >= end) return;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  // Uniform, so that the per-group scale reads are scalar loads: a vector
+  // load here would make the wait for it drain the weight ring at every unit.
+  const int wave = uniform(static_cast<int>(threadIdx.x / kWave));
   const uint32_t lane_bytes = lane * 16;
   const uint32_t kcol_bytes = (wave * 128 * GPW + (lane / 32) * 8) * 2;  // this lane's first bf16 K column
   const Rsrc wr = make_rsrc(Wq, static_cast<uint32_t>(kExperts) * kHidden * kFF * (GATEUP ? 2 : 1));
@@ -405,7 +407,7 @@ __device__ __forceinline__ void stream_units_fp8(const uint16_t* __restrict__ B,
 
   // Token rows: 8 bf16 K steps per group and lane as loaded; quantised in
   // place to the bf16 values of their E4M3 codes (K step k stays in xb[k]).
-  uint4 w0[kFrags], w1[kFrags], w2[kFrags], xb[kSteps];
+  uint4 w[RING][kFrags], xb[kSteps];
   float xscale[GPW] = {};
   bool fresh = false;
   int xe = -1, xpass = -1;
@@ -452,60 +454,69 @@ __device__ __forceinline__ void stream_units_fp8(const uint16_t* __restrict__ B,
 
   Cursor cp{begin, 0, 0}, ld{begin, 0, 0};
   load_rows(cp);
-  issue(ld, w0);
-  advance(ld);
-  issue(ld, w1);
-  advance(ld);
+#pragma unroll
+  for (int r = 0; r + 1 < RING; ++r) {
+    issue(ld, w[r]);
+    advance(ld);
+  }
 
-  auto step = [&](uint4 (&wc)[kFrags], uint4 (&wi)[kFrags]) -> bool {
-    if (cp.u >= end) return false;
-    if (fresh) {
-      quantize_rows();
-      fresh = false;
-    }
-    // One accumulator per K group: the groups have their own scales.
-    f32x16 acc[GPW];
-#pragma unroll
-    for (int g = 0; g < GPW; ++g) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[g][r] = 0.f;
-#pragma unroll
-      for (int f = 4 * g; f < 4 * g + 4; ++f) {
-        acc[g] = mfma32(e4m3x8_to_bf16(wc[f].x, wc[f].y), xb[2 * f], acc[g]);
-        acc[g] = mfma32(e4m3x8_to_bf16(wc[f].z, wc[f].w), xb[2 * f + 1], acc[g]);
-      }
-    }
+  // One unit: multiply the weights in wc, issue the loads RING - 1 units ahead
+  // into wi, add the partial tiles.  Past the end of the share (the last
+  // round of the loop) the arithmetic and the stores are skipped while the
+  // loads and barriers still run: the loop then has a single exit, and the
+  // compiler's counts of loads in flight stay exact around it (with an exit
+  // after every unit they merge into a full drain of the ring each unit).
+  auto step = [&](uint4 (&wc)[kFrags], uint4 (&wi)[kFrags]) {
+    const bool live = cp.u < end;
     const Cursor cur = cp;
-    const int e = expert_of(cur.u);
-    const int b = cur.u % kUnitsPerExpert;
-    // Each group's products times weight scale x token scale, the groups
-    // added in order: this wavefront's partial tile.
-    if (GATEUP) {
-      float sg[GPW], su[GPW];
+    if (live) {
+      if (fresh) {
+        quantize_rows();
+        fresh = false;
+      }
+      // One accumulator per K group: the groups have their own scales.
+      f32x16 acc[GPW];
 #pragma unroll
       for (int g = 0; g < GPW; ++g) {
-        const int kg = wave * GPW + g;
-        sg[g] = Ws[((e * 2 + 0) * (kFF / 128) + b / 8) * (kHidden / 128) + kg] * xscale[g];
-        su[g] = Ws[((e * 2 + 1) * (kFF / 128) + b / 8) * (kHidden / 128) + kg] * xscale[g];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[g][r] = 0.f;
+#pragma unroll
+        for (int f = 4 * g; f < 4 * g + 4; ++f) {
+          acc[g] = mfma32(e4m3x8_to_bf16(wc[f].x, wc[f].y), xb[2 * f], acc[g]);
+          acc[g] = mfma32(e4m3x8_to_bf16(wc[f].z, wc[f].w), xb[2 * f + 1], acc[g]);
+        }
       }
+      const int e = expert_of(cur.u);
+      const int b = cur.u % kUnitsPerExpert;
+      // Each group's products times weight scale x token scale, the groups
+      // added in order: this wavefront's partial tile.
+      if (GATEUP) {
+        float sg[GPW], su[GPW];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = acc[0][r] * (r < 8 ? sg[0] : su[0]);
+        for (int g = 0; g < GPW; ++g) {
+          const int kg = wave * GPW + g;
+          sg[g] = Ws[((e * 2 + 0) * (kFF / 128) + b / 8) * (kHidden / 128) + kg] * xscale[g];
+          su[g] = Ws[((e * 2 + 1) * (kFF / 128) + b / 8) * (kHidden / 128) + kg] * xscale[g];
+        }
 #pragma unroll
-        for (int g = 1; g < GPW; ++g) v += acc[g][r] * (r < 8 ? sg[g] : su[g]);
-        S.red[wave][r][lane] = v;
-      }
-    } else {
-      float sd[GPW];
+        for (int r = 0; r < 16; ++r) {
+          float v = acc[0][r] * (r < 8 ? sg[0] : su[0]);
 #pragma unroll
-      for (int g = 0; g < GPW; ++g)
-        sd[g] = Ws[(e * (kHidden / 128) + b / 4) * (kFF / 128) + wave * GPW + g] * xscale[g];
+          for (int g = 1; g < GPW; ++g) v += acc[g][r] * (r < 8 ? sg[g] : su[g]);
+          S.red[wave][r][lane] = v;
+        }
+      } else {
+        float sd[GPW];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = acc[0][r] * sd[0];
+        for (int g = 0; g < GPW; ++g)
+          sd[g] = Ws[(e * (kHidden / 128) + b / 4) * (kFF / 128) + wave * GPW + g] * xscale[g];
 #pragma unroll
-        for (int g = 1; g < GPW; ++g) v += acc[g][r] * sd[g];
-        S.red[wave][r][lane] = v;
+        for (int r = 0; r < 16; ++r) {
+          float v = acc[0][r] * sd[0];
+#pragma unroll
+          for (int g = 1; g < GPW; ++g) v += acc[g][r] * sd[g];
+          S.red[wave][r][lane] = v;
+        }
       }
     }
     advance(cp);
@@ -513,47 +524,51 @@ __device__ __forceinline__ void stream_units_fp8(const uint16_t* __restrict__ B,
     issue(ld, wi);
     advance(ld);
     __syncthreads();
-    const int r0 = cur.pass * kPassRows;
-    const int rows = min(kPassRows, count_of(e) - r0);
-    const int* slots = S.G.list + S.G.off[e] + r0;
-    // Thread (r, ln) adds value r of lane ln over the wavefronts (token
-    // ln % 32, row mfma32_row(r, ln) of the unit's 32-row tile), for r =
-    // its wavefront index and, with fewer than 16 wavefronts, r + kWaves.
-    const int ln = threadIdx.x % kWave;
-    if (ln % 32 < rows) {
-      const int slot = slots[ln % 32];
-      for (int r = threadIdx.x / kWave; r < 16; r += kWaves) {
-        if (GATEUP) {
-          if (r < 8) {  // rows r (gate) and r + 8 (up) hold H column mfma32_row(r, ln)
-            float gs = 0.f, us = 0.f;
+    if (live) {
+      const int e = expert_of(cur.u);
+      const int b = cur.u % kUnitsPerExpert;
+      const int r0 = cur.pass * kPassRows;
+      const int rows = min(kPassRows, count_of(e) - r0);
+      const int* slots = S.G.list + S.G.off[e] + r0;
+      // Thread (r, ln) adds value r of lane ln over the wavefronts (token
+      // ln % 32, row mfma32_row(r, ln) of the unit's 32-row tile), for r =
+      // its wavefront index and, with fewer than 16 wavefronts, r + kWaves.
+      const int ln = threadIdx.x % kWave;
+      if (ln % 32 < rows) {
+        const int slot = slots[ln % 32];
+        for (int r = threadIdx.x / kWave; r < 16; r += kWaves) {
+          if (GATEUP) {
+            if (r < 8) {  // rows r (gate) and r + 8 (up) hold H column mfma32_row(r, ln)
+              float gs = 0.f, us = 0.f;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-              gs += S.red[w][r][ln];
-              us += S.red[w][r + 8][ln];
+              for (int w = 0; w < kWaves; ++w) {
+                gs += S.red[w][r][ln];
+                us += S.red[w][r + 8][ln];
+              }
+              H[static_cast<size_t>(slot) * kFF + b * 16 + mfma32_row(r, ln)] = f32_to_bf16(silu(gs) * us);
             }
-            H[static_cast<size_t>(slot) * kFF + b * 16 + mfma32_row(r, ln)] = f32_to_bf16(silu(gs) * us);
-          }
-        } else {
-          float ys = 0.f;
+          } else {
+            float ys = 0.f;
 #pragma unroll
-          for (int w = 0; w < kWaves; ++w) ys += S.red[w][r][ln];
-          Y[static_cast<size_t>(slot) * kHidden + b * 32 + mfma32_row(r, ln)] = ys;
+            for (int w = 0; w < kWaves; ++w) ys += S.red[w][r][ln];
+            Y[static_cast<size_t>(slot) * kHidden + b * 32 + mfma32_row(r, ln)] = ys;
+          }
         }
       }
     }
     __syncthreads();
-    return true;
   };
-  for (;;) {
-    if (!step(w0, w2)) break;
-    if (!step(w1, w0)) break;
-    if (!step(w2, w1)) break;
-  }
+  // Unit s uses buffer s % RING.
+  do {
+#pragma unroll
+    for (int r = 0; r < RING; ++r) step(w[r], w[(r + RING - 1) % RING]);
+  } while (cp.u < end);
 }
 
 // K groups of 128 per wavefront: gate/up 2 (8 wavefronts), down 1 (12).
 constexpr int kFp8GateupGroups = 2;
 constexpr int kFp8DownGroups = 1;
+constexpr int kFp8Ring = 3;  // units of weights in the register ring (two in flight)
 constexpr int kFp8GateupThreads = kHidden / (128 * kFp8GateupGroups) * kWave;
 constexpr int kFp8DownThreads = kFF / (128 * kFp8DownGroups) * kWave;
 
@@ -562,7 +577,7 @@ __global__ __launch_bounds__(kFp8GateupThreads) void gateup_decode_fp8_kernel(
     const int32_t* __restrict__ idx, uint16_t* __restrict__ H, int N) {
   __shared__ StreamShared S;
   group_slots(idx, N, S.G);
-  stream_units_fp8<true, kFp8GateupGroups>(X, Wq, Ws, H, nullptr, N, S);
+  stream_units_fp8<true, kFp8GateupGroups, kFp8Ring>(X, Wq, Ws, H, nullptr, N, S);
 }
 
 __global__ __launch_bounds__(kFp8DownThreads) void down_decode_fp8_kernel(
@@ -570,7 +585,7 @@ __global__ __launch_bounds__(kFp8DownThreads) void down_decode_fp8_kernel(
     const int32_t* __restrict__ idx, float* __restrict__ Y, int N) {
   __shared__ StreamShared S;
   group_slots(idx, N, S.G);
-  stream_units_fp8<false, kFp8DownGroups>(H, Wq, Ws, nullptr, Y, N, S);
+  stream_units_fp8<false, kFp8DownGroups, kFp8Ring>(H, Wq, Ws, nullptr, Y, N, S);
 }
 
 // Wavefronts splitting K: gate/up 16 (8 K steps each), down 16 (6 each).
