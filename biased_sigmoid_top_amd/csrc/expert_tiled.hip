@@ -98,8 +98,15 @@ struct TileShape {
 // FP8: Wp holds the FP8 codes of the experts (pack_fp8.hip layout: 1 KB
 // fragments of 32 rows x 32 K, one per K stage), Ws their fp32 block scales,
 // A the bf16 values of the token rows' E4M3 codes and As the rows' scales per
-// 128-wide K group.  Each group of four stages (128 K) is accumulated on its
-// own and added into the result times weight scale x token scale.
+// 128-wide K group.  A group of four stages (128 K) adds its products times
+// weight scale x token scale.  One accumulator set serves all groups: it
+// holds the sum so far in units of the current group's scale product (one
+// per token column and, for gate/up, per gate or up half), so before each
+// group it is multiplied by old unit / new unit, and at the end by the last
+// unit.  (Where a scale is 0 the group's codes are all 0, and the unit
+// stays.)  The products are exact and the sums fp32, as with a second
+// accumulator set per group, up to the rounding of the unit changes (a few
+// fp32 ulps per group; the ratio uses the hardware reciprocal).
 template <bool GATEUP, int FB_, int WAVES_, int TB_, bool FP8 = false, bool NTW = false>
 __global__ __launch_bounds__((TileShape<GATEUP, FB_, WAVES_, TB_>::kThreads),
                              (TileShape<GATEUP, FB_, WAVES_, TB_>::kPerCu))
@@ -193,8 +200,6 @@ void expert_tiled_kernel(
   };
 
   f32x16 acc[TB][FB];
-  // FP8: the current K group's products (unused otherwise).
-  f32x16 part[FP8 ? TB : 1][FP8 ? FB : 1];
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
@@ -202,6 +207,63 @@ void expert_tiled_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[tb][f][r] = 0.f;
 
+  // FP8 scales: this wavefront's weight row blocks (128 rows) and the
+  // tile rows' token rows (padding rows take row 0's; their results are
+  // dropped).
+  int srow[FP8 ? TB : 1];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const int row = tb * 32 + lane % 32;
+      const int slot = row2slot[tile.row_begin + (row < tile.rows ? row : 0)];
+      srow[tb] = GATEUP ? slot / kTopK : slot;
+    }
+  }
+  // FP8 scales of one K group, and the units of the accumulators.
+  constexpr int kG = T::K / 128;
+  float xs[FP8 ? TB : 1], wsa[FP8 ? FB : 1], wsb[FP8 ? FB : 1];
+  float unit[FP8 ? TB : 1][FP8 ? FB : 1][2];
+  auto load_scales = [&](int g) {
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) xs[tb] = As[static_cast<size_t>(srow[tb]) * kG + g];
+    const int e = uniform(tile.expert);
+#pragma unroll
+    for (int f = 0; f < FB; ++f) {
+      const int blk = nb * T::kBlocksPerTile + wave * FB + f;
+      if (GATEUP) {  // gate rows (values r < 8 of a tile) and up rows
+        wsa[f] = Ws[((e * 2 + 0) * (kFF / 128) + blk / 8) * kG + g];
+        wsb[f] = Ws[((e * 2 + 1) * (kFF / 128) + blk / 8) * kG + g];
+      } else {
+        wsa[f] = wsb[f] = Ws[(e * (kHidden / 128) + blk / 4) * kG + g];
+      }
+    }
+  };
+  // Re-expresses the sums in units of the scales last loaded.
+  auto rebase = [&] {
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int f = 0; f < FB; ++f) {
+        const float sc[2] = {wsa[f] * xs[tb], wsb[f] * xs[tb]};
+        float k[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          k[h] = sc[h] != 0.f ? unit[tb][f][h] * __builtin_amdgcn_rcpf(sc[h]) : 1.f;
+          unit[tb][f][h] = sc[h] != 0.f ? sc[h] : unit[tb][f][h];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[tb][f][r] *= (r < 8 ? k[0] : k[1]);
+      }
+  };
+  // Group 0's scales go first, so that waiting for them leaves the ring's
+  // loads in flight.
+  if constexpr (FP8) {
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int f = 0; f < FB; ++f) unit[tb][f][0] = unit[tb][f][1] = 1.f;
+    load_scales(0);
+  }
 #pragma unroll
   for (int s = 0; s < kWSlots - 1; ++s) load_w(s, wring[s]);
   load_x(0);
@@ -229,7 +291,7 @@ void expert_tiled_kernel(
             // Lane bytes 0..7: K step 0 of the stage, 8..15: K step 1.
             const uint4 wbf = j == 0 ? e4m3x8_to_bf16(wj[f][0].x, wj[f][0].y)
                                      : e4m3x8_to_bf16(wj[f][0].z, wj[f][0].w);
-            part[tb][f] = mfma32(wbf, d[tb], part[tb][f]);
+            acc[tb][f] = mfma32(wbf, d[tb], acc[tb][f]);
           } else {
             acc[tb][f] = mfma32(wj[f][j], d[tb], acc[tb][f]);
           }
@@ -271,56 +333,23 @@ void expert_tiled_kernel(
       fence();
     }
   };
-  // FP8 scales: this wavefront's weight row blocks (128 rows) and the
-  // tile rows' token rows (padding rows take row 0's; their results are
-  // dropped).
-  int srow[FP8 ? TB : 1];
-  if constexpr (FP8) {
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      const int row = tb * 32 + lane % 32;
-      const int slot = row2slot[tile.row_begin + (row < tile.rows ? row : 0)];
-      srow[tb] = GATEUP ? slot / kTopK : slot;
-    }
-  }
+  if constexpr (FP8) rebase();  // the sums are 0: this sets the units of group 0
   for (int s = 0; s < T::kStages; s += kWSlots) {
-    float xs[FP8 ? TB : 1], wsa[FP8 ? FB : 1], wsb[FP8 ? FB : 1];
-    if constexpr (FP8) {
-      const int g = s / kWSlots;
-      constexpr int kG = T::K / 128;
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb) xs[tb] = As[static_cast<size_t>(srow[tb]) * kG + g];
-      const int e = uniform(tile.expert);
-#pragma unroll
-      for (int f = 0; f < FB; ++f) {
-        const int blk = nb * T::kBlocksPerTile + wave * FB + f;
-        if (GATEUP) {  // gate rows (values r < 8 of a tile) and up rows
-          wsa[f] = Ws[((e * 2 + 0) * (kFF / 128) + blk / 8) * kG + g];
-          wsb[f] = Ws[((e * 2 + 1) * (kFF / 128) + blk / 8) * kG + g];
-        } else {
-          wsa[f] = wsb[f] = Ws[(e * (kHidden / 128) + blk / 4) * kG + g];
-        }
-      }
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-        for (int f = 0; f < FB; ++f)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) part[tb][f][r] = 0.f;
-    }
+    // The next group's scales are loaded a group ahead (the last group loads
+    // its own again: the rebase is then exact, old unit / same unit = 1).
+    if constexpr (FP8) load_scales(min(s / kWSlots + 1, kG - 1));
 #pragma unroll
     for (int q = 0; q < kWSlots; ++q)
       stage(s + q, q % 2, q / 2, wring[q], wring[(q + kWSlots - 1) % kWSlots]);
-    if constexpr (FP8) {
+    if constexpr (FP8) rebase();
+  }
+  if constexpr (FP8) {
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
+    for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-        for (int f = 0; f < FB; ++f) {
-          const float sa = wsa[f] * xs[tb], sb = wsb[f] * xs[tb];
+      for (int f = 0; f < FB; ++f)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[tb][f][r] += part[tb][f][r] * (r < 8 ? sa : sb);
-        }
-    }
+        for (int r = 0; r < 16; ++r) acc[tb][f][r] *= unit[tb][f][r < 8 ? 0 : 1];
   }
 
   // acc[tb][f]: token row tb*32 + lane % 32 of the tile; rows
@@ -458,15 +487,28 @@ hipError_t launch_down_tiled(const uint16_t* H, const uint16_t* Wd, const int32_
 hipError_t launch_gateup_tiled_fp8(const uint16_t* Xq, const uint8_t* Wq, const float* Ws,
                                    const float* Xs, const int32_t* offsets, const int32_t* row2slot,
                                    uint16_t* H, int64_t N, hipStream_t stream) {
-  return N <= kOneTouchTokens ? launch_tiled<true, 1, 8, 4, true, true>(Xq, Wq, offsets, row2slot, H, N, stream, Ws, Xs)
-                              : launch_tiled<true, 1, 8, 4, true>(Xq, Wq, offsets, row2slot, H, N, stream, Ws, Xs);
+  switch (gateup_tiles(N)) {
+    case GateupTiles::kNarrow4:
+      return launch_tiled<true, 1, 4, 4, true, true>(Xq, Wq, offsets, row2slot, H, N, stream, Ws, Xs);
+    case GateupTiles::kNarrow8:
+      return launch_tiled<true, 1, 8, 4, true>(Xq, Wq, offsets, row2slot, H, N, stream, Ws, Xs);
+    default:
+      return N <= kOneTouchTokens ? launch_tiled<true, 2, 8, 4, true, true>(Xq, Wq, offsets, row2slot, H, N, stream, Ws, Xs)
+                                  : launch_tiled<true, 2, 8, 4, true>(Xq, Wq, offsets, row2slot, H, N, stream, Ws, Xs);
+  }
 }
 
 hipError_t launch_down_tiled_fp8(const uint16_t* Hq, const uint8_t* Wq, const float* Ws,
                                  const float* Hs, const int32_t* offsets, const int32_t* row2slot,
                                  float* Y, int64_t N, hipStream_t stream) {
-  return N <= kOneTouchTokens ? launch_tiled<false, 1, 4, 4, true, true>(Hq, Wq, offsets, row2slot, Y, N, stream, Ws, Hs)
-                              : launch_tiled<false, 1, 4, 4, true>(Hq, Wq, offsets, row2slot, Y, N, stream, Ws, Hs);
+  switch (down_tiles(N)) {
+    case DownTiles::kNarrow4:
+      return launch_tiled<false, 1, 4, 4, true, true>(Hq, Wq, offsets, row2slot, Y, N, stream, Ws, Hs);
+    case DownTiles::kNarrow8:
+      return launch_tiled<false, 1, 8, 4, true>(Hq, Wq, offsets, row2slot, Y, N, stream, Ws, Hs);
+    default:  // the 4-wavefront form of two blocks would spill in FP8 mode
+      return launch_tiled<false, 2, 8, 4, true>(Hq, Wq, offsets, row2slot, Y, N, stream, Ws, Hs);
+  }
 }
 
 }  // namespace lfm

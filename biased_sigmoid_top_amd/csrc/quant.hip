@@ -18,30 +18,41 @@ namespace lfm {
 namespace {
 
 constexpr int kQGroup = 128;
+constexpr int kQLanesPerGroup = kQGroup / 8;               // 8 values (16 bytes) per lane
+constexpr int kQGroupsPerWave = kWave / kQLanesPerGroup;   // 4
 constexpr int kQWavesPerBlock = 4;
 
-// One wavefront per (row, group): lane l holds values 2l and 2l + 1.
+// Four consecutive (row, group) items per wavefront, 16 lanes per item, 16
+// bytes per lane.  Rows have a multiple of four groups (K = 2048 or 1536),
+// so a wavefront's items share one row.
 __global__ __launch_bounds__(kQWavesPerBlock * kWave) void quantize_groups_kernel(
     const uint16_t* __restrict__ A, int64_t rows, int K, uint16_t* __restrict__ Q,
     float* __restrict__ S) {
   const int groups = K / kQGroup;
-  const int64_t item = static_cast<int64_t>(blockIdx.x) * kQWavesPerBlock + threadIdx.x / kWave;
-  if (item >= rows * groups) return;
   const int lane = threadIdx.x % kWave;
+  const int64_t item = (static_cast<int64_t>(blockIdx.x) * kQWavesPerBlock + threadIdx.x / kWave) *
+                           kQGroupsPerWave + lane / kQLanesPerGroup;
+  if (item >= rows * groups) return;
   const int64_t row = item / groups;
   const int g = static_cast<int>(item % groups);
-  const size_t at = static_cast<size_t>(row) * K + g * kQGroup + 2 * lane;
-  const uint32_t v = *reinterpret_cast<const uint32_t*>(A + at);
-  // Largest magnitude on the bf16 bit patterns (finite values order as their bits).
-  float amax = __uint_as_float(max(v & 0x7fffu, (v >> 16) & 0x7fffu) << 16);
+  const size_t at = static_cast<size_t>(row) * K + g * kQGroup + 8 * (lane % kQLanesPerGroup);
+  const uint4 v = *reinterpret_cast<const uint4*>(A + at);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  // Largest magnitude of the group on the bf16 bit patterns (finite values
+  // order as their bits), then over the group's 16 lanes.
+  uint32_t m = 0;
 #pragma unroll
-  for (int off = kWave / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+  for (int k = 0; k < 4; ++k) m = max(m, max(w[k] & 0x7fffu, (w[k] >> 16) & 0x7fffu));
+  float amax = __uint_as_float(m << 16);
+#pragma unroll
+  for (int off = kQLanesPerGroup / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
   const float inv = amax > 0.f ? 448.f / amax : 0.f;
-  const float lo = __uint_as_float(v << 16) * inv, hi = __uint_as_float(v & 0xffff0000u) * inv;
-  const uint32_t codes = e4m3x4(lo, hi, 0.f, 0.f);
-  const uint4 vals = e4m3x8_to_bf16(codes, 0u);
-  *reinterpret_cast<uint32_t*>(Q + at) = vals.x;
-  if (lane == 0) S[static_cast<size_t>(row) * groups + g] = amax / 448.f;
+  auto q4 = [&](uint32_t lo, uint32_t hi) {
+    return e4m3x4(__uint_as_float(lo << 16) * inv, __uint_as_float(lo & 0xffff0000u) * inv,
+                  __uint_as_float(hi << 16) * inv, __uint_as_float(hi & 0xffff0000u) * inv);
+  };
+  *reinterpret_cast<uint4*>(Q + at) = e4m3x8_to_bf16(q4(w[0], w[1]), q4(w[2], w[3]));
+  if (lane % kQLanesPerGroup == 0) S[static_cast<size_t>(row) * groups + g] = amax / 448.f;
 }
 
 }  // namespace
@@ -49,7 +60,8 @@ __global__ __launch_bounds__(kQWavesPerBlock * kWave) void quantize_groups_kerne
 hipError_t launch_quantize_groups(const uint16_t* A, int64_t rows, int K, uint16_t* Q, float* S,
                                   hipStream_t stream) {
   const int64_t items = rows * (K / kQGroup);
-  const int64_t blocks = (items + kQWavesPerBlock - 1) / kQWavesPerBlock;
+  const int64_t per_block = static_cast<int64_t>(kQWavesPerBlock) * kQGroupsPerWave;
+  const int64_t blocks = (items + per_block - 1) / per_block;
   hipLaunchKernelGGL(quantize_groups_kernel, dim3(static_cast<unsigned>(blocks)),
                      dim3(kQWavesPerBlock * kWave), 0, stream, A, rows, K, Q, S);
   return hipGetLastError();
