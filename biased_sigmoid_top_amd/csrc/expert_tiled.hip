@@ -221,6 +221,7 @@ void expert_tiled_kernel(
   }
   // FP8 scales of one K group, and the units of the accumulators.
   constexpr int kG = T::K / 128;
+  constexpr float kFltMin = 1.17549435e-38f;  // smallest normal fp32
   float xs[FP8 ? TB : 1], wsa[FP8 ? FB : 1], wsb[FP8 ? FB : 1];
   float unit[FP8 ? TB : 1][FP8 ? FB : 1][2];
   auto load_scales = [&](int g) {
@@ -249,6 +250,9 @@ void expert_tiled_kernel(
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           k[h] = sc[h] != 0.f ? unit[tb][f][h] * __builtin_amdgcn_rcpf(sc[h]) : 1.f;
+          // A subnormal scale product would overflow the reciprocal: there
+          // (rarely, per lane) the ratio is an IEEE division.
+          if (sc[h] != 0.f && !(sc[h] >= kFltMin)) k[h] = unit[tb][f][h] / sc[h];
           unit[tb][f][h] = sc[h] != 0.f ? sc[h] : unit[tb][f][h];
         }
 #pragma unroll
