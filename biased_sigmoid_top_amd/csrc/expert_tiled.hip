@@ -33,10 +33,11 @@
 // of pack_fp8.hip, one 1 KB fragment per 32-row block and K stage, widened
 // to bf16 in registers before each MFMA; the token rows are the bf16 values
 // of their E4M3 codes (quant.hip).  Each 128-wide K group -- one pass of the
-// four-stage loop -- is accumulated on its own (products of codes, exact,
-// summed in fp32) and added into the result times weight block scale x the
-// token row's scale, as the block-scaled format defines.  That second set of
-// accumulators leaves room for one weight block per wavefront only.
+// four-stage loop -- adds its products of codes (exact, summed in fp32)
+// times weight block scale x the token row's scale, as the block-scaled
+// format defines, through one accumulator set kept in units of the current
+// group's scale product (see the kernel), so the FP8 mode takes the same
+// tile shapes as the bf16 one.
 //
 // Grid: workgroup ids are dealt to the 8 XCDs round-robin.  Tiles are
 // launched in groups of m-tiles x column tiles that hold a multiple of 8
