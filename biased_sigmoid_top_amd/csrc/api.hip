@@ -45,9 +45,9 @@ void region_sizes(int64_t N, size_t (&sz)[LFM_MOE_WS_REGIONS]) {
   sz[LFM_MOE_WS_ROUTER_PARTIAL] = route_partial_bytes(N);
   // FP8 grouped path only: quantised rows and their per-128 group scales.
   const bool fp8_grouped = N > LFM_MOE_FP8_STREAM_TOKENS;
-  sz[LFM_MOE_WS_XQ] = fp8_grouped ? n * kHidden * sizeof(uint16_t) : 0;
+  sz[LFM_MOE_WS_XQ] = fp8_grouped ? n * kHidden : 0;  // one byte per code
   sz[LFM_MOE_WS_XS] = fp8_grouped ? n * (kHidden / 128) * sizeof(float) : 0;
-  sz[LFM_MOE_WS_HQ] = fp8_grouped ? rows * kFF * sizeof(uint16_t) : 0;
+  sz[LFM_MOE_WS_HQ] = fp8_grouped ? rows * kFF : 0;
   sz[LFM_MOE_WS_HS] = fp8_grouped ? rows * (kFF / 128) * sizeof(float) : 0;
 }
 
@@ -444,9 +444,9 @@ lfm_moe_status run_fp8(const uint16_t* X, const uint16_t* W_r, const float* bias
     // gate/up, H quantised per group (timed with down), down.
     int32_t* offsets = region<int32_t>(ws, N, LFM_MOE_WS_OFFSETS);
     int32_t* row2slot = region<int32_t>(ws, N, LFM_MOE_WS_ROW2SLOT);
-    uint16_t* Xq = region<uint16_t>(ws, N, LFM_MOE_WS_XQ);
+    uint8_t* Xq = region<uint8_t>(ws, N, LFM_MOE_WS_XQ);
     float* Xs = region<float>(ws, N, LFM_MOE_WS_XS);
-    uint16_t* Hq = region<uint16_t>(ws, N, LFM_MOE_WS_HQ);
+    uint8_t* Hq = region<uint8_t>(ws, N, LFM_MOE_WS_HQ);
     float* Hs = region<float>(ws, N, LFM_MOE_WS_HS);
     if ((e = launch_dispatch(idx, blockcounts, offsets, row2slot, n, stream)) != hipSuccess)
       return hip_fail(e, "dispatch kernel launch");

@@ -29,15 +29,20 @@
 // block are 16 gate rows and the matching 16 up rows, so the SiLU product
 // is formed in registers.
 //
-// FP8 mode (the FP8 layer above 256 tokens): the weights are the FP8 codes
-// of pack_fp8.hip, one 1 KB fragment per 32-row block and K stage, widened
-// to bf16 in registers before each MFMA; the token rows are the bf16 values
-// of their E4M3 codes (quant.hip).  Each 128-wide K group -- one pass of the
-// four-stage loop -- adds its products of codes (exact, summed in fp32)
+// FP8 mode (the FP8 layer above 256 tokens): the products run on the gfx950
+// FP8 matrix core (32x32x64 E4M3).  The weights are the FP8 codes of
+// pack_fp8.hip (two 1 KB fragments per 32-row block and 64-wide K stage),
+// the token rows their E4M3 codes from quant.hip, whose byte order makes a
+// stage's 64 code bytes of a row land in LDS exactly where 32 bf16 columns
+// land in bf16 mode, so staging, swizzle and operand reads are shared.  A
+// stage pair is one 128-wide K group, which adds its products of codes
 // times weight block scale x the token row's scale, as the block-scaled
 // format defines, through one accumulator set kept in units of the current
-// group's scale product (see the kernel), so the FP8 mode takes the same
-// tile shapes as the bf16 one.
+// group's scales (see the kernel), so the FP8 mode takes the bf16 mode's
+// tile shapes with half the stages.  The core's sums are not fp32 sums of
+// the exact products: it aligns a step's 64 products and drops the bits
+// below the alignment (measured: within 2^-11.6 of the sum of their
+// magnitudes).
 //
 // Grid: workgroup ids are dealt to the 8 XCDs round-robin.  Tiles are
 // launched in groups of m-tiles x column tiles that hold a multiple of 8
@@ -91,39 +96,71 @@ struct TileShape {
   // m-tiles per launch group: a group holds a multiple of kXcds tiles.
   static constexpr int kGroup =
       kXcds / (kColTiles % kXcds == 0 ? kXcds : kColTiles % 4 == 0 ? 4 : kColTiles % 2 == 0 ? 2 : 1);
-  static constexpr int kStages = K / kBK;
   static_assert(kBlocks % kBlocksPerTile == 0, "column tiles cover the weight rows");
   static_assert(kGroup * kColTiles % kXcds == 0, "a launch group deals evenly over the XCDs");
 };
 
-// FP8: Wp holds the FP8 codes of the experts (pack_fp8.hip layout: 1 KB
-// fragments of 32 rows x 32 K, one per K stage), Ws their fp32 block scales,
-// A the bf16 values of the token rows' E4M3 codes and As the rows' scales per
-// 128-wide K group.  A group of four stages (128 K) adds its products times
-// weight scale x token scale.  One accumulator set serves all groups: it
-// holds the sum so far in units of the current group's scale product (one
-// per token column and, for gate/up, per gate or up half), so before each
-// group it is multiplied by old unit / new unit, and at the end by the last
-// unit.  (Where a scale is 0 the group's codes are all 0, and the unit
-// stays.)  The products are exact and the sums fp32, as with a second
-// accumulator set per group, up to the rounding of the unit changes (a few
-// fp32 ulps per group; the ratio uses the hardware reciprocal).
+// D = A * B + C on a 32x32 tile with K = 64 on the FP8 matrix core (E4M3
+// codes in, fp32 out).  Lane l supplies 32 codes of row l % 32 of A (a0, then
+// a1) and 32 codes of column l % 32 of B (b0, then b1); byte i of a lane's A
+// and byte i of B in a lane of the same half (l / 32) meet the same K, so
+// both operands only need their bytes in one common order.  Accumulator
+// layout as mfma32.  (Zero scale operands select the unscaled instruction.)
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x16 mfma32_fp8(const uint4& a0, const uint4& a1, const uint4& b0,
+                                             const uint4& b1, f32x16 c) {
+  const i32x8 a = {static_cast<int>(a0.x), static_cast<int>(a0.y), static_cast<int>(a0.z),
+                   static_cast<int>(a0.w), static_cast<int>(a1.x), static_cast<int>(a1.y),
+                   static_cast<int>(a1.z), static_cast<int>(a1.w)};
+  const i32x8 b = {static_cast<int>(b0.x), static_cast<int>(b0.y), static_cast<int>(b0.z),
+                   static_cast<int>(b0.w), static_cast<int>(b1.x), static_cast<int>(b1.y),
+                   static_cast<int>(b1.z), static_cast<int>(b1.w)};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// FP8 mode: Wp holds the FP8 codes of the experts (pack_fp8.hip layout: 1 KB
+// fragments of 32 rows x 32 K, lane l's 16 bytes columns 8h..8h+7 and
+// 16+8h..16+8h+7 of row l % 32, h = l / 32), Ws their fp32 block scales, A
+// the token rows' E4M3 codes (quant.hip, whose byte order puts those same
+// columns in 16-byte chunk 2p + h of each 32-wide piece p) and As the rows'
+// scales per 128-wide K group.  A stage is 64 K: two fragments per block and
+// the 64 code bytes of each token row, which the LDS tile holds exactly as it
+// holds 32 bf16 columns, so one FP8 MFMA takes the stage's two K halves at
+// once.  A stage pair is one 128-wide K group, whose products of codes must
+// be multiplied by weight block scale x token scale.  One accumulator set
+// serves all groups: it holds the sum so far in units of the current group's
+// scales -- a token unit per token column and a weight unit per block (and
+// gate or up half) -- so at the start of each group the sums are multiplied
+// by old unit / new unit, and at the end by the last units.  Where a scale
+// is 0 the group's codes are all 0, and that unit stays.  The scales of a
+// tile are staged in LDS once, before the stage loop.
 template <bool GATEUP, int FB_, int WAVES_, int TB_, bool FP8 = false, bool NTW = false>
 __global__ __launch_bounds__((TileShape<GATEUP, FB_, WAVES_, TB_>::kThreads),
                              (TileShape<GATEUP, FB_, WAVES_, TB_>::kPerCu))
 void expert_tiled_kernel(
-    const uint16_t* __restrict__ A, const void* __restrict__ Wp,
+    const void* __restrict__ A, const void* __restrict__ Wp,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ row2slot,
     uint16_t* __restrict__ H, float* __restrict__ Y, const float* __restrict__ Ws,
     const float* __restrict__ As) {
   using T = TileShape<GATEUP, FB_, WAVES_, TB_>;
   constexpr int FB = T::FB;
   constexpr int TB = T::kTB;
-  constexpr int kWK = FP8 ? 1 : kKS;  // 16-byte weight loads per block and stage
-  static_assert(!FP8 || kWSlots * kBK == 128, "an FP8 scale group is one pass of the stage loop");
-  static_assert(T::kStages % kWSlots == 0, "the stage loop is unrolled by the ring size");
+  // K per stage: 32 bf16 or 64 E4M3 columns, 64 bytes of a token row either way.
+  constexpr int kStageK = FP8 ? 2 * kBK : kBK;
+  constexpr int kStages = T::K / kStageK;
+  constexpr int kRowBytes = T::K * (FP8 ? 1 : 2);
+  static_assert(kStages % kWSlots == 0, "the stage loop is unrolled by the ring size");
+  static_assert(!FP8 || 2 * kStageK == 128, "an FP8 scale group is one stage pair");
   // Token fragments: 2 pair buffers x (2 stages x 4 token blocks x kKS steps).
   __shared__ uint4 tok[2][2 * TB * kKS * kWave];
+  // FP8 scales of the tile: the token rows' ([group][tile row]) and the
+  // weight blocks' ([wavefront][block][gate | up][group]).
+  constexpr int kG = T::K / 128;
+  constexpr int kH = GATEUP ? 2 : 1;
+  constexpr int kWsPerWave = FB * kH * kG;
+  __shared__ float xs_lds[FP8 ? kG * T::kBM : 1];
+  __shared__ float ws_lds[FP8 ? T::kWaves * kWsPerWave : 1];
+  static_assert(!FP8 || (T::kThreads % T::kBM == 0 && kWsPerWave <= kWave), "scale staging");
 
   // Launch groups of kGroup m-tiles x kColTiles column tiles; workgroup ids
   // are dealt to the XCDs round-robin, so id w of a group runs on XCD w % 8.
@@ -149,17 +186,19 @@ void expert_tiled_kernel(
   // lanes read one whole line.  All the pieces share c and r0 % 32, so their
   // LDS positions differ by whole token-block fragments.
   const int r0 = tid / 8, c = tid % 8;
-  const uint16_t* arow[T::kChunks];
+  const uint8_t* arow[T::kChunks];
 #pragma unroll
   for (int i = 0; i < T::kChunks; ++i) {
     const int r = r0 + T::kRowStep * i;
     const int slot = row2slot[tile.row_begin + (r < tile.rows ? r : 0)];
-    arow[i] = A + static_cast<size_t>(GATEUP ? slot / kTopK : slot) * T::K + c * 8;
+    arow[i] = static_cast<const uint8_t*>(A) +
+              static_cast<size_t>(GATEUP ? slot / kTopK : slot) * kRowBytes + c * 16;
   }
   const int st_pos = ((c / 4) * TB * kKS + (c / 2) % 2) * kWave + (c % 2) * 32 + ((r0 % 32) ^ swz(c)) +
                      (r0 / 32) * kKS * kWave;
   static_assert(T::kRowStep % 32 == 0, "a thread's pieces share their row within a token block");
-  // MFMA operand position of this lane for stage sp of a pair, K step j.
+  // MFMA operand position of this lane for stage sp of a pair, K step (bf16)
+  // or K half (FP8) j.
   int rd_pos[2][kKS];
 #pragma unroll
   for (int sp = 0; sp < 2; ++sp)
@@ -167,33 +206,56 @@ void expert_tiled_kernel(
     for (int j = 0; j < kKS; ++j)
       rd_pos[sp][j] = (sp * TB * kKS + j) * kWave + (lane & 32) + ((lane & 31) ^ swz(sp * 4 + j * 2 + lane / 32));
 
-  // This wavefront's FB packed row blocks, K steps of a block contiguous,
-  // read as buffer loads: the expert's packed matrix (12 MB at most) is the
-  // buffer, the wavefront's first block a scalar offset, the lane's 16 bytes
-  // of a fragment the only per-lane offset.
-  constexpr uint32_t kBlockBytes = static_cast<uint32_t>(T::kStages * kWK) * kFragBytes;
+  // This wavefront's FB packed row blocks, the fragments of a block
+  // contiguous (two per stage), read as buffer loads: the expert's packed
+  // matrix (12 MB at most) is the buffer, the wavefront's first block a
+  // scalar offset, the lane's 16 bytes of a fragment the only per-lane offset.
+  constexpr uint32_t kBlockBytes = static_cast<uint32_t>(kStages * kKS) * kFragBytes;
   const Rsrc wr = make_rsrc(static_cast<const uint8_t*>(Wp) +
                                 static_cast<size_t>(uniform(tile.expert)) * T::kBlocks * kBlockBytes,
                             T::kBlocks * kBlockBytes);
   const uint32_t wbase = uniform(static_cast<uint32_t>((nb * T::kBlocksPerTile + wave * FB) * kBlockBytes));
   const uint32_t wlane = lane * 16;
 
-  uint4 wring[kWSlots][FB][kWK];
+  // FP8 scales, loaded first (stored to LDS with the first token pieces):
+  // thread tid takes entries tid + kThreads * i of [group][tile row] (one
+  // tile row: padding rows take row 0's scales, and their results are
+  // dropped), lane l < kWsPerWave entry l of its wavefront's weight scales.
+  constexpr int kXsPer = FP8 ? kG * T::kBM / T::kThreads : 1;
+  float xs_st[kXsPer];
+  float ws_st = 0.f;
+  if constexpr (FP8) {
+    const int r = tid % T::kBM;
+    const int slot = row2slot[tile.row_begin + (r < tile.rows ? r : 0)];
+    const float* src = As + static_cast<size_t>(GATEUP ? slot / kTopK : slot) * kG;
+#pragma unroll
+    for (int i = 0; i < kXsPer; ++i) xs_st[i] = src[(tid + T::kThreads * i) / T::kBM];
+    if (lane < kWsPerWave) {
+      const int f = lane / (kH * kG), h = lane / kG % kH, g = lane % kG;
+      const int blk = nb * T::kBlocksPerTile + wave * FB + f;
+      const int e = uniform(tile.expert);
+      // gate/up: [expert][gate | up][128-row block][group]; down: [expert][128-row block][group]
+      ws_st = GATEUP ? Ws[((e * 2 + h) * (kFF / 128) + blk / 8) * kG + g]
+                     : Ws[(e * (kHidden / 128) + blk / 4) * kG + g];
+    }
+  }
+
+  uint4 wring[kWSlots][FB][kKS];
   // Stages past the end reload the last stage (in bounds, never used).
-  auto load_w = [&](int s, uint4 (&wv)[FB][kWK]) {
-    const uint32_t sc = s < T::kStages ? s : T::kStages - 1;
+  auto load_w = [&](int s, uint4 (&wv)[FB][kKS]) {
+    const uint32_t sc = s < kStages ? s : kStages - 1;
 #pragma unroll
     for (int f = 0; f < FB; ++f)
 #pragma unroll
-      for (int j = 0; j < kWK; ++j)
-        wv[f][j] = buf_ld<NTW>(wr, wlane, wbase + f * kBlockBytes + (sc * kWK + j) * kFragBytes);
+      for (int j = 0; j < kKS; ++j)
+        wv[f][j] = buf_ld<NTW>(wr, wlane, wbase + f * kBlockBytes + (sc * kKS + j) * kFragBytes);
   };
-  constexpr int kPairs = T::kStages / 2;
+  constexpr int kPairs = kStages / 2;
   uint4 stg[T::kChunks];
   auto load_x = [&](int pair) {
     const int pc = pair < kPairs ? pair : kPairs - 1;
 #pragma unroll
-    for (int i = 0; i < T::kChunks; ++i) stg[i] = ld16(arow[i] + pc * (kPairBytes / 2));
+    for (int i = 0; i < T::kChunks; ++i) stg[i] = ld16(arow[i] + pc * kPairBytes);
   };
   auto store_x = [&](int pb) {
 #pragma unroll
@@ -208,153 +270,183 @@ void expert_tiled_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[tb][f][r] = 0.f;
 
-  // FP8 scales: this wavefront's weight row blocks (128 rows) and the
-  // tile rows' token rows (padding rows take row 0's; their results are
-  // dropped).
-  int srow[FP8 ? TB : 1];
-  if constexpr (FP8) {
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      const int row = tb * 32 + lane % 32;
-      const int slot = row2slot[tile.row_begin + (row < tile.rows ? row : 0)];
-      srow[tb] = GATEUP ? slot / kTopK : slot;
-    }
-  }
-  // FP8 scales of one K group, and the units of the accumulators.
-  constexpr int kG = T::K / 128;
-  constexpr float kFltMin = 1.17549435e-38f;  // smallest normal fp32
-  float xs[FP8 ? TB : 1], wsa[FP8 ? FB : 1], wsb[FP8 ? FB : 1];
-  float unit[FP8 ? TB : 1][FP8 ? FB : 1][2];
-  auto load_scales = [&](int g) {
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) xs[tb] = As[static_cast<size_t>(srow[tb]) * kG + g];
-    const int e = uniform(tile.expert);
-#pragma unroll
-    for (int f = 0; f < FB; ++f) {
-      const int blk = nb * T::kBlocksPerTile + wave * FB + f;
-      if (GATEUP) {  // gate rows (values r < 8 of a tile) and up rows
-        wsa[f] = Ws[((e * 2 + 0) * (kFF / 128) + blk / 8) * kG + g];
-        wsb[f] = Ws[((e * 2 + 1) * (kFF / 128) + blk / 8) * kG + g];
-      } else {
-        wsa[f] = wsb[f] = Ws[(e * (kHidden / 128) + blk / 4) * kG + g];
-      }
-    }
-  };
-  // Re-expresses the sums in units of the scales last loaded.
-  auto rebase = [&] {
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-      for (int f = 0; f < FB; ++f) {
-        const float sc[2] = {wsa[f] * xs[tb], wsb[f] * xs[tb]};
-        float k[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          k[h] = sc[h] != 0.f ? unit[tb][f][h] * __builtin_amdgcn_rcpf(sc[h]) : 1.f;
-          // A subnormal scale product would overflow the reciprocal: there
-          // (rarely, per lane) the ratio is an IEEE division.
-          if (sc[h] != 0.f && !(sc[h] >= kFltMin)) k[h] = unit[tb][f][h] / sc[h];
-          unit[tb][f][h] = sc[h] != 0.f ? sc[h] : unit[tb][f][h];
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[tb][f][r] *= (r < 8 ? k[0] : k[1]);
-      }
-  };
-  // Group 0's scales go first, so that waiting for them leaves the ring's
-  // loads in flight.
-  if constexpr (FP8) {
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-      for (int f = 0; f < FB; ++f) unit[tb][f][0] = unit[tb][f][1] = 1.f;
-    load_scales(0);
-  }
 #pragma unroll
   for (int s = 0; s < kWSlots - 1; ++s) load_w(s, wring[s]);
   load_x(0);
+  if constexpr (FP8) {
+#pragma unroll
+    for (int i = 0; i < kXsPer; ++i) xs_lds[tid + T::kThreads * i] = xs_st[i];
+    if (lane < kWsPerWave) ws_lds[wave * kWsPerWave + lane] = ws_st;
+  }
   store_x(0);
   load_x(1);
   __syncthreads();
 
-  // Token operands, double-buffered: tk[x] holds the four token-block
-  // fragments of one K step.
-  uint4 tk[2][TB];
-  auto read_tk = [&](int pb, int sp, int j, uint4 (&d)[TB]) {
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) d[tb] = tok[pb][rd_pos[sp][j] + tb * kKS * kWave];
-  };
-  // Gate/up skips the MFMAs of 32-row token blocks that are all padding
-  // (the last m-tile of an expert); in the down kernel the branches cost
-  // more registers than it has.
-  auto mma = [&](const uint4 (&wj)[FB][kWK], int j, const uint4 (&d)[TB]) {
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
-      if (!GATEUP || tb == 0 || tb * 32 < live_rows)
-#pragma unroll
-        for (int f = 0; f < FB; ++f) {
-          if constexpr (FP8) {
-            // Lane bytes 0..7: K step 0 of the stage, 8..15: K step 1.
-            const uint4 wbf = j == 0 ? e4m3x8_to_bf16(wj[f][0].x, wj[f][0].y)
-                                     : e4m3x8_to_bf16(wj[f][0].z, wj[f][0].w);
-            acc[tb][f] = mfma32(wbf, d[tb], acc[tb][f]);
-          } else {
-            acc[tb][f] = mfma32(wj[f][j], d[tb], acc[tb][f]);
-          }
-        }
-  };
   // The fences keep the issue order written here, which the wait counts
   // below rely on: weight loads, then the next LDS operands, then MFMAs.
   auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-  read_tk(0, 0, 0, tk[0]);
 
-  // Stage s of pair p (LDS buffer pb = p % 2) multiplies with ring slot
-  // s % 4 and loads the weights of stage s + 3 into the free slot; the LDS
-  // operands of each K step are read one step ahead.  The first stage of a
-  // pair stores the next pair's tokens (loaded one pair ago) into the other
-  // buffer, whose last readers passed the previous barrier, and loads the
-  // pair after that.  The second stage's barrier comes once its own LDS
-  // reads are done, before its last MFMAs: it publishes the stored tokens
-  // and frees buffer pb for the next store.
-  auto stage = [&](int s, int sp, int pb, uint4 (&wc)[FB][kWK], uint4 (&wn)[FB][kWK]) {
-    static_assert(kKS == 2, "two K steps per stage");
-    load_w(s + kWSlots - 1, wn);
-    read_tk(pb, sp, 1, tk[1]);
-    fence();
-    mma(wc, 0, tk[0]);
-    fence();
-    if (sp == 0) {
-      read_tk(pb, 1, 0, tk[0]);
-      fence();
-      mma(wc, 1, tk[1]);
-      fence();
-      store_x(pb ^ 1);
-      load_x(s / 2 + 2);
-      fence();
-    } else {
-      __syncthreads();
-      read_tk(pb ^ 1, 0, 0, tk[0]);
-      fence();
-      mma(wc, 1, tk[1]);
-      fence();
-    }
-  };
-  if constexpr (FP8) rebase();  // the sums are 0: this sets the units of group 0
-  for (int s = 0; s < T::kStages; s += kWSlots) {
-    // The next group's scales are loaded a group ahead (the last group loads
-    // its own again: the rebase is then exact, old unit / same unit = 1).
-    if constexpr (FP8) load_scales(min(s / kWSlots + 1, kG - 1));
+  if constexpr (!FP8) {
+    // Token operands, double-buffered: tk[x] holds the four token-block
+    // fragments of one K step.
+    uint4 tk[2][TB];
+    auto read_tk = [&](int pb, int sp, int j, uint4 (&d)[TB]) {
 #pragma unroll
-    for (int q = 0; q < kWSlots; ++q)
-      stage(s + q, q % 2, q / 2, wring[q], wring[(q + kWSlots - 1) % kWSlots]);
-    if constexpr (FP8) rebase();
-  }
-  if constexpr (FP8) {
+      for (int tb = 0; tb < TB; ++tb) d[tb] = tok[pb][rd_pos[sp][j] + tb * kKS * kWave];
+    };
+    // Gate/up skips the MFMAs of 32-row token blocks that are all padding
+    // (the last m-tile of an expert); in the down kernel the branches cost
+    // more registers than it has.
+    auto mma = [&](const uint4 (&wj)[FB][kKS], int j, const uint4 (&d)[TB]) {
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+        if (!GATEUP || tb == 0 || tb * 32 < live_rows)
+#pragma unroll
+          for (int f = 0; f < FB; ++f) acc[tb][f] = mfma32(wj[f][j], d[tb], acc[tb][f]);
+    };
+    read_tk(0, 0, 0, tk[0]);
+
+    // Stage s of pair p (LDS buffer pb = p % 2) multiplies with ring slot
+    // s % 4 and loads the weights of stage s + 3 into the free slot; the LDS
+    // operands of each K step are read one step ahead.  The first stage of a
+    // pair stores the next pair's tokens (loaded one pair ago) into the other
+    // buffer, whose last readers passed the previous barrier, and loads the
+    // pair after that.  The second stage's barrier comes once its own LDS
+    // reads are done, before its last MFMAs: it publishes the stored tokens
+    // and frees buffer pb for the next store.
+    auto stage = [&](int s, int sp, int pb, uint4 (&wc)[FB][kKS], uint4 (&wn)[FB][kKS]) {
+      static_assert(kKS == 2, "two K steps per stage");
+      load_w(s + kWSlots - 1, wn);
+      read_tk(pb, sp, 1, tk[1]);
+      fence();
+      mma(wc, 0, tk[0]);
+      fence();
+      if (sp == 0) {
+        read_tk(pb, 1, 0, tk[0]);
+        fence();
+        mma(wc, 1, tk[1]);
+        fence();
+        store_x(pb ^ 1);
+        load_x(s / 2 + 2);
+        fence();
+      } else {
+        __syncthreads();
+        read_tk(pb ^ 1, 0, 0, tk[0]);
+        fence();
+        mma(wc, 1, tk[1]);
+        fence();
+      }
+    };
+    for (int s = 0; s < kStages; s += kWSlots) {
+#pragma unroll
+      for (int q = 0; q < kWSlots; ++q)
+        stage(s + q, q % 2, q / 2, wring[q], wring[(q + kWSlots - 1) % kWSlots]);
+    }
+  } else {
+    // Token operands of one token block (both K halves), double-buffered by
+    // token block: the operands of block tb + 1 (or of the next stage's
+    // block 0) are read while block tb multiplies.
+    uint4 tk[2][kKS];
+    auto read_tk = [&](int pb, int sp, int tb, uint4 (&d)[kKS]) {
+#pragma unroll
+      for (int j = 0; j < kKS; ++j) d[j] = tok[pb][rd_pos[sp][j] + tb * kKS * kWave];
+    };
+    // Scales of group g: the lane's token rows, the wavefront's blocks (the
+    // same in every lane: kept in scalar registers).
+    float xn[TB], wn[FB][kH];
+    auto read_scales = [&](int g) {
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) xn[tb] = xs_lds[g * T::kBM + tb * 32 + lane % 32];
+#pragma unroll
+      for (int f = 0; f < FB; ++f)
+#pragma unroll
+        for (int h = 0; h < kH; ++h)
+          wn[f][h] = __int_as_float(__builtin_amdgcn_readfirstlane(
+              __float_as_int(ws_lds[wave * kWsPerWave + (f * kH + h) * kG + g])));
+    };
+    // Units: where a scale is 0 the unit stays (that group adds nothing).
+    constexpr float kFltMin = 1.17549435e-38f;  // smallest normal fp32
+    auto ratio = [](float& u, float s) {
+      float k = 1.f;
+      if (s != 0.f) {
+        k = u * __builtin_amdgcn_rcpf(s);
+        // A subnormal scale would overflow the reciprocal: there (rarely,
+        // per lane) the ratio is an IEEE division.
+        if (!(s >= kFltMin)) k = u / s;
+        u = s;
+      }
+      return k;
+    };
+    float ux[TB], uw[FB][kH];
+    read_scales(0);
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) ux[tb] = xn[tb] != 0.f ? xn[tb] : 1.f;
+#pragma unroll
+    for (int f = 0; f < FB; ++f)
+#pragma unroll
+      for (int h = 0; h < kH; ++h) uw[f][h] = wn[f][h] != 0.f ? wn[f][h] : 1.f;
+    read_tk(0, 0, 0, tk[0]);
+
+    // Stage s of pair p (LDS buffer pb = p % 2; pair p is scale group p)
+    // multiplies with ring slot s % 4 and loads the weights of stage s + 3
+    // into the free slot.  The first stage of a pair reads the group's
+    // scales and re-expresses the sums in its units (each token block just
+    // before its MFMAs), stores the next pair's tokens (loaded one pair ago)
+    // into the other buffer, whose last readers passed the previous barrier,
+    // and loads the pair after that.  The second stage's barrier, before its
+    // first read of the next pair's buffer, publishes the stored tokens and
+    // frees buffer pb for the next store.
+    auto stage = [&](int s, int sp, int pb, uint4 (&wc)[FB][kKS], uint4 (&wnext)[FB][kKS]) {
+      load_w(s + kWSlots - 1, wnext);
+      float kx[TB], kw[FB][kH];
+      if (sp == 0) {
+        read_scales(s / 2);
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) kx[tb] = ratio(ux[tb], xn[tb]);
+#pragma unroll
+        for (int f = 0; f < FB; ++f)
+#pragma unroll
+          for (int h = 0; h < kH; ++h) kw[f][h] = ratio(uw[f][h], wn[f][h]);
+      }
+      fence();
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        if (tb + 1 < TB) {
+          read_tk(pb, sp, tb + 1, tk[(tb + 1) % 2]);
+        } else {
+          if (sp == 1) __syncthreads();
+          read_tk(sp == 0 ? pb : pb ^ 1, sp ^ 1, 0, tk[0]);
+        }
+        fence();
+        if (!GATEUP || tb == 0 || tb * 32 < live_rows) {
+#pragma unroll
+          for (int f = 0; f < FB; ++f) {
+            if (sp == 0) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) acc[tb][f][r] *= kx[tb] * kw[f][GATEUP && r >= 8 ? 1 : 0];
+            }
+            acc[tb][f] = mfma32_fp8(wc[f][0], wc[f][1], tk[tb % 2][0], tk[tb % 2][1], acc[tb][f]);
+          }
+        }
+        fence();
+      }
+      if (sp == 0) {
+        store_x(pb ^ 1);
+        load_x(s / 2 + 2);
+        fence();
+      }
+    };
+    for (int s = 0; s < kStages; s += kWSlots) {
+#pragma unroll
+      for (int q = 0; q < kWSlots; ++q)
+        stage(s + q, q % 2, q / 2, wring[q], wring[(q + kWSlots - 1) % kWSlots]);
+    }
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
       for (int f = 0; f < FB; ++f)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[tb][f][r] *= unit[tb][f][r < 8 ? 0 : 1];
+        for (int r = 0; r < 16; ++r) acc[tb][f][r] *= ux[tb] * uw[f][GATEUP && r >= 8 ? 1 : 0];
   }
 
   // acc[tb][f]: token row tb*32 + lane % 32 of the tile; rows
@@ -446,7 +538,7 @@ DownTiles down_tiles(int64_t N) {
 
 template <bool GATEUP, int FB, int WAVES = (GATEUP ? 8 : 4), int TB = 4, bool FP8 = false,
           bool NTW = false, typename Out>
-hipError_t launch_tiled(const uint16_t* A, const void* W, const int32_t* offsets,
+hipError_t launch_tiled(const void* A, const void* W, const int32_t* offsets,
                         const int32_t* row2slot, Out* out, int64_t N, hipStream_t stream,
                         const float* Ws = nullptr, const float* As = nullptr) {
   uint16_t* H = nullptr;
@@ -489,7 +581,7 @@ hipError_t launch_down_tiled(const uint16_t* H, const uint16_t* Wd, const int32_
   }
 }
 
-hipError_t launch_gateup_tiled_fp8(const uint16_t* Xq, const uint8_t* Wq, const float* Ws,
+hipError_t launch_gateup_tiled_fp8(const uint8_t* Xq, const uint8_t* Wq, const float* Ws,
                                    const float* Xs, const int32_t* offsets, const int32_t* row2slot,
                                    uint16_t* H, int64_t N, hipStream_t stream) {
   switch (gateup_tiles(N)) {
@@ -503,7 +595,7 @@ hipError_t launch_gateup_tiled_fp8(const uint16_t* Xq, const uint8_t* Wq, const 
   }
 }
 
-hipError_t launch_down_tiled_fp8(const uint16_t* Hq, const uint8_t* Wq, const float* Ws,
+hipError_t launch_down_tiled_fp8(const uint8_t* Hq, const uint8_t* Wq, const float* Ws,
                                  const float* Hs, const int32_t* offsets, const int32_t* row2slot,
                                  float* Y, int64_t N, hipStream_t stream) {
   switch (down_tiles(N)) {

@@ -52,15 +52,15 @@ hipError_t launch_gateup_decode_fp8(const uint16_t* X, const uint8_t* Wq, const 
 hipError_t launch_down_decode_fp8(const uint16_t* H, const uint8_t* Wq, const float* scales,
                                   const int32_t* idx, float* Y, int N, hipStream_t stream);
 
-// FP8 grouped path: rows quantised per 128-wide group (codes stored as their
-// bf16 values, fp32 scales [rows][K / 128]), then the tiled kernels in FP8
-// mode.
-hipError_t launch_quantize_groups(const uint16_t* A, int64_t rows, int K, uint16_t* Q, float* S,
+// FP8 grouped path: rows quantised per 128-wide group (E4M3 codes, one byte
+// each, in the run order of quant.hip; fp32 scales [rows][K / 128]), then
+// the tiled kernels in FP8 mode (the FP8 matrix cores).
+hipError_t launch_quantize_groups(const uint16_t* A, int64_t rows, int K, uint8_t* Q, float* S,
                                   hipStream_t stream);
-hipError_t launch_gateup_tiled_fp8(const uint16_t* Xq, const uint8_t* Wq, const float* Ws,
+hipError_t launch_gateup_tiled_fp8(const uint8_t* Xq, const uint8_t* Wq, const float* Ws,
                                    const float* Xs, const int32_t* offsets, const int32_t* row2slot,
                                    uint16_t* H, int64_t N, hipStream_t stream);
-hipError_t launch_down_tiled_fp8(const uint16_t* Hq, const uint8_t* Wq, const float* Ws,
+hipError_t launch_down_tiled_fp8(const uint8_t* Hq, const uint8_t* Wq, const float* Ws,
                                  const float* Hs, const int32_t* offsets, const int32_t* row2slot,
                                  float* Y, int64_t N, hipStream_t stream);
 

@@ -1,6 +1,8 @@
 // FP8 (E4M3) block quantisation of the expert weights, packed into the
 // operand-fragment layout of the 32x32x16 MFMAs (each lane's 8 codes of a
-// 16-wide K step are its operand, widened to bf16 in registers).
+// 16-wide K step are its operand, widened to bf16 in registers by the
+// weight-streaming kernels); two consecutive fragments give a lane its 32
+// codes of a 32x32x64 FP8 MFMA (the grouped kernels).
 //
 // Method: the inferencekey.com page on the 24B reasoning MoE (German
 // edition, "Für Engineers" part, the quantisation entry) describes the

@@ -8,8 +8,15 @@
 // amax)) in fp32 (round to nearest even, the sign of a zero kept) with the
 // scale amax / 448; amax = 0 gives zero codes and scale 0 -- the same
 // arithmetic as the weight-streaming FP8 kernels, which quantise in
-// registers.  The codes are stored as their bf16 values (every E4M3 value is
-// a bf16 value), so the grouped kernels stage them as they stage bf16 rows.
+// registers.
+//
+// Code layout (one byte per value, row pitch K bytes): within each 32-wide
+// piece of a row the 8-code runs are stored in the order 0, 2, 1, 3, so
+// that 16-byte chunk 2p + h of the row holds columns 32p + 8h .. + 7 and
+// 32p + 16 + 8h .. + 7 -- the columns that lane half h of an FP8 matrix-core
+// operand meets in the packed weight fragments (pack_fp8.hip).  The grouped
+// kernels stage these chunks exactly as they stage 16-byte chunks of bf16
+// rows.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -22,11 +29,11 @@ constexpr int kQLanesPerGroup = kQGroup / 8;               // 8 values (16 bytes
 constexpr int kQGroupsPerWave = kWave / kQLanesPerGroup;   // 4
 constexpr int kQWavesPerBlock = 4;
 
-// Four consecutive (row, group) items per wavefront, 16 lanes per item, 16
-// bytes per lane.  Rows have a multiple of four groups (K = 2048 or 1536),
+// Four consecutive (row, group) items per wavefront, 16 lanes per item, 8
+// values per lane.  Rows have a multiple of four groups (K = 2048 or 1536),
 // so a wavefront's items share one row.
 __global__ __launch_bounds__(kQWavesPerBlock * kWave) void quantize_groups_kernel(
-    const uint16_t* __restrict__ A, int64_t rows, int K, uint16_t* __restrict__ Q,
+    const uint16_t* __restrict__ A, int64_t rows, int K, uint8_t* __restrict__ Q,
     float* __restrict__ S) {
   const int groups = K / kQGroup;
   const int lane = threadIdx.x % kWave;
@@ -35,8 +42,9 @@ __global__ __launch_bounds__(kQWavesPerBlock * kWave) void quantize_groups_kerne
   if (item >= rows * groups) return;
   const int64_t row = item / groups;
   const int g = static_cast<int>(item % groups);
-  const size_t at = static_cast<size_t>(row) * K + g * kQGroup + 8 * (lane % kQLanesPerGroup);
-  const uint4 v = *reinterpret_cast<const uint4*>(A + at);
+  const int run = lane % kQLanesPerGroup;  // 8-value run of the group
+  const size_t at = static_cast<size_t>(row) * K + g * kQGroup;
+  const uint4 v = *reinterpret_cast<const uint4*>(A + at + 8 * run);
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   // Largest magnitude of the group on the bf16 bit patterns (finite values
   // order as their bits), then over the group's 16 lanes.
@@ -51,13 +59,15 @@ __global__ __launch_bounds__(kQWavesPerBlock * kWave) void quantize_groups_kerne
     return e4m3x4(__uint_as_float(lo << 16) * inv, __uint_as_float(lo & 0xffff0000u) * inv,
                   __uint_as_float(hi << 16) * inv, __uint_as_float(hi & 0xffff0000u) * inv);
   };
-  *reinterpret_cast<uint4*>(Q + at) = e4m3x8_to_bf16(q4(w[0], w[1]), q4(w[2], w[3]));
-  if (lane % kQLanesPerGroup == 0) S[static_cast<size_t>(row) * groups + g] = amax / 448.f;
+  // Run r of a 32-wide piece (r = run % 4) goes to 8-byte slot 0, 2, 1, 3.
+  const int slot = (run & ~3) | ((run & 1) << 1) | ((run >> 1) & 1);
+  *reinterpret_cast<uint2*>(Q + at + 8 * slot) = make_uint2(q4(w[0], w[1]), q4(w[2], w[3]));
+  if (run == 0) S[static_cast<size_t>(row) * groups + g] = amax / 448.f;
 }
 
 }  // namespace
 
-hipError_t launch_quantize_groups(const uint16_t* A, int64_t rows, int K, uint16_t* Q, float* S,
+hipError_t launch_quantize_groups(const uint16_t* A, int64_t rows, int K, uint8_t* Q, float* S,
                                   hipStream_t stream) {
   const int64_t items = rows * (K / kQGroup);
   const int64_t per_block = static_cast<int64_t>(kQWavesPerBlock) * kQGroupsPerWave;

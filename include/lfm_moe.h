@@ -189,10 +189,11 @@ typedef enum {
   LFM_MOE_WS_X = 7,         /* [N, 2048] bf16 normalised input (block forward only) */
   LFM_MOE_WS_ROUTER_PARTIAL = 8, /* [ceil(N/16), 16, 16, 64] fp32 router partial logits per K slice;
                                     empty above 2048 tokens, where the router keeps them in LDS */
-  LFM_MOE_WS_XQ = 9,        /* [N, 2048] bf16: the values of X's E4M3 codes per 128-wide group
-                               (FP8 layer above LFM_MOE_FP8_STREAM_TOKENS only) */
+  LFM_MOE_WS_XQ = 9,        /* [N, 2048] uint8: X's E4M3 codes per 128-wide group (FP8 layer above
+                               LFM_MOE_FP8_STREAM_TOKENS only); in each 32-wide piece of a row the
+                               8-code runs are stored in the order 0, 2, 1, 3 */
   LFM_MOE_WS_XS = 10,       /* [N, 16] fp32: their scales */
-  LFM_MOE_WS_HQ = 11,       /* [4N, 1536] bf16: the values of H's E4M3 codes, slot order (same) */
+  LFM_MOE_WS_HQ = 11,       /* [4N, 1536] uint8: H's E4M3 codes, slot order (same layout and condition) */
   LFM_MOE_WS_HS = 12,       /* [4N, 12] fp32: their scales */
   LFM_MOE_WS_REGIONS = 13
 } lfm_moe_ws_region;

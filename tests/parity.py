@@ -16,6 +16,42 @@ import oracle
 MARGIN = 1e-4
 OUT_GATE = 2e-2
 W_ATOL = 2e-6  # fp32 sigmoid + normalisation vs float64
+# The FP8 layer's grouped kernels multiply on the gfx950 FP8 matrix core
+# (32x32x64 E4M3), whose sums are not fp32 sums of the exact products: it
+# aligns the products of a step before adding them and drops the bits below
+# the alignment.  Measured (probes of single and of 32 chained steps, random
+# and normally distributed codes): a step's result lies within 2^-11.7 of
+# the sum of its 64 products' magnitudes of the exact accumulator-plus-sum,
+# after half an fp32 ulp of the result.  The stage checks of that path allow
+# FP8_CORE_ACC times the sum of the magnitudes of a value's products.
+FP8_CORE_ACC = 2.0 ** -11
+
+
+def fp8_core_hidden_bound(Xq: np.ndarray, q: dict, e: int) -> np.ndarray:
+    """Bound of |H - H64| that the FP8 matrix core's summation adds, for the
+    dequantised token rows Xq of expert e: first order in the errors of G and
+    U (each FP8_CORE_ACC times its sum of product magnitudes), plus the
+    second-order terms (|silu''| <= 1/2, |silu'| <= 1.1)."""
+    from oracle import fp8
+    Wg = fp8.dequantize_blocks(q["gate_codes"][e], q["gate_scales"][e])
+    Wu = fp8.dequantize_blocks(q["up_codes"][e], q["up_scales"][e])
+    G, U = Xq @ Wg.T, Xq @ Wu.T
+    dG = FP8_CORE_ACC * (np.abs(Xq) @ np.abs(Wg).T)
+    dU = FP8_CORE_ACC * (np.abs(Xq) @ np.abs(Wu).T)
+    sig = 1.0 / (1.0 + np.exp(-G))
+    silu = G * sig
+    dsilu = sig * (1.0 + G * (1.0 - sig))
+    return (np.abs(dsilu * U) * dG + np.abs(silu) * dU
+            + 1.1 * dG * dU + 0.25 * dG ** 2 * (np.abs(U) + dU))
+
+
+def fp8_core_down_bound(H: np.ndarray, q: dict, e: int) -> np.ndarray:
+    """Bound of |Y - Y_ref| that the FP8 matrix core's summation adds to the
+    down step of expert e on bf16 hidden rows H."""
+    from oracle import fp8
+    Hq = fp8.dequantize_groups(*fp8.quantize_groups(H))
+    Wd = fp8.dequantize_blocks(q["down_codes"][e], q["down_scales"][e])
+    return FP8_CORE_ACC * (np.abs(Hq) @ np.abs(Wd).T)
 
 
 def oracle_inputs(layer: dict) -> dict:

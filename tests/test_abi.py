@@ -54,9 +54,9 @@ def test_workspace_layout(lib):
             assert size(_lib.WS_ROUTER_PARTIAL) == 0  # the fused router keeps its partials in LDS
         # Quantised rows and scales of the FP8 layer's grouped path (above 256 tokens only).
         fp8 = N > _lib.FP8_STREAM_TOKENS
-        assert size(_lib.WS_XQ) >= (N * 2048 * 2 if fp8 else 0)
+        assert size(_lib.WS_XQ) >= (N * 2048 if fp8 else 0)
         assert size(_lib.WS_XS) >= (N * 16 * 4 if fp8 else 0)
-        assert size(_lib.WS_HQ) >= (4 * N * 1536 * 2 if fp8 else 0)
+        assert size(_lib.WS_HQ) >= (4 * N * 1536 if fp8 else 0)
         assert size(_lib.WS_HS) >= (4 * N * 12 * 4 if fp8 else 0)
         if not fp8:
             assert all(size(r) == 0 for r in (_lib.WS_XQ, _lib.WS_XS, _lib.WS_HQ, _lib.WS_HS))

@@ -16,8 +16,8 @@ import torch
 import oracle
 import synth
 from conftest import cached_layer
-from parity import (check_route, device_inputs, expected_outputs, fp8_output_check,
-                    oracle_fp8_experts, oracle_inputs)
+from parity import (check_route, device_inputs, expected_outputs, fp8_core_down_bound,
+                    fp8_core_hidden_bound, fp8_output_check, oracle_fp8_experts, oracle_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -129,31 +129,43 @@ def _check_fp8_forward(moe, inp, dev, q, N):
     perm = np.array([[list(sel[t]).index(int(e)) for e in idx[t]] for t in tokens])
     oslot = (tokens[:, None] * 4 + perm).reshape(-1)
     H_ref = H_ref[oslot]
-    # Unrounded float64 H of the same decisions.
+    # Unrounded float64 H of the same decisions (and, for the grouped
+    # kernels, the bound of their matrix-core summation).
+    grouped = N > _lib.FP8_STREAM_TOKENS
     xq = fp8.dequantize_groups(*fp8.quantize_groups(inp["X"]))
     H64 = np.zeros_like(H)
+    H_acc = np.zeros_like(H)
     for e in np.unique(sel):
         rows = np.nonzero(sel.reshape(-1) == e)[0]
         H64[rows] = fp8.expert_hidden_fp8(xq[rows // 4], q, int(e), rounded=False)
+        if grouped:
+            H_acc[rows] = fp8_core_hidden_bound(xq[rows // 4], q, int(e))
     H64 = H64[oslot]
-    # The products are exact and summed in fp32: H is the correctly rounded
-    # bf16 of the oracle value, up to half a bf16 ulp, plus the fp32 error
-    # of the sums (absolute, ~1e-6 of the RMS, so it only matters for values
-    # near zero).
+    H_acc = H_acc[oslot]
+    # Streaming kernels: the products are exact and summed in fp32, so H is
+    # the correctly rounded bf16 of the oracle value, up to half a bf16 ulp,
+    # plus the fp32 error of the sums (absolute, ~1e-6 of the RMS, so it only
+    # matters for values near zero).  Grouped kernels: plus the matrix
+    # core's summation bound.
     _, ex = np.frexp(H64)
     h_rms = float(np.sqrt(np.mean(H64 ** 2)))
-    assert np.all(np.abs(H - H64) <= np.ldexp(1.0, ex - 9) * (1 + 2 ** -6) + 1e-4 * h_rms), \
-        "H is not the rounded oracle value"
+    h_err = np.abs(H - H64) - np.ldexp(1.0, ex - 9) * (1 + 2 ** -6) - 1e-4 * h_rms
+    assert np.all(h_err <= H_acc), "H is not the rounded oracle value"
     same = float(np.mean(H == H_ref))
-    assert same > 0.99, same
+    # The matrix core's summation moves some values across a bf16 rounding
+    # midpoint (measured: 1-2% at these sizes).
+    assert same > (0.95 if grouped else 0.99), same
     # Down step on the GPU's H, expert by expert.
     Y_tf = np.zeros_like(Y)
+    Y_acc = np.zeros_like(Y)
     flat = idx.reshape(-1)
     for e in np.unique(flat):
         rows = np.nonzero(flat == e)[0]
         Y_tf[rows] = fp8.expert_down_fp8(H[rows], q, int(e))
+        if grouped:
+            Y_acc[rows] = fp8_core_down_bound(H[rows], q, int(e))
     y_rms = float(np.sqrt(np.mean(Y_tf ** 2)))
-    y_err = float(np.max(np.abs(Y - Y_tf))) / y_rms
+    y_err = float(np.max((np.abs(Y - Y_tf) - Y_acc) / y_rms))
     assert y_err <= 1e-4, y_err
     comb = (w[:, :, None] * Y.reshape(N, 4, 2048)).sum(axis=1)
     c_err = float(np.max(np.abs(out - comb))) / float(np.sqrt(np.mean(comb ** 2)))
@@ -163,7 +175,8 @@ def _check_fp8_forward(moe, inp, dev, q, N):
     # weights and inputs moves the output by far more than the parity error).
     ref16 = expected_outputs(inp, r, tokens, alt)
     ratio16 = float(np.max(np.abs(out - ref16))) / float(np.sqrt(np.mean(ref16 ** 2)))
-    print(f"  H equal {same:.5f}; Y vs oracle-on-GPU-H {y_err:.2e}; combine {c_err:.2e}; "
+    print(f"  H equal {same:.5f}, max excess over the bound {float(np.max(h_err - H_acc)):.2e}; "
+          f"Y vs oracle-on-GPU-H {y_err:.2e}; combine {c_err:.2e}; "
           f"out vs FP8 oracle on the GPU's H {res['same_codes']:.2e}, end to end {res['end_to_end']:.4f} "
           f"({res['code_flips']} of {H.size} H codes and {res['scale_flips']} group scales differ); "
           f"vs bf16 oracle {ratio16:.4f}", flush=True)
