@@ -226,7 +226,7 @@ def summarize(p, wall_ms, per_kernel):
     )
 
 
-FP8_STREAM = 256  # FP8 layer: weight-streaming kernels up to this many tokens
+FP8_STREAM = 4  # FP8 layer: weight-streaming kernels up to this many tokens
 
 
 def summarize_fp8(p, wall_ms, per_kernel, label, note):
@@ -243,11 +243,12 @@ def summarize_fp8(p, wall_ms, per_kernel, label, note):
     gu_tflops = gateup_flops(N) / (gu_ms * 1e-3) / 1e12
     gbs = fp8_layer_bytes(A, N) / s / 1e9
     tflops = N * FLOP_PER_TOKEN / s / 1e12
-    hbm = N <= FP8_STREAM
+    hbm = tflops * 1e3 / gbs < 0.5 * FP8_PEAK_TFLOPS * 1e3 / HBM_PEAK_GBS
     kernel = "gateup_decode_fp8" if N <= FP8_STREAM else "gateup_tiled_fp8"
     if hbm:
         roof = dict(bound="hbm", kernel=kernel, achieved=gu_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=gu_gbs / HBM_PEAK_GBS, traffic=measured_traffic(p["name"], "gateup_fp8"),
+                    frac=gu_gbs / HBM_PEAK_GBS,
+                    traffic=measured_traffic(p["name"], "gateup_fp8", KERNEL_SOURCE[kernel]),
                     bytes_per_launch=fp8_gateup_bytes(A, N), avg_launch_ms=gu_ms, timing=EVENT_TIMING,
                     down_gbs=fp8_down_bytes(A, N) / (dn_ms * 1e-3) / 1e9)
     else:
@@ -274,16 +275,21 @@ def measure_fp8(p, steps, warmup, label, note, q=None):
     return e
 
 
+# Source file of each dominant kernel named in the roofline objects.
+KERNEL_SOURCE = {"gateup_decode": "expert_stream.hip", "gateup_tiled": "expert_tiled.hip",
+                 "gateup_decode_fp8": "expert_stream.hip", "gateup_tiled_fp8": "expert_tiled.hip"}
+
+
 def kernel_source_digest(path):
     import hashlib
     with open(os.path.join(ROOT, "biased_sigmoid_top_amd", "csrc", path), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(workload, kernel="gateup"):
+def measured_traffic(workload, kernel, source):
     """HBM bytes per gate/up launch from the committed rocprofv3 counter
-    summary of this workload, or None when it is missing or was taken on a
-    different version of the kernel source."""
+    summary of this workload, or None when it is missing, was taken on
+    another kernel (source file) or on a different version of its source."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
     if not os.path.exists(path):
         return None
@@ -292,7 +298,7 @@ def measured_traffic(workload, kernel="gateup"):
     if start < 0:
         return None
     rec = json.loads(text[start + 7:text.index("```", start + 7)])
-    if rec.get("source_digest") != kernel_source_digest(rec["source"]):
+    if rec.get("source") != source or rec.get("source_digest") != kernel_source_digest(source):
         return None
     return rec["hbm_bytes_per_launch"]
 
@@ -308,11 +314,13 @@ def roofline(h, workload):
         kernel = "gateup_decode" if N <= DECODE_MAX_TOKENS else "gateup_tiled"
         return dict(bound="hbm", kernel=kernel, achieved=h["gateup_gbs"],
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=h["gateup_gbs"] / HBM_PEAK_GBS,
-                    traffic=measured_traffic(workload), bytes_per_launch=gateup_bytes(A, N),
+                    traffic=measured_traffic(workload, "gateup", KERNEL_SOURCE[kernel]),
+                    bytes_per_launch=gateup_bytes(A, N),
                     avg_launch_ms=ms, timing=EVENT_TIMING)
     return dict(bound="mfma", kernel="gateup_tiled", achieved=h["gateup_tflops"],
                 peak=BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=h["gateup_tflops"] / BF16_PEAK_TFLOPS,
-                traffic=measured_traffic(workload), flops_per_launch=gateup_flops(N),
+                traffic=measured_traffic(workload, "gateup", KERNEL_SOURCE["gateup_tiled"]),
+                flops_per_launch=gateup_flops(N),
                 avg_launch_ms=ms, timing=EVENT_TIMING)
 
 

@@ -22,11 +22,11 @@ ERR_HIP = 4
 
 (WS_IDX, WS_W, WS_BLOCKCOUNTS, WS_OFFSETS, WS_ROW2SLOT, WS_H, WS_Y, WS_X, WS_ROUTER_PARTIAL,
  WS_XQ, WS_XS, WS_HQ, WS_HS) = range(13)
-DECODE_MAX_TOKENS = 96
+DECODE_MAX_TOKENS = 4
 FP8_MAX_TOKENS = 1 << 24
-FP8_STREAM_TOKENS = 256
+FP8_STREAM_TOKENS = 4
 NOALLOC_MAX_TOKENS = 256
-NOALLOC_SCRATCH_BYTES = 14 << 20
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64

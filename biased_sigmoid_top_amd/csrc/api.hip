@@ -312,8 +312,8 @@ T* region(void* ws, int64_t N, lfm_moe_ws_region r) {
 // Decode-shaped batches take the expert-major streaming kernels, which
 // group their own tokens; larger batches go through the dispatch step.
 bool use_decode_path(int64_t N) { return N <= kDecodeMaxTokens; }
-static_assert(kStreamMaxTokens == LFM_MOE_FP8_STREAM_TOKENS,
-              "the FP8 layer streams exactly the batches the streaming kernels can group");
+static_assert(kDecodeMaxTokens == LFM_MOE_FP8_STREAM_TOKENS && kDecodeMaxTokens <= kStreamMaxTokens,
+              "both layers stream the same batches, which the streaming kernels can group");
 
 // The router's outputs in the workspace: from the router, or copied from
 // caller-given selections and weights (idx_in, w_in not null), with the

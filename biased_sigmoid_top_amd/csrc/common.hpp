@@ -13,13 +13,14 @@ constexpr int kFF = 1536;       // expert intermediate width
 constexpr int kWave = 64;       // CDNA wavefront width
 constexpr float kRouterEps = 1e-6f;
 constexpr float kRmsEps = 1e-6f;
-// Largest N taken by the decode path (its per-expert slot lists live in
-// LDS).  Measured crossover: the decode kernels win while the experts' token
-// counts fit one 32-token pass (N = 96: 150 us against 190 us for the
-// grouped path); beyond it they stream an expert's weights once per pass
-// (N = 128: 307 us against 192 us).
-constexpr int kDecodeMaxTokens = 96;   // bf16 layer: weight-streaming path up to here
-constexpr int kStreamMaxTokens = 256;  // tokens the weight-streaming kernels can group (FP8 layer up to here)
+// Largest N taken by the weight-streaming (decode) kernels, which group
+// their own tokens in LDS (capacity kStreamMaxTokens).  Measured against the
+// grouped kernels with 32- and 64-row token tiles (layer us, first N tokens
+// of one layer, streaming / grouped): bf16 N = 1: 31.0-32.0 / 38.2-40.2;
+// 8: 68.5 / 64.7-65.4; 64 (the 64-token decode workload): 143.4-146.5 /
+// 136.6-137.7.  FP8 experts: N = 1: 30.8-31.2 / 36.1-36.6; 8: 52.3 / 47.6.
+constexpr int kDecodeMaxTokens = 4;    // both layers: weight-streaming kernels up to here
+constexpr int kStreamMaxTokens = 256;  // tokens the weight-streaming kernels can group
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

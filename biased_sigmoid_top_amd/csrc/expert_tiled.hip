@@ -151,6 +151,7 @@ void expert_tiled_kernel(
   constexpr int kRowBytes = T::K * (FP8 ? 1 : 2);
   static_assert(kStages % kWSlots == 0, "the stage loop is unrolled by the ring size");
   static_assert(!FP8 || 2 * kStageK == 128, "an FP8 scale group is one stage pair");
+  static_assert(!FP8 || TB % 2 == 0, "FP8 token operands alternate between two slots per stage");
   // Token fragments: 2 pair buffers x (2 stages x 4 token blocks x kKS steps).
   __shared__ uint4 tok[2][2 * TB * kKS * kWave];
   // FP8 scales of the tile: the token rows' ([group][tile row]) and the
@@ -493,48 +494,59 @@ int64_t tiled_grid(int64_t N) {
   return groups * T::kGroup * T::kColTiles;
 }
 
-// Column tiles by batch size.  With few tokens per expert the kernels are
+// Tile shapes by batch size.  With few tokens per expert the kernels are
 // bound by the weight stream, each expert has one or two m-tiles, and the
 // tile count barely exceeds what the device holds, so the last round of
 // tiles runs on a fraction of the CUs; narrower tiles make that tail
-// shorter.  Gate/up: 512 weight rows (8 wavefronts x two blocks) by
-// default, 128 rows (4 wavefronts x one block, two workgroups per CU) for
-// 193-512 tokens, 256 rows (8 x one) for 513-2048.  Down: 128 rows (4 x
-// one) up to 512 tokens, 256 rows (8 x one) for 513-2048, 256 rows (4 x
-// two) for 2049-6144, 512 rows (8 x two) above.  Measured (layer of seed
-// 4, first N tokens; gate/up 512 / 128 / 256 rows, us): N = 160: 92 / 97 /
-// -; 256: 132 / 112 / -; 320: - / 112 / 117; 512: - / 119 / 121; 640: - /
-// 130 / 126; 1024: - / 140 / 133; earlier, 4096: 245 / - / 261.  Down 256 /
-// 128 rows: N = 128: 61 / 52; 320: 71 / 61; 512: 77 / 69; 640: 74 / 75;
-// 2048: 104 / 108.  Down by N (us, same box, mean of two runs for the
-// 256-row form; 256 rows as 4 x two / 256 rows as 8 x one / 512 rows as 8 x
-// two): N = 1024: 83.1 / 78.6 / 83.8; 2048: 112.3 / 104.5 / 115.8; 4096:
-// 157.3 / 160.3 / 165.7; 6144: 210.6 / 217.6 / 209.9; 8192: 277.6 / 299.0 /
-// 264.8; 16384: 497.2 / 541.0 / 470.8.  With eight wavefronts a workgroup
-// has a CU to itself and its token tile feeds twice the weight rows.
+// shorter, and token tiles no taller than the experts' token counts keep
+// the registers, LDS and MFMAs of all-padding rows out of the weight
+// stream (more workgroups per CU, more weight loads in flight).
+//  * Up to 256 tokens (bf16: from 5; FP8: from 5): 128 weight rows (4
+//    wavefronts x one block), token tiles of 32 rows up to 96 tokens (bf16)
+//    and of 64 rows otherwise (the FP8 mode needs an even number of token
+//    blocks).  Measured, layer us at N = 64 (the 64-token decode workload;
+//    the streaming kernels / 128 token rows / 64 / 32): bf16 143.4-146.5 /
+//    140.3-141.5 / 137.5-137.7 / 136.6-136.9; FP8 102.0-102.5 (streaming) /
+//    90.6-95.9 / 84.0-84.4.  First N tokens of the 4,096-token workload
+//    (streaming / 64 rows / 32 rows): bf16 N = 8: 68.5 / 65.4 / 64.7-65.3;
+//    48: 112.6-113.4 / 103.3 / 102.5-102.9; 96: 135.3-135.8 / 132.8 / 131.0;
+//    192: 184.1 (512 weight rows) / 150.6-150.9 / 176.5; FP8 (streaming /
+//    64 rows / 128 rows) N = 8: 52.3 / 47.7 / 51.7; 32: 79.3 / 65.8 / 73.7;
+//    128: 111.9 / 87.5 / 92.8; 256: 157.6 / 102.4 / 109.8; 512: 129.4 /
+//    129.3 / 129.7.
+//  * bf16, 257-512 tokens: 128 weight rows, 128 token rows; 513-2048: 256
+//    rows (8 wavefronts x one block); above, gate/up 512 rows (8 x two).
+//    Down: 128 rows up to 512 tokens, 256 rows (8 x one) for 513-2048, 256
+//    rows (4 x two) for 2049-6144, 512 rows (8 x two) above.  Measured
+//    (layer of seed 4, first N tokens; gate/up 512 / 128 / 256 rows, us):
+//    N = 256: 132 / 112 / -; 320: - / 112 / 117; 512: - / 119 / 121; 640: -
+//    / 130 / 126; 1024: - / 140 / 133; earlier, 4096: 245 / - / 261.  Down
+//    by N (us, same box, mean of two runs for the 256-row form; 256 rows as
+//    4 x two / 256 rows as 8 x one / 512 rows as 8 x two): N = 1024: 83.1 /
+//    78.6 / 83.8; 2048: 112.3 / 104.5 / 115.8; 4096: 157.3 / 160.3 / 165.7;
+//    6144: 210.6 / 217.6 / 209.9; 8192: 277.6 / 299.0 / 264.8; 16384: 497.2
+//    / 541.0 / 470.8.  With eight wavefronts a workgroup has a CU to itself
+//    and its token tile feeds twice the weight rows.
+//  * FP8, 257-2048 tokens: 128 weight rows and 128 token rows for both
+//    kernels; above, gate/up 512 rows (8 x two), down 256 rows (4 x two) up
+//    to 6144 tokens and 512 (8 x two) above.  Measured (us, gate/up 128 /
+//    256 / 512 rows; down 128 / 256 (8 x one) / 512 / 256 (4 x two) rows):
+//    N = 512: 66.9 / 72.3 / 87.7, 49.2 / 48.7 / 49.9 / 54.8; 2048: 115.2 /
+//    117.6-118.8 / 120.5, 80.5 / 88.3 / 83.5 / 82.7; 4096: 180.5-181.1 /
+//    182.0 / 165.5, 129.2-129.7 / 128.1-128.9 / 125.1-125.4 / 122.0-122.4.
 // Weight loads: up to kOneTouchTokens tokens most experts have a single
 // m-tile, so each weight byte is read once and the loads are non-temporal
 // (layer us, same box, plain / non-temporal: N = 160: 149.5-152.9 /
 // 141.8-144.3; 320: 174.1-177.9 / 164.5-168.5; 640: 219-220 both); above,
 // the m-tiles of an expert share its weight tiles through the L2 and
 // non-temporal loads cost (N = 2048: 333 / 362-368; 4096: 465-476 / 532-535).
-// The FP8 grouped kernels (from 257 tokens) follow the same rule (FP8 layer
-// us: N = 300: 141.1-141.6 / 138.0-138.9; 400: 156.1-156.3 / 152.3-152.4;
-// 512: 166.4-167.0 / 165.5-165.9).
+// The FP8 kernels follow the same rule (FP8 layer us: N = 300: 141.1-141.6 /
+// 138.0-138.9; 400: 156.1-156.3 / 152.3-152.4; 512: 166.4-167.0 /
+// 165.5-165.9).
 constexpr int64_t kOneTouchTokens = 512;
-enum class GateupTiles { kWide, kNarrow4, kNarrow8 };
-GateupTiles gateup_tiles(int64_t N) {
-  if (N > 192 && N <= 512) return GateupTiles::kNarrow4;
-  if (N > 512 && N <= 2048) return GateupTiles::kNarrow8;
-  return GateupTiles::kWide;
-}
-enum class DownTiles { kNarrow4, kNarrow8, kMid, kWide8 };
-DownTiles down_tiles(int64_t N) {
-  if (N <= 512) return DownTiles::kNarrow4;
-  if (N <= 2048) return DownTiles::kNarrow8;
-  if (N <= 6144) return DownTiles::kMid;
-  return DownTiles::kWide8;
-}
+constexpr int64_t kShortTileTokens = 256;  // 128 weight rows, short token tiles
+constexpr int64_t kBf16TB1Tokens = 96;     // bf16: 32-row token tiles up to here
+constexpr int64_t kFp8NarrowTokens = 2048; // FP8: 128 x 128 tiles up to here
 
 template <bool GATEUP, int FB, int WAVES = (GATEUP ? 8 : 4), int TB = 4, bool FP8 = false,
           bool NTW = false, typename Out>
@@ -556,56 +568,53 @@ hipError_t launch_tiled(const void* A, const void* W, const int32_t* offsets,
 hipError_t launch_gateup_tiled(const uint16_t* X, const uint16_t* Wgu, const int32_t* offsets,
                                const int32_t* row2slot, uint16_t* H, int64_t N,
                                hipStream_t stream) {
-  switch (gateup_tiles(N)) {
-    case GateupTiles::kNarrow4:
-      return launch_tiled<true, 1, 4, 4, false, true>(X, Wgu, offsets, row2slot, H, N, stream);
-    case GateupTiles::kNarrow8:
-      return launch_tiled<true, 1>(X, Wgu, offsets, row2slot, H, N, stream);
-    default:
-      return N <= kOneTouchTokens ? launch_tiled<true, 2, 8, 4, false, true>(X, Wgu, offsets, row2slot, H, N, stream)
-                                  : launch_tiled<true, 2>(X, Wgu, offsets, row2slot, H, N, stream);
-  }
+  if (N <= kBf16TB1Tokens)
+    return launch_tiled<true, 1, 4, 1, false, true>(X, Wgu, offsets, row2slot, H, N, stream);
+  if (N <= kShortTileTokens)
+    return launch_tiled<true, 1, 4, 2, false, true>(X, Wgu, offsets, row2slot, H, N, stream);
+  if (N <= kOneTouchTokens)
+    return launch_tiled<true, 1, 4, 4, false, true>(X, Wgu, offsets, row2slot, H, N, stream);
+  if (N <= 2048) return launch_tiled<true, 1>(X, Wgu, offsets, row2slot, H, N, stream);
+  return launch_tiled<true, 2>(X, Wgu, offsets, row2slot, H, N, stream);
 }
 
 hipError_t launch_down_tiled(const uint16_t* H, const uint16_t* Wd, const int32_t* offsets,
                              const int32_t* row2slot, float* Y, int64_t N, hipStream_t stream) {
-  switch (down_tiles(N)) {
-    case DownTiles::kNarrow4:
-      return launch_tiled<false, 1, 4, 4, false, true>(H, Wd, offsets, row2slot, Y, N, stream);
-    case DownTiles::kNarrow8:
-      return launch_tiled<false, 1, 8>(H, Wd, offsets, row2slot, Y, N, stream);
-    case DownTiles::kWide8:
-      return launch_tiled<false, 2, 8>(H, Wd, offsets, row2slot, Y, N, stream);
-    default:
-      return launch_tiled<false, 2>(H, Wd, offsets, row2slot, Y, N, stream);
-  }
+  if (N <= kBf16TB1Tokens)
+    return launch_tiled<false, 1, 4, 1, false, true>(H, Wd, offsets, row2slot, Y, N, stream);
+  if (N <= kShortTileTokens)
+    return launch_tiled<false, 1, 4, 2, false, true>(H, Wd, offsets, row2slot, Y, N, stream);
+  if (N <= kOneTouchTokens)
+    return launch_tiled<false, 1, 4, 4, false, true>(H, Wd, offsets, row2slot, Y, N, stream);
+  if (N <= 2048) return launch_tiled<false, 1, 8>(H, Wd, offsets, row2slot, Y, N, stream);
+  if (N <= 6144) return launch_tiled<false, 2>(H, Wd, offsets, row2slot, Y, N, stream);
+  return launch_tiled<false, 2, 8>(H, Wd, offsets, row2slot, Y, N, stream);
 }
 
 hipError_t launch_gateup_tiled_fp8(const uint8_t* Xq, const uint8_t* Wq, const float* Ws,
                                    const float* Xs, const int32_t* offsets, const int32_t* row2slot,
                                    uint16_t* H, int64_t N, hipStream_t stream) {
-  switch (gateup_tiles(N)) {
-    case GateupTiles::kNarrow4:
-      return launch_tiled<true, 1, 4, 4, true, true>(Xq, Wq, offsets, row2slot, H, N, stream, Ws, Xs);
-    case GateupTiles::kNarrow8:
-      return launch_tiled<true, 1, 8, 4, true>(Xq, Wq, offsets, row2slot, H, N, stream, Ws, Xs);
-    default:
-      return N <= kOneTouchTokens ? launch_tiled<true, 2, 8, 4, true, true>(Xq, Wq, offsets, row2slot, H, N, stream, Ws, Xs)
-                                  : launch_tiled<true, 2, 8, 4, true>(Xq, Wq, offsets, row2slot, H, N, stream, Ws, Xs);
-  }
+  if (N <= kShortTileTokens)
+    return launch_tiled<true, 1, 4, 2, true, true>(Xq, Wq, offsets, row2slot, H, N, stream, Ws, Xs);
+  if (N <= kOneTouchTokens)
+    return launch_tiled<true, 1, 4, 4, true, true>(Xq, Wq, offsets, row2slot, H, N, stream, Ws, Xs);
+  if (N <= kFp8NarrowTokens)
+    return launch_tiled<true, 1, 4, 4, true>(Xq, Wq, offsets, row2slot, H, N, stream, Ws, Xs);
+  return launch_tiled<true, 2, 8, 4, true>(Xq, Wq, offsets, row2slot, H, N, stream, Ws, Xs);
 }
 
 hipError_t launch_down_tiled_fp8(const uint8_t* Hq, const uint8_t* Wq, const float* Ws,
                                  const float* Hs, const int32_t* offsets, const int32_t* row2slot,
                                  float* Y, int64_t N, hipStream_t stream) {
-  switch (down_tiles(N)) {
-    case DownTiles::kNarrow4:
-      return launch_tiled<false, 1, 4, 4, true, true>(Hq, Wq, offsets, row2slot, Y, N, stream, Ws, Hs);
-    case DownTiles::kNarrow8:
-      return launch_tiled<false, 1, 8, 4, true>(Hq, Wq, offsets, row2slot, Y, N, stream, Ws, Hs);
-    default:  // the 4-wavefront form of two blocks would spill in FP8 mode
-      return launch_tiled<false, 2, 8, 4, true>(Hq, Wq, offsets, row2slot, Y, N, stream, Ws, Hs);
-  }
+  if (N <= kShortTileTokens)
+    return launch_tiled<false, 1, 4, 2, true, true>(Hq, Wq, offsets, row2slot, Y, N, stream, Ws, Hs);
+  if (N <= kOneTouchTokens)
+    return launch_tiled<false, 1, 4, 4, true, true>(Hq, Wq, offsets, row2slot, Y, N, stream, Ws, Hs);
+  if (N <= kFp8NarrowTokens)
+    return launch_tiled<false, 1, 4, 4, true>(Hq, Wq, offsets, row2slot, Y, N, stream, Ws, Hs);
+  // The two-block shapes spill a few registers, outside the stage loop.
+  if (N <= 6144) return launch_tiled<false, 2, 4, 4, true>(Hq, Wq, offsets, row2slot, Y, N, stream, Ws, Hs);
+  return launch_tiled<false, 2, 8, 4, true>(Hq, Wq, offsets, row2slot, Y, N, stream, Ws, Hs);
 }
 
 }  // namespace lfm

@@ -53,10 +53,10 @@ extern "C" {
 /* Largest N accepted: grouped rows (4N) and their element offsets stay in range. */
 #define LFM_MOE_MAX_TOKENS (1LL << 24)
 /* Largest N of lfm_moe_forward_fp8, and the largest N it runs on the
- * weight-streaming kernels (decode and verification-shaped batches; larger
- * batches take the grouped kernels in FP8 mode). */
+ * weight-streaming kernels (the smallest batches; larger ones take the
+ * grouped kernels in FP8 mode).  lfm_moe_forward takes the same split. */
 #define LFM_MOE_FP8_MAX_TOKENS LFM_MOE_MAX_TOKENS
-#define LFM_MOE_FP8_STREAM_TOKENS 256
+#define LFM_MOE_FP8_STREAM_TOKENS 4
 
 typedef enum {
   LFM_MOE_OK = 0,
@@ -355,13 +355,15 @@ lfm_moe_status lfm_moe_stack_forward_ws(float* x_inout, const lfm_moe_block_weig
  *   LFM_MOE_FP8_MAX_TOKENS.  Router and mixture weights as in
  *   lfm_moe_forward; each expert's input rows (X, then the bf16 hidden rows)
  *   are quantised per group of 128 features as above; the products of
- *   codes are exact and summed in fp32, then scaled by weight scale x
- *   activation scale per 128-wide K group; out [N, 2048] fp32.  Up to
- *   LFM_MOE_FP8_STREAM_TOKENS tokens the expert kernels stream the weights
- *   and quantise the rows in registers; above, the dispatch step groups the
- *   rows, X and H are quantised into the XQ/XS and HQ/HS workspace regions
- *   and the grouped kernels run in FP8 mode.  Library-owned workspace, as
- *   lfm_moe_forward.
+ *   codes are summed per 128-wide K group, then scaled by weight scale x
+ *   activation scale; out [N, 2048] fp32.  Up to LFM_MOE_FP8_STREAM_TOKENS
+ *   tokens the expert kernels stream the weights and quantise the rows in
+ *   registers (exact products, fp32 sums); above, the dispatch step groups
+ *   the rows, X and H are quantised into the XQ/XS and HQ/HS workspace
+ *   regions and the grouped kernels multiply on the FP8 matrix core, whose
+ *   sums are not fp32 sums: it aligns each step's 64 products and drops the
+ *   bits below the alignment (measured: within 2^-11.6 of the sum of their
+ *   magnitudes).  Library-owned workspace, as lfm_moe_forward.
  * lfm_moe_forward_fp8_ws: the same with a caller workspace, as
  *   lfm_moe_forward_ws (same size and regions: the routing, the bf16 hidden
  *   rows H and the fp32 expert rows Y, both in slot order t * 4 + j; up to
@@ -410,7 +412,7 @@ lfm_moe_status lfm_moe_experts_fp8_ws(const uint16_t* X, const int32_t* idx, con
  * results: serialise them, or use lfm_moe_forward_ws.
  */
 #define LFM_MOE_NOALLOC_MAX_TOKENS 256
-#define LFM_MOE_NOALLOC_SCRATCH_BYTES (14u << 20)
+#define LFM_MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
 lfm_moe_status lfm_moe_forward_noalloc(const uint16_t* X, const uint16_t* W_r, const float* bias,
                                        const uint16_t* W_gateup, const uint16_t* W_down,
                                        float* out, int64_t N, hipStream_t stream);

@@ -220,7 +220,7 @@ def test_noalloc_forward_checks(lib):
     with open(_lib.HEADER) as fh:
         text = fh.read()
     assert f"#define LFM_MOE_NOALLOC_MAX_TOKENS {_lib.NOALLOC_MAX_TOKENS}" in text
-    assert "#define LFM_MOE_NOALLOC_SCRATCH_BYTES (14u << 20)" in text
+    assert "#define LFM_MOE_NOALLOC_SCRATCH_BYTES (16u << 20)" in text
 
 
 def test_pack_checks(lib):

@@ -221,9 +221,10 @@ def test_fp8_forward_skewed_all_tokens(moe):
           f"and {res['scale_flips']} group scales differ)", flush=True)
 
 
-@pytest.mark.parametrize("N", [1, 17, 33, 95, 96, 97, 160, 255, 256, 257, 700, 2049, 4096])
+@pytest.mark.parametrize("N", [1, 4, 5, 17, 33, 95, 96, 97, 160, 255, 256, 257, 700, 2049, 4096])
 def test_fp8_forward_ragged(moe, N):
-    """Streaming kernels up to 256 tokens, grouped kernels in FP8 mode above."""
+    """Streaming kernels up to 4 tokens, grouped kernels in FP8 mode above
+    (64-row token tiles up to 256 tokens, 128-row tiles above)."""
     inp0, dev0, q = _decode_case(moe)
     X = oracle.block_input(synth.hidden_states(N, 500 + N).numpy())
     inp = dict(inp0, X=X)

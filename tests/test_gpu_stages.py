@@ -64,7 +64,7 @@ def _chain(moe, dev, X, idx, w, ws):
     return moe.stage_combine(X.shape[0], ws)
 
 
-@pytest.mark.parametrize("N", [64, 700])
+@pytest.mark.parametrize("N", [3, 64, 700])
 def test_stage_chain_equals_the_expert_path(moe, N):
     inp, dev = _case()
     _, X = _x(N, 4100 + N)
@@ -81,7 +81,7 @@ def test_stage_chain_equals_the_expert_path(moe, N):
     assert torch.equal(out, ref), "the stage chain differs from lfm_moe_experts_ws"
 
 
-@pytest.mark.parametrize("N", [64, 700])
+@pytest.mark.parametrize("N", [3, 64, 700])
 def test_each_stage_against_the_oracle(moe, N):
     from biased_sigmoid_top_amd import _lib
     inp, dev = _case()

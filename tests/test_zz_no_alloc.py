@@ -38,7 +38,7 @@ def test_noalloc_forward_equals_forward(moe):
     w = synth.WORKLOADS["tiny_n32"]
     dev = device_weights(cached_layer(w["N"], w["seed"], w["skew"]))
     cases = []
-    for N, seed in ((_lib.NOALLOC_MAX_TOKENS, 1900), (64, 1901)):
+    for N, seed in ((_lib.NOALLOC_MAX_TOKENS, 1900), (64, 1901), (3, 1902)):
         X = torch.from_numpy(oracle.block_input(synth.hidden_states(N, seed).numpy())).to(torch.bfloat16).cuda()
         cases.append((N, X, torch.full((N, 2048), np.nan, device="cuda"),
                       torch.full((N, 2048), np.nan, device="cuda")))
