@@ -344,8 +344,9 @@ lfm_moe_status run_layer(const uint16_t* X, const uint16_t* W_r, const float* bi
   float* part = region<float>(ws, N, LFM_MOE_WS_ROUTER_PARTIAL);
   const int n = static_cast<int>(N);
   const bool decode = use_decode_path(N);
+  const bool dispatch = !decode && !gateup_groups_slots(N);
   hipError_t e;
-  if ((e = route_or_ingest(X, W_r, bias, idx_in, w_in, idx, w, decode ? nullptr : blockcounts, part, n,
+  if ((e = route_or_ingest(X, W_r, bias, idx_in, w_in, idx, w, dispatch ? blockcounts : nullptr, part, n,
                            stream)) != hipSuccess)
     return hip_fail(e, idx_in ? "routing copy kernel launch" : "route kernel launch");
   timer.after(1);
@@ -357,10 +358,12 @@ lfm_moe_status run_layer(const uint16_t* X, const uint16_t* W_r, const float* bi
       return hip_fail(e, "down kernel launch");
     timer.after(4);
   } else {
-    if ((e = launch_dispatch(idx, blockcounts, offsets, row2slot, n, stream)) != hipSuccess)
-      return hip_fail(e, "dispatch kernel launch");
-    timer.after(2);
-    if ((e = launch_gateup_tiled(X, W_gateup, offsets, row2slot, H, N, stream)) != hipSuccess)
+    if (dispatch) {
+      if ((e = launch_dispatch(idx, blockcounts, offsets, row2slot, n, stream)) != hipSuccess)
+        return hip_fail(e, "dispatch kernel launch");
+      timer.after(2);
+    }
+    if ((e = launch_gateup_tiled(X, W_gateup, idx, offsets, row2slot, H, N, stream)) != hipSuccess)
       return hip_fail(e, "gate/up kernel launch");
     timer.after(3);
     if ((e = launch_down_tiled(H, W_down, offsets, row2slot, Y, N, stream)) != hipSuccess)
@@ -426,9 +429,10 @@ lfm_moe_status run_fp8(const uint16_t* X, const uint16_t* W_r, const float* bias
   float* part = region<float>(ws, N, LFM_MOE_WS_ROUTER_PARTIAL);
   const int n = static_cast<int>(N);
   const bool streaming = N <= LFM_MOE_FP8_STREAM_TOKENS;
+  const bool dispatch = !streaming && !gateup_groups_slots(N);
   int32_t* blockcounts = region<int32_t>(ws, N, LFM_MOE_WS_BLOCKCOUNTS);
   hipError_t e;
-  if ((e = route_or_ingest(X, W_r, bias, idx_in, w_in, idx, w, streaming ? nullptr : blockcounts, part,
+  if ((e = route_or_ingest(X, W_r, bias, idx_in, w_in, idx, w, dispatch ? blockcounts : nullptr, part,
                            n, stream)) != hipSuccess)
     return hip_fail(e, idx_in ? "routing copy kernel launch" : "route kernel launch");
   timer.after(1);
@@ -440,21 +444,22 @@ lfm_moe_status run_fp8(const uint16_t* X, const uint16_t* W_r, const float* bias
       return hip_fail(e, "fp8 down kernel launch");
     timer.after(4);
   } else {
-    // Grouped: dispatch, X quantised per group (timed with the dispatch),
-    // gate/up, H quantised per group (timed with down), down.
+    // Grouped: dispatch (unless the gate/up kernel groups the slots), X
+    // quantised per group (timed as the dispatch stage), gate/up, H
+    // quantised per group (timed with down), down.
     int32_t* offsets = region<int32_t>(ws, N, LFM_MOE_WS_OFFSETS);
     int32_t* row2slot = region<int32_t>(ws, N, LFM_MOE_WS_ROW2SLOT);
     uint8_t* Xq = region<uint8_t>(ws, N, LFM_MOE_WS_XQ);
     float* Xs = region<float>(ws, N, LFM_MOE_WS_XS);
     uint8_t* Hq = region<uint8_t>(ws, N, LFM_MOE_WS_HQ);
     float* Hs = region<float>(ws, N, LFM_MOE_WS_HS);
-    if ((e = launch_dispatch(idx, blockcounts, offsets, row2slot, n, stream)) != hipSuccess)
+    if (dispatch && (e = launch_dispatch(idx, blockcounts, offsets, row2slot, n, stream)) != hipSuccess)
       return hip_fail(e, "dispatch kernel launch");
     if ((e = launch_quantize_groups(X, N, kHidden, Xq, Xs, stream)) != hipSuccess)
       return hip_fail(e, "quantize kernel launch");
     timer.after(2);
-    if ((e = launch_gateup_tiled_fp8(Xq, W_gateup_fp8, scales_gateup, Xs, offsets, row2slot, H, N,
-                                     stream)) != hipSuccess)
+    if ((e = launch_gateup_tiled_fp8(Xq, W_gateup_fp8, scales_gateup, Xs, idx, offsets, row2slot, H,
+                                     N, stream)) != hipSuccess)
       return hip_fail(e, "fp8 gate/up kernel launch");
     timer.after(3);
     if ((e = launch_quantize_groups(H, N * kTopK, kFF, Hq, Hs, stream)) != hipSuccess)
@@ -828,7 +833,8 @@ lfm_moe_status lfm_moe_stage_gateup(const uint16_t* X, const uint16_t* W_gateup,
   const hipError_t e =
       use_decode_path(N)
           ? launch_gateup_decode(X, W_gateup, region<int32_t>(ws, N, LFM_MOE_WS_IDX), H, static_cast<int>(N), stream)
-          : launch_gateup_tiled(X, W_gateup, region<int32_t>(ws, N, LFM_MOE_WS_OFFSETS),
+          : launch_gateup_tiled(X, W_gateup, region<int32_t>(ws, N, LFM_MOE_WS_IDX),
+                                region<int32_t>(ws, N, LFM_MOE_WS_OFFSETS),
                                 region<int32_t>(ws, N, LFM_MOE_WS_ROW2SLOT), H, N, stream);
   return e == hipSuccess ? LFM_MOE_OK : hip_fail(e, "gate/up kernel launch");
 }

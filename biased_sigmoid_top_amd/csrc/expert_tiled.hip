@@ -134,12 +134,60 @@ __device__ __forceinline__ f32x16 mfma32_fp8(const uint4& a0, const uint4& a1, c
 // by old unit / new unit, and at the end by the last units.  Where a scale
 // is 0 the group's codes are all 0, and that unit stays.  The scales of a
 // tile are staged in LDS once, before the stage loop.
-template <bool GATEUP, int FB_, int WAVES_, int TB_, bool FP8 = false, bool NTW = false>
+// Slots of at most kSelfTokens tokens grouped by expert, as the dispatch
+// step groups them (offsets: exclusive prefix of the per-expert counts;
+// rows: slots t * 4 + j of each expert in token order), computed in LDS by
+// one workgroup of at least kSelfTokens threads, one token per thread:
+// per-expert token bitmasks, a word prefix per expert, a prefix over the
+// experts, then each slot's rank from one popcount.  A token's four experts
+// are distinct, so each (expert, token) bit is set once.  scratch holds at
+// least 2 * kExperts * kSelfWords words and is free again on return.
+constexpr int kSelfTokens = 256;
+constexpr int kSelfWords = kSelfTokens / 32;
+__device__ __forceinline__ void group_slots_lds(const int32_t* __restrict__ idx, int N, int* off,
+                                                int* rows, uint32_t* scratch, int nthreads) {
+  uint32_t (*mask)[kSelfWords] = reinterpret_cast<uint32_t (*)[kSelfWords]>(scratch);
+  int (*wbase)[kSelfWords] = reinterpret_cast<int (*)[kSelfWords]>(scratch + kExperts * kSelfWords);
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kExperts * kSelfWords; i += nthreads) (&mask[0][0])[i] = 0u;
+  __syncthreads();
+  int my_e[kTopK];
+  if (tid < N) {
+    const int4 v = *reinterpret_cast<const int4*>(idx + static_cast<size_t>(tid) * kTopK);
+    my_e[0] = v.x; my_e[1] = v.y; my_e[2] = v.z; my_e[3] = v.w;
+#pragma unroll
+    for (int j = 0; j < kTopK; ++j) atomicOr(&mask[my_e[j]][tid / 32], 1u << (tid % 32));
+  }
+  __syncthreads();
+  if (tid < kExperts) {  // wavefront 0, lane = expert
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < kSelfWords; ++w) {
+      wbase[tid][w] = run;
+      run += __popc(mask[tid][w]);
+    }
+    const int incl = wave_inclusive_scan(run, tid);
+    off[tid] = incl - run;
+    if (tid == kExperts - 1) off[kExperts] = incl;
+  }
+  __syncthreads();
+  if (tid < N) {
+#pragma unroll
+    for (int j = 0; j < kTopK; ++j) {
+      const int e = my_e[j];
+      const int rank = wbase[e][tid / 32] + __popc(mask[e][tid / 32] & ((1u << (tid % 32)) - 1u));
+      rows[off[e] + rank] = tid * kTopK + j;
+    }
+  }
+  __syncthreads();
+}
+
+template <bool GATEUP, int FB_, int WAVES_, int TB_, bool FP8 = false, bool NTW = false, bool SELF = false>
 __global__ __launch_bounds__((TileShape<GATEUP, FB_, WAVES_, TB_>::kThreads),
                              (TileShape<GATEUP, FB_, WAVES_, TB_>::kPerCu))
 void expert_tiled_kernel(
-    const void* __restrict__ A, const void* __restrict__ Wp,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ row2slot,
+    const void* __restrict__ A, const void* __restrict__ Wp, const int32_t* __restrict__ idx, int ntok,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ row2slot,
     uint16_t* __restrict__ H, float* __restrict__ Y, const float* __restrict__ Ws,
     const float* __restrict__ As) {
   using T = TileShape<GATEUP, FB_, WAVES_, TB_>;
@@ -174,8 +222,27 @@ void expert_tiled_kernel(
   const int t = (w % kXcds) * kPerXcd + w / kXcds;
   const int nb = t / T::kGroup;
   const int mt = blockIdx.x / (T::kGroup * T::kColTiles) * T::kGroup + t % T::kGroup;
+  // SELF (gate/up of small batches): the workgroup groups the slots itself
+  // from the selections, and workgroup 0 publishes the grouping for the
+  // down kernel; otherwise the dispatch step's grouping is read.
+  __shared__ int self_off[SELF ? kExperts + 1 : 1];
+  __shared__ int self_rows[SELF ? kSelfTokens * kTopK : 1];
+  const int32_t* grp_off = offsets;
+  const int32_t* grp_rows = row2slot;
+  if constexpr (SELF) {
+    static_assert(GATEUP && T::kThreads >= kSelfTokens &&
+                      sizeof(tok) >= 2 * kExperts * kSelfWords * sizeof(uint32_t),
+                  "one token per thread; the masks fit in the token tile");
+    group_slots_lds(idx, ntok, self_off, self_rows, reinterpret_cast<uint32_t*>(&tok[0][0]), T::kThreads);
+    if (blockIdx.x == 0) {
+      for (int i = threadIdx.x; i <= kExperts; i += T::kThreads) offsets[i] = self_off[i];
+      for (int i = threadIdx.x; i < ntok * kTopK; i += T::kThreads) row2slot[i] = self_rows[i];
+    }
+    grp_off = self_off;
+    grp_rows = self_rows;
+  }
   MTile tile;
-  if (!map_mtile(offsets, mt, T::kBM, tile)) return;
+  if (!map_mtile(grp_off, mt, T::kBM, tile)) return;
   const int live_rows = uniform(tile.rows);
 
   const int tid = threadIdx.x;
@@ -191,7 +258,7 @@ void expert_tiled_kernel(
 #pragma unroll
   for (int i = 0; i < T::kChunks; ++i) {
     const int r = r0 + T::kRowStep * i;
-    const int slot = row2slot[tile.row_begin + (r < tile.rows ? r : 0)];
+    const int slot = grp_rows[tile.row_begin + (r < tile.rows ? r : 0)];
     arow[i] = static_cast<const uint8_t*>(A) +
               static_cast<size_t>(GATEUP ? slot / kTopK : slot) * kRowBytes + c * 16;
   }
@@ -227,7 +294,7 @@ void expert_tiled_kernel(
   float ws_st = 0.f;
   if constexpr (FP8) {
     const int r = tid % T::kBM;
-    const int slot = row2slot[tile.row_begin + (r < tile.rows ? r : 0)];
+    const int slot = grp_rows[tile.row_begin + (r < tile.rows ? r : 0)];
     const float* src = As + static_cast<size_t>(GATEUP ? slot / kTopK : slot) * kG;
 #pragma unroll
     for (int i = 0; i < kXsPer; ++i) xs_st[i] = src[(tid + T::kThreads * i) / T::kBM];
@@ -456,7 +523,7 @@ void expert_tiled_kernel(
   for (int tb = 0; tb < TB; ++tb) {
     const int row = tb * 32 + lane % 32;
     if (row >= tile.rows) continue;
-    const int slot = row2slot[tile.row_begin + row];
+    const int slot = grp_rows[tile.row_begin + row];
 #pragma unroll
     for (int f = 0; f < FB; ++f) {
       const int blk = nb * T::kBlocksPerTile + wave * FB + f;
@@ -549,72 +616,81 @@ constexpr int64_t kBf16TB1Tokens = 96;     // bf16: 32-row token tiles up to her
 constexpr int64_t kFp8NarrowTokens = 2048; // FP8: 128 x 128 tiles up to here
 
 template <bool GATEUP, int FB, int WAVES = (GATEUP ? 8 : 4), int TB = 4, bool FP8 = false,
-          bool NTW = false, typename Out>
-hipError_t launch_tiled(const void* A, const void* W, const int32_t* offsets,
-                        const int32_t* row2slot, Out* out, int64_t N, hipStream_t stream,
+          bool NTW = false, bool SELF = false, typename Out>
+hipError_t launch_tiled(const void* A, const void* W, const int32_t* idx, int32_t* offsets,
+                        int32_t* row2slot, Out* out, int64_t N, hipStream_t stream,
                         const float* Ws = nullptr, const float* As = nullptr) {
   uint16_t* H = nullptr;
   float* Y = nullptr;
   if constexpr (GATEUP) H = out; else Y = out;
-  hipLaunchKernelGGL((expert_tiled_kernel<GATEUP, FB, WAVES, TB, FP8, NTW>),
+  hipLaunchKernelGGL((expert_tiled_kernel<GATEUP, FB, WAVES, TB, FP8, NTW, SELF>),
                      dim3(tiled_grid<GATEUP, FB, WAVES, TB>(N)),
-                     dim3(TileShape<GATEUP, FB, WAVES, TB>::kThreads), 0, stream, A, W, offsets,
-                     row2slot, H, Y, Ws, As);
+                     dim3(TileShape<GATEUP, FB, WAVES, TB>::kThreads), 0, stream, A, W, idx,
+                     static_cast<int>(N), offsets, row2slot, H, Y, Ws, As);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gateup_tiled(const uint16_t* X, const uint16_t* Wgu, const int32_t* offsets,
-                               const int32_t* row2slot, uint16_t* H, int64_t N,
+bool gateup_groups_slots(int64_t N) { return N <= kShortTileTokens; }
+static_assert(kShortTileTokens <= kSelfTokens, "short-tile batches are grouped in the gate/up kernel");
+
+hipError_t launch_gateup_tiled(const uint16_t* X, const uint16_t* Wgu, const int32_t* idx,
+                               int32_t* offsets, int32_t* row2slot, uint16_t* H, int64_t N,
                                hipStream_t stream) {
   if (N <= kBf16TB1Tokens)
-    return launch_tiled<true, 1, 4, 1, false, true>(X, Wgu, offsets, row2slot, H, N, stream);
+    return launch_tiled<true, 1, 4, 1, false, true, true>(X, Wgu, idx, offsets, row2slot, H, N, stream);
   if (N <= kShortTileTokens)
-    return launch_tiled<true, 1, 4, 2, false, true>(X, Wgu, offsets, row2slot, H, N, stream);
+    return launch_tiled<true, 1, 4, 2, false, true, true>(X, Wgu, idx, offsets, row2slot, H, N, stream);
   if (N <= kOneTouchTokens)
-    return launch_tiled<true, 1, 4, 4, false, true>(X, Wgu, offsets, row2slot, H, N, stream);
-  if (N <= 2048) return launch_tiled<true, 1>(X, Wgu, offsets, row2slot, H, N, stream);
-  return launch_tiled<true, 2>(X, Wgu, offsets, row2slot, H, N, stream);
+    return launch_tiled<true, 1, 4, 4, false, true>(X, Wgu, idx, offsets, row2slot, H, N, stream);
+  if (N <= 2048) return launch_tiled<true, 1>(X, Wgu, idx, offsets, row2slot, H, N, stream);
+  return launch_tiled<true, 2>(X, Wgu, idx, offsets, row2slot, H, N, stream);
 }
 
+// The down kernels only read the grouping (their SELF mode is off).
 hipError_t launch_down_tiled(const uint16_t* H, const uint16_t* Wd, const int32_t* offsets,
                              const int32_t* row2slot, float* Y, int64_t N, hipStream_t stream) {
+  int32_t* off = const_cast<int32_t*>(offsets);
+  int32_t* r2s = const_cast<int32_t*>(row2slot);
   if (N <= kBf16TB1Tokens)
-    return launch_tiled<false, 1, 4, 1, false, true>(H, Wd, offsets, row2slot, Y, N, stream);
+    return launch_tiled<false, 1, 4, 1, false, true>(H, Wd, nullptr, off, r2s, Y, N, stream);
   if (N <= kShortTileTokens)
-    return launch_tiled<false, 1, 4, 2, false, true>(H, Wd, offsets, row2slot, Y, N, stream);
+    return launch_tiled<false, 1, 4, 2, false, true>(H, Wd, nullptr, off, r2s, Y, N, stream);
   if (N <= kOneTouchTokens)
-    return launch_tiled<false, 1, 4, 4, false, true>(H, Wd, offsets, row2slot, Y, N, stream);
-  if (N <= 2048) return launch_tiled<false, 1, 8>(H, Wd, offsets, row2slot, Y, N, stream);
-  if (N <= 6144) return launch_tiled<false, 2>(H, Wd, offsets, row2slot, Y, N, stream);
-  return launch_tiled<false, 2, 8>(H, Wd, offsets, row2slot, Y, N, stream);
+    return launch_tiled<false, 1, 4, 4, false, true>(H, Wd, nullptr, off, r2s, Y, N, stream);
+  if (N <= 2048) return launch_tiled<false, 1, 8>(H, Wd, nullptr, off, r2s, Y, N, stream);
+  if (N <= 6144) return launch_tiled<false, 2>(H, Wd, nullptr, off, r2s, Y, N, stream);
+  return launch_tiled<false, 2, 8>(H, Wd, nullptr, off, r2s, Y, N, stream);
 }
 
 hipError_t launch_gateup_tiled_fp8(const uint8_t* Xq, const uint8_t* Wq, const float* Ws,
-                                   const float* Xs, const int32_t* offsets, const int32_t* row2slot,
-                                   uint16_t* H, int64_t N, hipStream_t stream) {
+                                   const float* Xs, const int32_t* idx, int32_t* offsets,
+                                   int32_t* row2slot, uint16_t* H, int64_t N, hipStream_t stream) {
   if (N <= kShortTileTokens)
-    return launch_tiled<true, 1, 4, 2, true, true>(Xq, Wq, offsets, row2slot, H, N, stream, Ws, Xs);
+    return launch_tiled<true, 1, 4, 2, true, true, true>(Xq, Wq, idx, offsets, row2slot, H, N, stream, Ws, Xs);
   if (N <= kOneTouchTokens)
-    return launch_tiled<true, 1, 4, 4, true, true>(Xq, Wq, offsets, row2slot, H, N, stream, Ws, Xs);
+    return launch_tiled<true, 1, 4, 4, true, true>(Xq, Wq, idx, offsets, row2slot, H, N, stream, Ws, Xs);
   if (N <= kFp8NarrowTokens)
-    return launch_tiled<true, 1, 4, 4, true>(Xq, Wq, offsets, row2slot, H, N, stream, Ws, Xs);
-  return launch_tiled<true, 2, 8, 4, true>(Xq, Wq, offsets, row2slot, H, N, stream, Ws, Xs);
+    return launch_tiled<true, 1, 4, 4, true>(Xq, Wq, idx, offsets, row2slot, H, N, stream, Ws, Xs);
+  return launch_tiled<true, 2, 8, 4, true>(Xq, Wq, idx, offsets, row2slot, H, N, stream, Ws, Xs);
 }
 
 hipError_t launch_down_tiled_fp8(const uint8_t* Hq, const uint8_t* Wq, const float* Ws,
                                  const float* Hs, const int32_t* offsets, const int32_t* row2slot,
                                  float* Y, int64_t N, hipStream_t stream) {
+  int32_t* off = const_cast<int32_t*>(offsets);
+  int32_t* r2s = const_cast<int32_t*>(row2slot);
   if (N <= kShortTileTokens)
-    return launch_tiled<false, 1, 4, 2, true, true>(Hq, Wq, offsets, row2slot, Y, N, stream, Ws, Hs);
+    return launch_tiled<false, 1, 4, 2, true, true>(Hq, Wq, nullptr, off, r2s, Y, N, stream, Ws, Hs);
   if (N <= kOneTouchTokens)
-    return launch_tiled<false, 1, 4, 4, true, true>(Hq, Wq, offsets, row2slot, Y, N, stream, Ws, Hs);
+    return launch_tiled<false, 1, 4, 4, true, true>(Hq, Wq, nullptr, off, r2s, Y, N, stream, Ws, Hs);
   if (N <= kFp8NarrowTokens)
-    return launch_tiled<false, 1, 4, 4, true>(Hq, Wq, offsets, row2slot, Y, N, stream, Ws, Hs);
+    return launch_tiled<false, 1, 4, 4, true>(Hq, Wq, nullptr, off, r2s, Y, N, stream, Ws, Hs);
   // The two-block shapes spill a few registers, outside the stage loop.
-  if (N <= 6144) return launch_tiled<false, 2, 4, 4, true>(Hq, Wq, offsets, row2slot, Y, N, stream, Ws, Hs);
-  return launch_tiled<false, 2, 8, 4, true>(Hq, Wq, offsets, row2slot, Y, N, stream, Ws, Hs);
+  if (N <= 6144)
+    return launch_tiled<false, 2, 4, 4, true>(Hq, Wq, nullptr, off, r2s, Y, N, stream, Ws, Hs);
+  return launch_tiled<false, 2, 8, 4, true>(Hq, Wq, nullptr, off, r2s, Y, N, stream, Ws, Hs);
 }
 
 }  // namespace lfm

@@ -58,15 +58,19 @@ hipError_t launch_down_decode_fp8(const uint16_t* H, const uint8_t* Wq, const fl
 hipError_t launch_quantize_groups(const uint16_t* A, int64_t rows, int K, uint8_t* Q, float* S,
                                   hipStream_t stream);
 hipError_t launch_gateup_tiled_fp8(const uint8_t* Xq, const uint8_t* Wq, const float* Ws,
-                                   const float* Xs, const int32_t* offsets, const int32_t* row2slot,
-                                   uint16_t* H, int64_t N, hipStream_t stream);
+                                   const float* Xs, const int32_t* idx, int32_t* offsets,
+                                   int32_t* row2slot, uint16_t* H, int64_t N, hipStream_t stream);
 hipError_t launch_down_tiled_fp8(const uint8_t* Hq, const uint8_t* Wq, const float* Ws,
                                  const float* Hs, const int32_t* offsets, const int32_t* row2slot,
                                  float* Y, int64_t N, hipStream_t stream);
 
-// Grouped path, LDS-tiled MFMA kernels (prefill-shaped batches).
-hipError_t launch_gateup_tiled(const uint16_t* X, const uint16_t* Wgu, const int32_t* offsets,
-                               const int32_t* row2slot, uint16_t* H, int64_t N,
+// Grouped path, LDS-tiled MFMA kernels.  Where gateup_groups_slots(N) the
+// gate/up kernels group the slots themselves from idx (no dispatch step)
+// and write offsets and row2slot for the down kernels; otherwise they read
+// the dispatch step's.
+bool gateup_groups_slots(int64_t N);
+hipError_t launch_gateup_tiled(const uint16_t* X, const uint16_t* Wgu, const int32_t* idx,
+                               int32_t* offsets, int32_t* row2slot, uint16_t* H, int64_t N,
                                hipStream_t stream);
 hipError_t launch_down_tiled(const uint16_t* H, const uint16_t* Wd, const int32_t* offsets,
                              const int32_t* row2slot, float* Y, int64_t N, hipStream_t stream);
