@@ -26,40 +26,37 @@ constexpr int kRowThreads = 256;  // one token row of 2048 values per workgroup
 
 // Thread `tid`'s part of row t: sum_j w[t, j] * Y[t*4 + j] (+ resid[t]) over
 // columns (h * kRowThreads + tid) * 4 .. + 3, h = 0, 1.
+// Four values (columns col .. col + 3) of out[t] = (resid[t] +) sum_j
+// w[t, j] * Y[t*4 + j], in the fixed order j = 0..3.
+__device__ __forceinline__ float4 combine4(const float* __restrict__ Y, const float4 wt, const float* resid,
+                                          size_t t, int col) {
+  const float* y0 = Y + t * kTopK * kHidden + col;
+  const float4 a = *reinterpret_cast<const float4*>(y0);
+  const float4 b = *reinterpret_cast<const float4*>(y0 + kHidden);
+  const float4 c = *reinterpret_cast<const float4*>(y0 + 2 * kHidden);
+  const float4 d = *reinterpret_cast<const float4*>(y0 + 3 * kHidden);
+  float4 acc;
+  acc.x = fmaf(wt.w, d.x, fmaf(wt.z, c.x, fmaf(wt.y, b.x, wt.x * a.x)));
+  acc.y = fmaf(wt.w, d.y, fmaf(wt.z, c.y, fmaf(wt.y, b.y, wt.x * a.y)));
+  acc.z = fmaf(wt.w, d.z, fmaf(wt.z, c.z, fmaf(wt.y, b.z, wt.x * a.z)));
+  acc.w = fmaf(wt.w, d.w, fmaf(wt.z, c.w, fmaf(wt.y, b.w, wt.x * a.w)));
+  if (resid != nullptr) {
+    const float4 x = *reinterpret_cast<const float4*>(resid + t * kHidden + col);
+    acc.x = x.x + acc.x;
+    acc.y = x.y + acc.y;
+    acc.z = x.z + acc.z;
+    acc.w = x.w + acc.w;
+  }
+  return acc;
+}
+
 __device__ __forceinline__ void combine_row(const float* __restrict__ Y, const float* __restrict__ w,
                                             const float* resid, size_t t, float4 (&v)[2]) {
   const float4 wt = *reinterpret_cast<const float4*>(w + t * kTopK);
-  const float* y0 = Y + t * kTopK * kHidden;
-  const float* y1 = y0 + kHidden;
-  const float* y2 = y1 + kHidden;
-  const float* y3 = y2 + kHidden;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int col = (h * kRowThreads + threadIdx.x) * 4;
-    const float4 a = *reinterpret_cast<const float4*>(y0 + col);
-    const float4 b = *reinterpret_cast<const float4*>(y1 + col);
-    const float4 c = *reinterpret_cast<const float4*>(y2 + col);
-    const float4 d = *reinterpret_cast<const float4*>(y3 + col);
-    float4 acc;
-    acc.x = fmaf(wt.w, d.x, fmaf(wt.z, c.x, fmaf(wt.y, b.x, wt.x * a.x)));
-    acc.y = fmaf(wt.w, d.y, fmaf(wt.z, c.y, fmaf(wt.y, b.y, wt.x * a.y)));
-    acc.z = fmaf(wt.w, d.z, fmaf(wt.z, c.z, fmaf(wt.y, b.z, wt.x * a.z)));
-    acc.w = fmaf(wt.w, d.w, fmaf(wt.z, c.w, fmaf(wt.y, b.w, wt.x * a.w)));
-    if (resid != nullptr) {
-      const float4 x = *reinterpret_cast<const float4*>(resid + t * kHidden + col);
-      acc.x = x.x + acc.x;
-      acc.y = x.y + acc.y;
-      acc.z = x.z + acc.z;
-      acc.w = x.w + acc.w;
-    }
-    v[h] = acc;
-  }
+  for (int h = 0; h < 2; ++h) v[h] = combine4(Y, wt, resid, t, (h * kRowThreads + threadIdx.x) * 4);
 }
 
-// X[t] = bf16(v / sqrt(mean(v^2) + eps)) (unit weight) for the row whose
-// columns (h * kRowThreads + tid) * 4 .. + 3 thread tid holds in v[h]; the
-// sum of squares in a fixed order (per thread, then the wavefront's
-// butterfly, then the four wavefronts in pairs).
 __device__ __forceinline__ void norm_row(const float4 (&v)[2], size_t t, float* wave_ss,
                                          uint16_t* __restrict__ X) {
   float ss = 0.0f;
@@ -101,6 +98,20 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(const float* __res
   store_row(v, blockIdx.x, out);
 }
 
+// The same for small batches: a quarter row (512 values) per workgroup,
+// four workgroups per token, so that more of the device has loads in
+// flight; the same arithmetic per value.
+constexpr int kQuarterThreads = kRowThreads / 2;
+constexpr int64_t kQuarterRowTokens = 256;
+__global__ __launch_bounds__(kQuarterThreads) void combine_quarter_kernel(const float* __restrict__ Y,
+                                                                          const float* __restrict__ w,
+                                                                          const float* resid, float* out) {
+  const size_t t = blockIdx.x;
+  const int col = (blockIdx.y * kQuarterThreads + threadIdx.x) * 4;
+  const float4 wt = *reinterpret_cast<const float4*>(w + t * kTopK);
+  *reinterpret_cast<float4*>(out + t * kHidden + col) = combine4(Y, wt, resid, t, col);
+}
+
 // The same with the residual (x <- x + sum_j ...), then the next block's
 // input Xn[t] = bf16(RMSNorm(x[t])) from the new row.
 __global__ __launch_bounds__(kRowThreads) void combine_norm_kernel(const float* __restrict__ Y,
@@ -129,7 +140,11 @@ __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const float* __res
 
 hipError_t launch_combine(const float* Y, const float* w, const float* resid, float* out,
                           int64_t N, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(N), dim3(kRowThreads), 0, stream, Y, w, resid, out);
+  static_assert(4 * kQuarterThreads * 4 == kHidden, "four quarters of a row");
+  if (N <= kQuarterRowTokens)
+    hipLaunchKernelGGL(combine_quarter_kernel, dim3(N, 4), dim3(kQuarterThreads), 0, stream, Y, w, resid, out);
+  else
+    hipLaunchKernelGGL(combine_kernel, dim3(N), dim3(kRowThreads), 0, stream, Y, w, resid, out);
   return hipGetLastError();
 }
 
