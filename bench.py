@@ -63,12 +63,22 @@ def fp8_layer_bytes(A, N):
     return A * (FP8_GATEUP_W_BYTES + FP8_DOWN_W_BYTES) + ROUTER_BYTES + N * (D * 2 + D * 4)
 
 
+FP8_STREAM = 4  # FP8 layer: weight-streaming kernels up to this many tokens
+
+
+def fp8_act_bytes(rows, width, N):
+    """Bytes of the rows an FP8 kernel reads: bf16 for the weight-streaming
+    kernels (they quantise in registers), E4M3 codes plus a fp32 scale per
+    128 values for the grouped ones."""
+    return rows * width * 2 if N <= FP8_STREAM else rows * (width + width // 128 * 4)
+
+
 def fp8_gateup_bytes(A, N):
-    return A * FP8_GATEUP_W_BYTES + N * D * 2 + K * N * FF * 2
+    return A * FP8_GATEUP_W_BYTES + fp8_act_bytes(N, D, N) + K * N * FF * 2
 
 
 def fp8_down_bytes(A, N):
-    return A * FP8_DOWN_W_BYTES + K * N * FF * 2 + K * N * D * 4
+    return A * FP8_DOWN_W_BYTES + fp8_act_bytes(K * N, FF, N) + K * N * D * 4
 
 
 def down_bytes(A, N):
@@ -226,7 +236,6 @@ def summarize(p, wall_ms, per_kernel):
     )
 
 
-FP8_STREAM = 4  # FP8 layer: weight-streaming kernels up to this many tokens
 
 
 def summarize_fp8(p, wall_ms, per_kernel, label, note):

@@ -28,7 +28,10 @@ def test_algorithmic_counts():
     # FP8 experts: one byte per weight and a fp32 scale per 128 x 128 block
     # (gate and up: 2 x 12 x 16 blocks, down: 16 x 12).
     assert bench.FP8_GATEUP_W_BYTES + bench.FP8_DOWN_W_BYTES == 9_437_184 + (384 + 192) * 4
-    assert bench.fp8_gateup_bytes(40, 64) == 40 * 6_292_992 + 64 * 4096 + 256 * 3072
+    # grouped kernels (N > 4): token codes and scales; streaming kernels: bf16 rows
+    assert bench.fp8_gateup_bytes(40, 64) == 40 * 6_292_992 + 64 * (2048 + 64) + 256 * 3072
+    assert bench.fp8_gateup_bytes(40, 4) == 40 * 6_292_992 + 4 * 4096 + 16 * 3072
+    assert bench.fp8_down_bytes(40, 64) == 40 * 3_146_496 + 256 * (1536 + 48) + 256 * 8192
 
 
 def _summary(N, A, ms, gu_ms):
