@@ -251,8 +251,9 @@ void expert_tiled_kernel(
 
   // Token pieces of this thread: row r0 + kRowStep * i of the tile, 16-byte
   // chunk c of the row's 128-byte line of a stage pair; eight consecutive
-  // lanes read one whole line.  All the pieces share c and r0 % 32, so their
-  // LDS positions differ by whole token-block fragments.
+  // lanes read one whole line.  With 32 or more rows per pass the pieces
+  // share r0 % 32, so their LDS positions differ by whole token-block
+  // fragments (the 2-wavefront shapes take 16 rows per pass).
   const int r0 = tid / 8, c = tid % 8;
   const uint8_t* arow[T::kChunks];
 #pragma unroll
@@ -262,9 +263,16 @@ void expert_tiled_kernel(
     arow[i] = static_cast<const uint8_t*>(A) +
               static_cast<size_t>(GATEUP ? slot / kTopK : slot) * kRowBytes + c * 16;
   }
-  const int st_pos = ((c / 4) * TB * kKS + (c / 2) % 2) * kWave + (c % 2) * 32 + ((r0 % 32) ^ swz(c)) +
-                     (r0 / 32) * kKS * kWave;
-  static_assert(T::kRowStep % 32 == 0, "a thread's pieces share their row within a token block");
+  constexpr bool kWholeBlocks = T::kRowStep % 32 == 0;
+  static_assert(T::kRowStep % 16 == 0 && T::kChunks >= 1, "whole 16-row groups per pass");
+  auto st_at = [&](int i) {
+    const int r = r0 + T::kRowStep * i;
+    return ((c / 4) * TB * kKS + (c / 2) % 2) * kWave + (c % 2) * 32 + ((r % 32) ^ swz(c)) +
+           (r / 32) * kKS * kWave;
+  };
+  int st_pos[kWholeBlocks ? 1 : T::kChunks];
+#pragma unroll
+  for (int i = 0; i < (kWholeBlocks ? 1 : T::kChunks); ++i) st_pos[i] = st_at(i);
   // MFMA operand position of this lane for stage sp of a pair, K step (bf16)
   // or K half (FP8) j.
   int rd_pos[2][kKS];
@@ -327,7 +335,8 @@ void expert_tiled_kernel(
   };
   auto store_x = [&](int pb) {
 #pragma unroll
-    for (int i = 0; i < T::kChunks; ++i) tok[pb][st_pos + i * (T::kRowStep / 32) * kKS * kWave] = stg[i];
+    for (int i = 0; i < T::kChunks; ++i)
+      tok[pb][kWholeBlocks ? st_pos[0] + i * (T::kRowStep / 32) * kKS * kWave : st_pos[i]] = stg[i];
   };
 
   f32x16 acc[TB][FB];
@@ -571,7 +580,9 @@ int64_t tiled_grid(int64_t N) {
 //  * Up to 256 tokens (bf16: from 5; FP8: from 5): 128 weight rows (4
 //    wavefronts x one block), token tiles of 32 rows up to 96 tokens (bf16)
 //    and of 64 rows otherwise (the FP8 mode needs an even number of token
-//    blocks).  Measured, layer us at N = 64 (the 64-token decode workload;
+//    blocks); down takes 64 weight rows (2 wavefronts x one block) up to 96
+//    tokens, which doubles its tile count (N = 64, down us, 128 / 64 weight
+//    rows: bf16 46.1 / 44.5, FP8 31.3 / 30.7-30.9; N = 256: 55.4 / 59.5).  Measured, layer us at N = 64 (the 64-token decode workload;
 //    the streaming kernels / 128 token rows / 64 / 32): bf16 143.4-146.5 /
 //    140.3-141.5 / 137.5-137.7 / 136.6-136.9; FP8 102.0-102.5 (streaming) /
 //    90.6-95.9 / 84.0-84.4.  First N tokens of the 4,096-token workload
@@ -612,7 +623,7 @@ int64_t tiled_grid(int64_t N) {
 // 165.5-165.9).
 constexpr int64_t kOneTouchTokens = 512;
 constexpr int64_t kShortTileTokens = 256;  // 128 weight rows, short token tiles
-constexpr int64_t kBf16TB1Tokens = 96;     // bf16: 32-row token tiles up to here
+constexpr int64_t kBf16TB1Tokens = 96;     // bf16: 32-row token tiles up to here; down: 64 weight rows
 constexpr int64_t kFp8NarrowTokens = 2048; // FP8: 128 x 128 tiles up to here
 
 template <bool GATEUP, int FB, int WAVES = (GATEUP ? 8 : 4), int TB = 4, bool FP8 = false,
@@ -654,7 +665,7 @@ hipError_t launch_down_tiled(const uint16_t* H, const uint16_t* Wd, const int32_
   int32_t* off = const_cast<int32_t*>(offsets);
   int32_t* r2s = const_cast<int32_t*>(row2slot);
   if (N <= kBf16TB1Tokens)
-    return launch_tiled<false, 1, 4, 1, false, true>(H, Wd, nullptr, off, r2s, Y, N, stream);
+    return launch_tiled<false, 1, 2, 1, false, true>(H, Wd, nullptr, off, r2s, Y, N, stream);
   if (N <= kShortTileTokens)
     return launch_tiled<false, 1, 4, 2, false, true>(H, Wd, nullptr, off, r2s, Y, N, stream);
   if (N <= kOneTouchTokens)
@@ -681,6 +692,8 @@ hipError_t launch_down_tiled_fp8(const uint8_t* Hq, const uint8_t* Wq, const flo
                                  float* Y, int64_t N, hipStream_t stream) {
   int32_t* off = const_cast<int32_t*>(offsets);
   int32_t* r2s = const_cast<int32_t*>(row2slot);
+  if (N <= kBf16TB1Tokens)
+    return launch_tiled<false, 1, 2, 2, true, true>(Hq, Wq, nullptr, off, r2s, Y, N, stream, Ws, Hs);
   if (N <= kShortTileTokens)
     return launch_tiled<false, 1, 4, 2, true, true>(Hq, Wq, nullptr, off, r2s, Y, N, stream, Ws, Hs);
   if (N <= kOneTouchTokens)
