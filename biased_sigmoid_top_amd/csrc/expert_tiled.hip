@@ -137,9 +137,9 @@ __device__ __forceinline__ f32x16 mfma32_fp8(const uint4& a0, const uint4& a1, c
 // Slots of at most kSelfTokens tokens grouped by expert, as the dispatch
 // step groups them (offsets: exclusive prefix of the per-expert counts;
 // rows: slots t * 4 + j of each expert in token order), computed in LDS by
-// one workgroup of at least kSelfTokens threads, one token per thread:
-// per-expert token bitmasks, a word prefix per expert, a prefix over the
-// experts, then each slot's rank from one popcount.  A token's four experts
+// one workgroup of at least kExperts threads, token t on thread t %
+// nthreads: per-expert token bitmasks, a word prefix per expert, a prefix
+// over the experts, then each slot's rank from one popcount.  A token's four experts
 // are distinct, so each (expert, token) bit is set once.  scratch holds at
 // least 2 * kExperts * kSelfWords words and is free again on return.
 constexpr int kSelfTokens = 256;
@@ -151,12 +151,11 @@ __device__ __forceinline__ void group_slots_lds(const int32_t* __restrict__ idx,
   const int tid = threadIdx.x;
   for (int i = tid; i < kExperts * kSelfWords; i += nthreads) (&mask[0][0])[i] = 0u;
   __syncthreads();
-  int my_e[kTopK];
-  if (tid < N) {
-    const int4 v = *reinterpret_cast<const int4*>(idx + static_cast<size_t>(tid) * kTopK);
-    my_e[0] = v.x; my_e[1] = v.y; my_e[2] = v.z; my_e[3] = v.w;
+  for (int t = tid; t < N; t += nthreads) {
+    const int4 v = *reinterpret_cast<const int4*>(idx + static_cast<size_t>(t) * kTopK);
+    const int e4[kTopK] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int j = 0; j < kTopK; ++j) atomicOr(&mask[my_e[j]][tid / 32], 1u << (tid % 32));
+    for (int j = 0; j < kTopK; ++j) atomicOr(&mask[e4[j]][t / 32], 1u << (t % 32));
   }
   __syncthreads();
   if (tid < kExperts) {  // wavefront 0, lane = expert
@@ -171,12 +170,14 @@ __device__ __forceinline__ void group_slots_lds(const int32_t* __restrict__ idx,
     if (tid == kExperts - 1) off[kExperts] = incl;
   }
   __syncthreads();
-  if (tid < N) {
+  for (int t = tid; t < N; t += nthreads) {
+    const int4 v = *reinterpret_cast<const int4*>(idx + static_cast<size_t>(t) * kTopK);
+    const int e4[kTopK] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int j = 0; j < kTopK; ++j) {
-      const int e = my_e[j];
-      const int rank = wbase[e][tid / 32] + __popc(mask[e][tid / 32] & ((1u << (tid % 32)) - 1u));
-      rows[off[e] + rank] = tid * kTopK + j;
+      const int e = e4[j];
+      const int rank = wbase[e][t / 32] + __popc(mask[e][t / 32] & ((1u << (t % 32)) - 1u));
+      rows[off[e] + rank] = t * kTopK + j;
     }
   }
   __syncthreads();
@@ -230,9 +231,9 @@ void expert_tiled_kernel(
   const int32_t* grp_off = offsets;
   const int32_t* grp_rows = row2slot;
   if constexpr (SELF) {
-    static_assert(GATEUP && T::kThreads >= kSelfTokens &&
+    static_assert(GATEUP && T::kThreads >= kExperts &&
                       sizeof(tok) >= 2 * kExperts * kSelfWords * sizeof(uint32_t),
-                  "one token per thread; the masks fit in the token tile");
+                  "a wavefront of experts; the masks fit in the token tile");
     group_slots_lds(idx, ntok, self_off, self_rows, reinterpret_cast<uint32_t*>(&tok[0][0]), T::kThreads);
     if (blockIdx.x == 0) {
       for (int i = threadIdx.x; i <= kExperts; i += T::kThreads) offsets[i] = self_off[i];
@@ -580,9 +581,12 @@ int64_t tiled_grid(int64_t N) {
 //  * Up to 256 tokens (bf16: from 5; FP8: from 5): 128 weight rows (4
 //    wavefronts x one block), token tiles of 32 rows up to 96 tokens (bf16)
 //    and of 64 rows otherwise (the FP8 mode needs an even number of token
-//    blocks); down takes 64 weight rows (2 wavefronts x one block) up to 96
-//    tokens, which doubles its tile count (N = 64, down us, 128 / 64 weight
-//    rows: bf16 46.1 / 44.5, FP8 31.3 / 30.7-30.9; N = 256: 55.4 / 59.5).  Measured, layer us at N = 64 (the 64-token decode workload;
+//    blocks).  Up to 96 tokens down, and bf16 gate/up, take 64 weight rows
+//    (2 wavefronts x one block), which doubles their tile counts.  Down us,
+//    128 / 64 weight rows: N = 64 bf16 46.1 / 44.5, FP8 31.3 / 30.7-30.9;
+//    N = 256: 55.4 / 59.5.  bf16 gate/up: N = 16 58.2 / 55.6, 32 62.5 /
+//    63.6, 64 85.6-85.9 / 84.6, 96 80.8 / 76.1; FP8 gate/up at N = 64 46.6 /
+//    48.1 (kept at 128 rows).  Measured, layer us at N = 64 (the 64-token decode workload;
 //    the streaming kernels / 128 token rows / 64 / 32): bf16 143.4-146.5 /
 //    140.3-141.5 / 137.5-137.7 / 136.6-136.9; FP8 102.0-102.5 (streaming) /
 //    90.6-95.9 / 84.0-84.4.  First N tokens of the 4,096-token workload
@@ -623,7 +627,7 @@ int64_t tiled_grid(int64_t N) {
 // 165.5-165.9).
 constexpr int64_t kOneTouchTokens = 512;
 constexpr int64_t kShortTileTokens = 256;  // 128 weight rows, short token tiles
-constexpr int64_t kBf16TB1Tokens = 96;     // bf16: 32-row token tiles up to here; down: 64 weight rows
+constexpr int64_t kBf16TB1Tokens = 96;     // bf16: 32-row token tiles up to here; 64 weight rows (down: FP8 too)
 constexpr int64_t kFp8NarrowTokens = 2048; // FP8: 128 x 128 tiles up to here
 
 template <bool GATEUP, int FB, int WAVES = (GATEUP ? 8 : 4), int TB = 4, bool FP8 = false,
@@ -650,7 +654,7 @@ hipError_t launch_gateup_tiled(const uint16_t* X, const uint16_t* Wgu, const int
                                int32_t* offsets, int32_t* row2slot, uint16_t* H, int64_t N,
                                hipStream_t stream) {
   if (N <= kBf16TB1Tokens)
-    return launch_tiled<true, 1, 4, 1, false, true, true>(X, Wgu, idx, offsets, row2slot, H, N, stream);
+    return launch_tiled<true, 1, 2, 1, false, true, true>(X, Wgu, idx, offsets, row2slot, H, N, stream);
   if (N <= kShortTileTokens)
     return launch_tiled<true, 1, 4, 2, false, true, true>(X, Wgu, idx, offsets, row2slot, H, N, stream);
   if (N <= kOneTouchTokens)
