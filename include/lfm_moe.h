@@ -181,7 +181,7 @@ size_t lfm_moe_workspace_bytes(int64_t N);
 typedef enum {
   LFM_MOE_WS_IDX = 0,       /* [N, 4] int32 selected experts */
   LFM_MOE_WS_W = 1,         /* [N, 4] fp32 mixture weights */
-  LFM_MOE_WS_BLOCKCOUNTS = 2, /* [ceil(N / 16), 64] int32 per-16-token histogram (grouped path) */
+  LFM_MOE_WS_BLOCKCOUNTS = 2, /* [ceil(N / 16), 64] int32 per-16-token histogram (dispatch step) */
   LFM_MOE_WS_OFFSETS = 3,   /* [65] int32: offsets[e] = first grouped row of expert e, offsets[64] = 4N */
   LFM_MOE_WS_ROW2SLOT = 4,  /* [4N] int32 grouped row -> slot t*4 + j (stable: token order inside an expert) */
   LFM_MOE_WS_H = 5,         /* [4N, 1536] bf16 expert hidden rows, slot order (row t*4 + j) */
@@ -207,9 +207,11 @@ size_t lfm_moe_workspace_offset(int64_t N, int region);
  * overlapping neither the output nor any input tensor: every _ws entry
  * point returns LFM_MOE_ERR_INVALID_ARGUMENT otherwise).
  * The workspace holds the intermediate results listed in lfm_moe_ws_region
- * after the call completes.  Batches of up to 96 tokens take the
- * decode-shaped path, whose expert kernels group their own tokens and leave
- * BLOCKCOUNTS, OFFSETS and ROW2SLOT unwritten; larger batches write them.
+ * after the call completes.  Batches of up to 4 tokens take the
+ * weight-streaming kernels, which group their own tokens and leave
+ * BLOCKCOUNTS, OFFSETS and ROW2SLOT unwritten; batches of 5 to 256 tokens
+ * are grouped by the gate/up kernel, which writes OFFSETS and ROW2SLOT
+ * (BLOCKCOUNTS stays unwritten); larger batches write all three.
  * Concurrent calls need distinct workspaces.
  */
 lfm_moe_status lfm_moe_forward_ws(const uint16_t* X, const uint16_t* W_r, const float* bias,
@@ -254,8 +256,9 @@ lfm_moe_status lfm_moe_experts_ws(const uint16_t* X, const int32_t* idx, const f
  * regions).  Between calls a test may overwrite the H region (bf16
  * [4N, 1536], slot order) or the Y region (fp32 [4N, 2048], slot order)
  * with values of its own, to check the next stage alone; the IDX, W,
- * BLOCKCOUNTS, OFFSETS and ROW2SLOT regions must hold what
- * lfm_moe_stage_dispatch (or a layer call with the same N) stored there.
+ * OFFSETS and ROW2SLOT regions must hold what lfm_moe_stage_dispatch (or a
+ * layer call with the same N) stored there (for 5 to 256 tokens the gate/up
+ * stage recomputes OFFSETS and ROW2SLOT from IDX, with the same result).
  * Asynchronous on stream; arguments checked before any HIP call; N == 0 is
  * a no-op; 0 <= N <= LFM_MOE_MAX_TOKENS.
  *

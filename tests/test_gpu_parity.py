@@ -367,7 +367,8 @@ def test_verification_batches(moe, c):
 @pytest.mark.parametrize("N", [3, 17, 200, 300, 1000, 4096, 6145])
 def test_writes_stay_in_bounds(moe, N):
     """Canaries after the output rows and after the workspace's documented
-    size are left untouched (decode path and every grouped tile shape)."""
+    size are left untouched (weight-streaming kernels and every grouped tile
+    shape)."""
     inp, dev = _layer_case(N, 700 + N)
     _step(f"canaries N={N}")
     out_all = torch.full((N + 8, 2048), 12345.0, dtype=torch.float32, device="cuda")
@@ -434,7 +435,7 @@ def test_concurrent_streams_with_distinct_workspaces(moe):
 
 def test_stage_timing_counts_and_times(moe):
     """lfm_moe_timing_*: with timing on, each call records one launch per
-    stage it runs (the decode path has no dispatch stage) with a positive
+    stage it runs (no dispatch stage up to 256 tokens) with a positive
     time; after timing is switched off nothing more is recorded."""
     for N, stages in ((3, ("route", "gateup", "down", "combine")),
                       (300, ("route", "dispatch", "gateup", "down", "combine"))):

@@ -1,7 +1,8 @@
 """lfm_moe_forward_noalloc (the allocation-free layer entry point) through
-the C ABI, against lfm_moe_forward on the same inputs: bit for bit, on two
-calls in a row, the second with a smaller batch (grouped path, then the
-decode-shaped path), and with no change of the device's free memory."""
+the C ABI, against lfm_moe_forward on the same inputs: bit for bit, on
+three calls in a row, each with a smaller batch (256 and 64 tokens on the
+grouped kernels, 3 on the weight-streaming kernels), and with no change of
+the device's free memory."""
 
 import ctypes
 
