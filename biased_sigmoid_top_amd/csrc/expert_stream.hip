@@ -1,6 +1,5 @@
 // Expert GEMMs that stream the weights straight into MFMA registers: the
-// path of the smallest batches (up to kDecodeMaxTokens tokens, one or two
-// per expert).
+// path of the smallest batches (up to kDecodeMaxTokens tokens).
 //
 // Method: each selected expert is a gated SiLU MLP with three matrices
 // (flozi.net guide "LFM2.5-24B-A2B: Biased Routing, Short Convolutions and

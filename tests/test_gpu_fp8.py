@@ -167,6 +167,8 @@ def _check_fp8_forward(moe, inp, dev, q, N):
     y_rms = float(np.sqrt(np.mean(Y_tf ** 2)))
     y_err = float(np.max((np.abs(Y - Y_tf) - Y_acc) / y_rms))
     assert y_err <= 1e-4, y_err
+    if grouped:
+        _check_quantised_regions(moe, ws, N, inp["X"], H)
     comb = (w[:, :, None] * Y.reshape(N, 4, 2048)).sum(axis=1)
     c_err = float(np.max(np.abs(out - comb))) / float(np.sqrt(np.mean(comb ** 2)))
     assert c_err <= 1e-5, c_err
@@ -181,6 +183,29 @@ def _check_fp8_forward(moe, inp, dev, q, N):
           f"({res['code_flips']} of {H.size} H codes and {res['scale_flips']} group scales differ); "
           f"vs bf16 oracle {ratio16:.4f}", flush=True)
     assert ratio16 > 2 * max(res["end_to_end"], OUT_GATE_FP8)
+
+
+def _unpermute_runs(q):
+    """Inverse of the documented XQ / HQ byte order: in every 32-wide piece
+    of a row the 8-code runs are stored in the order 0, 2, 1, 3."""
+    M, K = q.shape
+    return q.reshape(M, K // 32, 4, 8)[:, :, [0, 2, 1, 3], :].reshape(M, K)
+
+
+def _check_quantised_regions(moe, ws, N, X, H):
+    """The grouped path's XQ/XS and HQ/HS regions hold the oracle's group
+    quantisation of X and of the GPU's own bf16 H (the codes are a decision
+    taken from the same values on both sides), bit for bit, in the byte
+    order the header documents."""
+    from biased_sigmoid_top_amd import _lib
+    from oracle import fp8
+    view = lambda reg, dt, shape: _np(moe.workspace_view(ws, N, reg, dt, shape))
+    for qreg, sreg, A, rows, K in ((_lib.WS_XQ, _lib.WS_XS, X, N, 2048),
+                                   (_lib.WS_HQ, _lib.WS_HS, H, 4 * N, 1536)):
+        codes, scales = fp8.quantize_groups(A)
+        got = _unpermute_runs(view(qreg, torch.uint8, (rows, K)))
+        np.testing.assert_array_equal(got, codes)
+        np.testing.assert_array_equal(view(sreg, torch.float32, (rows, K // 128)), scales)
 
 
 def test_fp8_forward_parity_decode_n64(moe):
