@@ -344,7 +344,7 @@ lfm_moe_status run_layer(const uint16_t* X, const uint16_t* W_r, const float* bi
   float* part = region<float>(ws, N, LFM_MOE_WS_ROUTER_PARTIAL);
   const int n = static_cast<int>(N);
   const bool decode = use_decode_path(N);
-  const bool dispatch = !decode && !gateup_groups_slots(N);
+  const bool dispatch = !decode && !gateup_groups_slots(N, false);
   hipError_t e;
   if ((e = route_or_ingest(X, W_r, bias, idx_in, w_in, idx, w, dispatch ? blockcounts : nullptr, part, n,
                            stream)) != hipSuccess)
@@ -429,7 +429,7 @@ lfm_moe_status run_fp8(const uint16_t* X, const uint16_t* W_r, const float* bias
   float* part = region<float>(ws, N, LFM_MOE_WS_ROUTER_PARTIAL);
   const int n = static_cast<int>(N);
   const bool streaming = N <= LFM_MOE_FP8_STREAM_TOKENS;
-  const bool dispatch = !streaming && !gateup_groups_slots(N);
+  const bool dispatch = !streaming && !gateup_groups_slots(N, true);
   int32_t* blockcounts = region<int32_t>(ws, N, LFM_MOE_WS_BLOCKCOUNTS);
   hipError_t e;
   if ((e = route_or_ingest(X, W_r, bias, idx_in, w_in, idx, w, dispatch ? blockcounts : nullptr, part,

@@ -134,7 +134,7 @@ __device__ __forceinline__ f32x16 mfma32_fp8(const uint4& a0, const uint4& a1, c
 // by old unit / new unit, and at the end by the last units.  Where a scale
 // is 0 the group's codes are all 0, and that unit stays.  The scales of a
 // tile are staged in LDS once, before the stage loop.
-// Slots of at most kSelfTokens tokens grouped by expert, as the dispatch
+// Slots of at most 32 * kSelfWords tokens grouped by expert, as the dispatch
 // step groups them (offsets: exclusive prefix of the per-expert counts;
 // rows: slots t * 4 + j of each expert in token order), computed in LDS by
 // one workgroup of at least kExperts threads, token t on thread t %
@@ -142,8 +142,11 @@ __device__ __forceinline__ f32x16 mfma32_fp8(const uint4& a0, const uint4& a1, c
 // over the experts, then each slot's rank from one popcount.  A token's four experts
 // are distinct, so each (expert, token) bit is set once.  scratch holds at
 // least 2 * kExperts * kSelfWords words and is free again on return.
-constexpr int kSelfTokens = 256;
-constexpr int kSelfWords = kSelfTokens / 32;
+// Capacity: 512 tokens in the 128-row token tiles, 256 in the shorter ones
+// (whose LDS token tile holds the masks of 256).
+constexpr int kSelfTokens = 512;
+constexpr int kSelfShortTokens = 256;
+template <int kSelfWords>
 __device__ __forceinline__ void group_slots_lds(const int32_t* __restrict__ idx, int N, int* off,
                                                 int* rows, uint32_t* scratch, int nthreads) {
   uint32_t (*mask)[kSelfWords] = reinterpret_cast<uint32_t (*)[kSelfWords]>(scratch);
@@ -227,14 +230,16 @@ void expert_tiled_kernel(
   // from the selections, and workgroup 0 publishes the grouping for the
   // down kernel; otherwise the dispatch step's grouping is read.
   __shared__ int self_off[SELF ? kExperts + 1 : 1];
-  __shared__ int self_rows[SELF ? kSelfTokens * kTopK : 1];
+  constexpr int kSelfCap = TB >= 4 ? kSelfTokens : kSelfShortTokens;
+  constexpr int kSelfWords = kSelfCap / 32;
+  __shared__ int self_rows[SELF ? kSelfCap * kTopK : 1];
   const int32_t* grp_off = offsets;
   const int32_t* grp_rows = row2slot;
   if constexpr (SELF) {
     static_assert(GATEUP && T::kThreads >= kExperts &&
                       sizeof(tok) >= 2 * kExperts * kSelfWords * sizeof(uint32_t),
                   "a wavefront of experts; the masks fit in the token tile");
-    group_slots_lds(idx, ntok, self_off, self_rows, reinterpret_cast<uint32_t*>(&tok[0][0]), T::kThreads);
+    group_slots_lds<kSelfWords>(idx, ntok, self_off, self_rows, reinterpret_cast<uint32_t*>(&tok[0][0]), T::kThreads);
     if (blockIdx.x == 0) {
       for (int i = threadIdx.x; i <= kExperts; i += T::kThreads) offsets[i] = self_off[i];
       for (int i = threadIdx.x; i < ntok * kTopK; i += T::kThreads) row2slot[i] = self_rows[i];
@@ -647,8 +652,14 @@ hipError_t launch_tiled(const void* A, const void* W, const int32_t* idx, int32_
 
 }  // namespace
 
-bool gateup_groups_slots(int64_t N) { return N <= kShortTileTokens; }
-static_assert(kShortTileTokens <= kSelfTokens, "short-tile batches are grouped in the gate/up kernel");
+// bf16: up to 512 tokens (N = 320 / 512, layer us, dispatch step / grouping
+// in the gate/up kernel: 192.5-196.2 / 188.6-189.6, 215.5-216.7 /
+// 211.6-212.0; with the grouping up to 1,024 tokens N = 1,024 took
+// 250.4-253.1 / 251.2-254.2).  FP8: up to 256 tokens (at N = 320 the FP8
+// layer took 136.8-137.3 with the dispatch step, 143.1-143.6 without).
+bool gateup_groups_slots(int64_t N, bool fp8) { return N <= (fp8 ? kShortTileTokens : kSelfTokens); }
+static_assert(kShortTileTokens <= kSelfShortTokens && kOneTouchTokens == kSelfTokens,
+              "the grouping fits the tiles that take it");
 
 hipError_t launch_gateup_tiled(const uint16_t* X, const uint16_t* Wgu, const int32_t* idx,
                                int32_t* offsets, int32_t* row2slot, uint16_t* H, int64_t N,
@@ -658,7 +669,7 @@ hipError_t launch_gateup_tiled(const uint16_t* X, const uint16_t* Wgu, const int
   if (N <= kShortTileTokens)
     return launch_tiled<true, 1, 4, 2, false, true, true>(X, Wgu, idx, offsets, row2slot, H, N, stream);
   if (N <= kOneTouchTokens)
-    return launch_tiled<true, 1, 4, 4, false, true>(X, Wgu, idx, offsets, row2slot, H, N, stream);
+    return launch_tiled<true, 1, 4, 4, false, true, true>(X, Wgu, idx, offsets, row2slot, H, N, stream);
   if (N <= 2048) return launch_tiled<true, 1>(X, Wgu, idx, offsets, row2slot, H, N, stream);
   return launch_tiled<true, 2>(X, Wgu, idx, offsets, row2slot, H, N, stream);
 }

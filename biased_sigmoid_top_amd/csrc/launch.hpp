@@ -64,11 +64,11 @@ hipError_t launch_down_tiled_fp8(const uint8_t* Hq, const uint8_t* Wq, const flo
                                  const float* Hs, const int32_t* offsets, const int32_t* row2slot,
                                  float* Y, int64_t N, hipStream_t stream);
 
-// Grouped path, LDS-tiled MFMA kernels.  Where gateup_groups_slots(N) the
-// gate/up kernels group the slots themselves from idx (no dispatch step)
-// and write offsets and row2slot for the down kernels; otherwise they read
-// the dispatch step's.
-bool gateup_groups_slots(int64_t N);
+// Grouped path, LDS-tiled MFMA kernels.  Where gateup_groups_slots(N, fp8)
+// the gate/up kernels (bf16 or FP8 mode) group the slots themselves from idx
+// (no dispatch step) and write offsets and row2slot for the down kernels;
+// otherwise they read the dispatch step's.
+bool gateup_groups_slots(int64_t N, bool fp8);
 hipError_t launch_gateup_tiled(const uint16_t* X, const uint16_t* Wgu, const int32_t* idx,
                                int32_t* offsets, int32_t* row2slot, uint16_t* H, int64_t N,
                                hipStream_t stream);

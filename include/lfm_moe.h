@@ -209,9 +209,10 @@ size_t lfm_moe_workspace_offset(int64_t N, int region);
  * The workspace holds the intermediate results listed in lfm_moe_ws_region
  * after the call completes.  Batches of up to 4 tokens take the
  * weight-streaming kernels, which group their own tokens and leave
- * BLOCKCOUNTS, OFFSETS and ROW2SLOT unwritten; batches of 5 to 256 tokens
+ * BLOCKCOUNTS, OFFSETS and ROW2SLOT unwritten; batches of 5 to 512 tokens
  * are grouped by the gate/up kernel, which writes OFFSETS and ROW2SLOT
- * (BLOCKCOUNTS stays unwritten); larger batches write all three.
+ * (BLOCKCOUNTS stays unwritten); larger batches write all three.  (The FP8
+ * layer groups 5 to 256 tokens in its gate/up kernel.)
  * Concurrent calls need distinct workspaces.
  */
 lfm_moe_status lfm_moe_forward_ws(const uint16_t* X, const uint16_t* W_r, const float* bias,
@@ -361,8 +362,9 @@ lfm_moe_status lfm_moe_stack_forward_ws(float* x_inout, const lfm_moe_block_weig
  *   codes are summed per 128-wide K group, then scaled by weight scale x
  *   activation scale; out [N, 2048] fp32.  Up to LFM_MOE_FP8_STREAM_TOKENS
  *   tokens the expert kernels stream the weights and quantise the rows in
- *   registers (exact products, fp32 sums); above, the dispatch step groups
- *   the rows, X and H are quantised into the XQ/XS and HQ/HS workspace
+ *   registers (exact products, fp32 sums); above, the rows are grouped by
+ *   expert (by the gate/up kernel up to 256 tokens, by the dispatch step
+ *   beyond), X and H are quantised into the XQ/XS and HQ/HS workspace
  *   regions and the grouped kernels multiply on the FP8 matrix core, whose
  *   sums are not fp32 sums: it aligns each step's 64 products and drops the
  *   bits below the alignment (measured: within 2^-11.6 of the sum of their

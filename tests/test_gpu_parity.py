@@ -435,10 +435,12 @@ def test_concurrent_streams_with_distinct_workspaces(moe):
 
 def test_stage_timing_counts_and_times(moe):
     """lfm_moe_timing_*: with timing on, each call records one launch per
-    stage it runs (no dispatch stage up to 256 tokens) with a positive
-    time; after timing is switched off nothing more is recorded."""
+    stage it runs (no dispatch stage up to 512 tokens, where the gate/up
+    kernel groups the slots) with a positive time; after timing is switched
+    off nothing more is recorded."""
     for N, stages in ((3, ("route", "gateup", "down", "combine")),
-                      (300, ("route", "dispatch", "gateup", "down", "combine"))):
+                      (300, ("route", "gateup", "down", "combine")),
+                      (600, ("route", "dispatch", "gateup", "down", "combine"))):
         inp, dev = _layer_case(N, 1200 + N)
         args = (dev["X"], dev["W_r"], dev["bias"], dev["W_gateup"], dev["W_down"])
         _step(f"stage timing N={N}")
