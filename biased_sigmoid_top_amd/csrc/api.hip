@@ -317,12 +317,14 @@ static_assert(kDecodeMaxTokens == LFM_MOE_FP8_STREAM_TOKENS && kDecodeMaxTokens 
 
 // The router's outputs in the workspace: from the router, or copied from
 // caller-given selections and weights (idx_in, w_in not null), with the
-// per-block histogram when the grouped path needs it.
+// per-block histogram when the grouped path needs it.  With Xq (FP8 layer)
+// the router also quantises X into Xq / Xs; the copy does not.
 hipError_t route_or_ingest(const uint16_t* X, const uint16_t* W_r, const float* bias,
                            const int32_t* idx_in, const float* w_in, int32_t* idx, float* w,
-                           int32_t* blockcounts, float* part, int n, hipStream_t stream) {
+                           int32_t* blockcounts, float* part, int n, hipStream_t stream,
+                           uint8_t* Xq = nullptr, float* Xs = nullptr) {
   if (idx_in != nullptr) return launch_ingest_routing(idx_in, w_in, idx, w, blockcounts, n, stream);
-  return launch_route(X, W_r, bias, idx, w, blockcounts, part, n, stream);
+  return launch_route(X, W_r, bias, idx, w, blockcounts, part, n, stream, Xq, Xs);
 }
 
 // route -> [dispatch] -> gate/up -> down -> combine.  Arguments already
@@ -431,9 +433,15 @@ lfm_moe_status run_fp8(const uint16_t* X, const uint16_t* W_r, const float* bias
   const bool streaming = N <= LFM_MOE_FP8_STREAM_TOKENS;
   const bool dispatch = !streaming && !gateup_groups_slots(N, true);
   int32_t* blockcounts = region<int32_t>(ws, N, LFM_MOE_WS_BLOCKCOUNTS);
+  uint8_t* Xq = region<uint8_t>(ws, N, LFM_MOE_WS_XQ);
+  float* Xs = region<float>(ws, N, LFM_MOE_WS_XS);
+  // The grouped path's router quantises X as it reads it (one launch fewer);
+  // caller-given routing leaves that to quantize_groups.
+  const bool route_quantises = !streaming && idx_in == nullptr;
   hipError_t e;
   if ((e = route_or_ingest(X, W_r, bias, idx_in, w_in, idx, w, dispatch ? blockcounts : nullptr, part,
-                           n, stream)) != hipSuccess)
+                           n, stream, route_quantises ? Xq : nullptr, route_quantises ? Xs : nullptr)) !=
+      hipSuccess)
     return hip_fail(e, idx_in ? "routing copy kernel launch" : "route kernel launch");
   timer.after(1);
   if (streaming) {
@@ -445,19 +453,18 @@ lfm_moe_status run_fp8(const uint16_t* X, const uint16_t* W_r, const float* bias
     timer.after(4);
   } else {
     // Grouped: dispatch (unless the gate/up kernel groups the slots), X
-    // quantised per group (timed as the dispatch stage), gate/up, H
-    // quantised per group (timed with down), down.
+    // quantised per group (by the router; with caller-given routing by
+    // quantize_groups, timed as the dispatch stage), gate/up, H quantised
+    // per group (timed with down), down.
     int32_t* offsets = region<int32_t>(ws, N, LFM_MOE_WS_OFFSETS);
     int32_t* row2slot = region<int32_t>(ws, N, LFM_MOE_WS_ROW2SLOT);
-    uint8_t* Xq = region<uint8_t>(ws, N, LFM_MOE_WS_XQ);
-    float* Xs = region<float>(ws, N, LFM_MOE_WS_XS);
     uint8_t* Hq = region<uint8_t>(ws, N, LFM_MOE_WS_HQ);
     float* Hs = region<float>(ws, N, LFM_MOE_WS_HS);
     if (dispatch && (e = launch_dispatch(idx, blockcounts, offsets, row2slot, n, stream)) != hipSuccess)
       return hip_fail(e, "dispatch kernel launch");
-    if ((e = launch_quantize_groups(X, N, kHidden, Xq, Xs, stream)) != hipSuccess)
+    if (!route_quantises && (e = launch_quantize_groups(X, N, kHidden, Xq, Xs, stream)) != hipSuccess)
       return hip_fail(e, "quantize kernel launch");
-    timer.after(2);
+    if (dispatch || !route_quantises) timer.after(2);
     if ((e = launch_gateup_tiled_fp8(Xq, W_gateup_fp8, scales_gateup, Xs, idx, offsets, row2slot, H,
                                      N, stream)) != hipSuccess)
       return hip_fail(e, "fp8 gate/up kernel launch");

@@ -28,8 +28,11 @@ hipError_t launch_rmsnorm(const float* x, uint16_t* X, int64_t N, hipStream_t st
 
 // Scratch bytes of the router's partial logits for N tokens.
 size_t route_partial_bytes(int64_t N);
+// With Xq and Xs (the FP8 layer's grouped path) the router also writes X's
+// E4M3 codes and group scales, as launch_quantize_groups(X, N, 2048, Xq, Xs).
 hipError_t launch_route(const uint16_t* X, const uint16_t* Wr, const float* bias, int32_t* idx,
-                        float* w, int32_t* blockcounts, float* part, int N, hipStream_t stream);
+                        float* w, int32_t* blockcounts, float* part, int N, hipStream_t stream,
+                        uint8_t* Xq = nullptr, float* Xs = nullptr);
 
 // Caller-given selections and weights -> workspace copies (ids made
 // memory-safe) and the per-block histogram (when blockcounts is not null).

@@ -26,6 +26,14 @@
 //    so it pays only once the split form's partial traffic is larger.
 //    Measured per call: N = 1024 split 9.2 us, fused 11.9; N = 4096 split
 //    18.6, fused 12.3.
+// For the FP8 layer's grouped path the router also writes X's E4M3 codes
+// and group scales: a K slice of 128 is one activation group (the
+// inferencekey.com page on the 24B reasoning MoE, "Für Engineers" part, the
+// quantisation entry: FP8 activations quantised dynamically per group of
+// 128), and the slice's wavefront already holds the group's 128 values of
+// each of its 16 rows, so no separate quantisation launch reads X again.
+// The codes and scales are those of quantize_groups_kernel (quant.hip):
+// the same fp32 decisions and the same byte order.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -56,15 +64,54 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+// E4M3 codes and scale of the 128-value group (row tok, group slice) whose
+// runs 4i + g (8 values each, i = 0..3) lane holds in a[i], g = lane / 16;
+// the four lanes of a row (lane % 16) hold the whole group.  Q: rows of 2048
+// codes, in every 32-wide piece the 8-code runs in the order 0, 2, 1, 3;
+// S: 16 scales per row.
+__device__ __forceinline__ void quantize_slice(const uint4 (&a)[4], int tok, bool real, int slice,
+                                               int lane, uint8_t* __restrict__ Q, float* __restrict__ S) {
+  const int g = lane >> 4;
+  // Largest magnitude on the bf16 bit patterns (finite values order as
+  // their bits), then over the row's four lanes.
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w[4] = {a[i].x, a[i].y, a[i].z, a[i].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m = max(m, max(w[k] & 0x7fffu, (w[k] >> 16) & 0x7fffu));
+  }
+  m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 16, kWave)));
+  m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 32, kWave)));
+  const float amax = __uint_as_float(m << 16);
+  const float inv = amax > 0.f ? 448.f / amax : 0.f;
+  auto q4 = [&](uint32_t lo, uint32_t hi) {
+    return e4m3x4(__uint_as_float(lo << 16) * inv, __uint_as_float(lo & 0xffff0000u) * inv,
+                  __uint_as_float(hi << 16) * inv, __uint_as_float(hi & 0xffff0000u) * inv);
+  };
+  if (!real) return;
+  uint8_t* row = Q + static_cast<size_t>(tok) * kHidden + slice * 128;
+  // Run 4i + g is run g of 32-wide piece i: 8-byte slot 0, 2, 1, 3 of it.
+  const int slot = ((g & 1) << 1) | (g >> 1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<uint2*>(row + 8 * (4 * i + slot)) = make_uint2(q4(a[i].x, a[i].y), q4(a[i].z, a[i].w));
+  if (g == 0) S[static_cast<size_t>(tok) * kSlices + slice] = amax / 448.f;
+}
+
 // Partial logits of token tile `tile` over K slice `slice`.  acc[et][r] of
 // a lane is expert et*16 + lane % 16, token 4 * (lane / 16) + r of the tile.
+// With Q (QUANT) the slice's group of each real token row is quantised too.
+template <bool QUANT>
 __device__ __forceinline__ void slice_partial(const uint16_t* __restrict__ X,
                                               const uint16_t* __restrict__ Wr, int tile, int slice,
-                                              int N, int lane, f32x4 (&acc)[4]) {
+                                              int N, int lane, f32x4 (&acc)[4],
+                                              uint8_t* __restrict__ Q, float* __restrict__ S) {
   const int r16 = lane & 15;
   const int g = lane >> 4;
   int tok = tile * kRouteTokens + r16;
-  tok = tok < N ? tok : N - 1;  // rows past N are computed and discarded
+  const bool real = tok < N;
+  tok = real ? tok : N - 1;  // rows past N are computed and discarded
   const int kb = slice * 128;
   const uint16_t* xrow = X + static_cast<size_t>(tok) * kHidden + kb;
   uint4 a[4], b[4][4];
@@ -84,6 +131,7 @@ __device__ __forceinline__ void slice_partial(const uint16_t* __restrict__ X,
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int et = 0; et < 4; ++et) acc[et] = mfma16(a[i], b[et][i], acc[et]);
+  if constexpr (QUANT) quantize_slice(a, tok, real, slice, lane, Q, S);
 }
 
 // Selection for one token on one wavefront (lane = expert), from the logit
@@ -137,12 +185,14 @@ __device__ __forceinline__ void store_histogram(int (&counts)[kRouteTokens][kExp
 }
 
 // part layout: [token tile][slice][16 tokens][64 experts] fp32.
+template <bool QUANT>
 __global__ __launch_bounds__(kWave) void route_partial_kernel(const uint16_t* __restrict__ X,
                                                               const uint16_t* __restrict__ Wr,
-                                                              float* __restrict__ part, int N) {
+                                                              float* __restrict__ part, int N,
+                                                              uint8_t* __restrict__ Q, float* __restrict__ S) {
   const int lane = threadIdx.x;
   f32x4 acc[4];
-  slice_partial(X, Wr, blockIdx.x / kSlices, blockIdx.x % kSlices, N, lane, acc);
+  slice_partial<QUANT>(X, Wr, blockIdx.x / kSlices, blockIdx.x % kSlices, N, lane, acc, Q, S);
   float* dst = part + static_cast<size_t>(blockIdx.x) * kRouteTokens * kExperts;
 #pragma unroll
   for (int et = 0; et < 4; ++et)
@@ -168,16 +218,18 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(
   if (blockcounts != nullptr) store_histogram(counts, t, lane, chosen, blockcounts);
 }
 
+template <bool QUANT>
 __global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wr, const float* __restrict__ bias,
-    int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ blockcounts, int N) {
+    int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ blockcounts, int N,
+    uint8_t* __restrict__ Q, float* __restrict__ S) {
   __shared__ float part[kSlices][kRouteTokens][kPartStride];
   __shared__ int counts[kRouteTokens][kExperts];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   {
     f32x4 acc[4];
-    slice_partial(X, Wr, blockIdx.x, wave, N, lane, acc);
+    slice_partial<QUANT>(X, Wr, blockIdx.x, wave, N, lane, acc, Q, S);
 #pragma unroll
     for (int et = 0; et < 4; ++et)
 #pragma unroll
@@ -203,15 +255,17 @@ size_t route_partial_bytes(int64_t N) {
 }
 
 hipError_t launch_route(const uint16_t* X, const uint16_t* Wr, const float* bias, int32_t* idx,
-                        float* w, int32_t* blockcounts, float* part, int N, hipStream_t stream) {
+                        float* w, int32_t* blockcounts, float* part, int N, hipStream_t stream,
+                        uint8_t* Xq, float* Xs) {
   const int tiles = (N + kRouteTokens - 1) / kRouteTokens;
+  const bool quant = Xq != nullptr;
   if (N > kSplitMaxTokens) {
-    hipLaunchKernelGGL(route_fused_kernel, dim3(tiles), dim3(kFusedThreads), 0, stream, X, Wr, bias,
-                       idx, w, blockcounts, N);
+    hipLaunchKernelGGL(quant ? route_fused_kernel<true> : route_fused_kernel<false>, dim3(tiles),
+                       dim3(kFusedThreads), 0, stream, X, Wr, bias, idx, w, blockcounts, N, Xq, Xs);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(route_partial_kernel, dim3(tiles * kSlices), dim3(kWave), 0, stream, X, Wr,
-                     part, N);
+  hipLaunchKernelGGL(quant ? route_partial_kernel<true> : route_partial_kernel<false>,
+                     dim3(tiles * kSlices), dim3(kWave), 0, stream, X, Wr, part, N, Xq, Xs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(route_select_kernel, dim3(tiles), dim3(kSelectThreads), 0, stream, part, bias,
