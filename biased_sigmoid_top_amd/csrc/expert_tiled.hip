@@ -186,7 +186,8 @@ __device__ __forceinline__ void group_slots_lds(const int32_t* __restrict__ idx,
   __syncthreads();
 }
 
-template <bool GATEUP, int FB_, int WAVES_, int TB_, bool FP8 = false, bool NTW = false, bool SELF = false>
+template <bool GATEUP, int FB_, int WAVES_, int TB_, bool FP8 = false, bool NTW = false, bool SELF = false,
+          bool OFF32 = true>
 __global__ __launch_bounds__((TileShape<GATEUP, FB_, WAVES_, TB_>::kThreads),
                              (TileShape<GATEUP, FB_, WAVES_, TB_>::kPerCu))
 void expert_tiled_kernel(
@@ -260,14 +261,34 @@ void expert_tiled_kernel(
   // lanes read one whole line.  With 32 or more rows per pass the pieces
   // share r0 % 32, so their LDS positions differ by whole token-block
   // fragments (the 2-wavefront shapes take 16 rows per pass).
+  // OFF32 (token matrices below 2 GB; the host picks it): the rows are read
+  // through a buffer resource over the token matrix with 32-bit offsets,
+  // and a padding row of the tile takes an offset past its end, which the
+  // range check turns into zeros with no memory read.  A CU's L1 request
+  // rate bounds these kernels, so the padding rows' bytes cost time
+  // (measured, layer us, 64-bit row pointers with padding rows reading row
+  // 0 / this form: N = 1,024 256.8-259.4 / 249.9-250.7, 2,048 342.2-343.5 /
+  // 331.5-331.8, 4,096 459.7-463.0 / 452.5-452.8; one register per token
+  // piece instead of two also removes the spills of the two-block down
+  // shapes).  The padding rows' products are zeros and are dropped.
+  // Otherwise 64-bit row pointers, a padding row reading row 0's bytes.
+  constexpr bool kPadZero = OFF32;
+  constexpr uint32_t kPadOff = 0x80000000u;
+  const Rsrc ar = make_rsrc(A, kPadZero ? static_cast<uint32_t>(
+                                              static_cast<uint64_t>(GATEUP ? ntok : kTopK * ntok) * kRowBytes)
+                                        : 0u);
   const int r0 = tid / 8, c = tid % 8;
-  const uint8_t* arow[T::kChunks];
+  uint32_t aoff[kPadZero ? T::kChunks : 1];
+  const uint8_t* arow[kPadZero ? 1 : T::kChunks];
 #pragma unroll
   for (int i = 0; i < T::kChunks; ++i) {
     const int r = r0 + T::kRowStep * i;
     const int slot = grp_rows[tile.row_begin + (r < tile.rows ? r : 0)];
-    arow[i] = static_cast<const uint8_t*>(A) +
-              static_cast<size_t>(GATEUP ? slot / kTopK : slot) * kRowBytes + c * 16;
+    const size_t off = static_cast<size_t>(GATEUP ? slot / kTopK : slot) * kRowBytes + c * 16;
+    if constexpr (kPadZero)
+      aoff[i] = r < tile.rows ? static_cast<uint32_t>(off) : kPadOff;
+    else
+      arow[i] = static_cast<const uint8_t*>(A) + off;
   }
   constexpr bool kWholeBlocks = T::kRowStep % 32 == 0;
   static_assert(T::kRowStep % 16 == 0 && T::kChunks >= 1, "whole 16-row groups per pass");
@@ -337,7 +358,12 @@ void expert_tiled_kernel(
   auto load_x = [&](int pair) {
     const int pc = pair < kPairs ? pair : kPairs - 1;
 #pragma unroll
-    for (int i = 0; i < T::kChunks; ++i) stg[i] = ld16(arow[i] + pc * kPairBytes);
+    for (int i = 0; i < T::kChunks; ++i) {
+      if constexpr (kPadZero)
+        stg[i] = buf_ld<false>(ar, aoff[i], pc * kPairBytes);
+      else
+        stg[i] = ld16(arow[i] + pc * kPairBytes);
+    }
   };
   auto store_x = [&](int pb) {
 #pragma unroll
@@ -643,10 +669,24 @@ hipError_t launch_tiled(const void* A, const void* W, const int32_t* idx, int32_
   uint16_t* H = nullptr;
   float* Y = nullptr;
   if constexpr (GATEUP) H = out; else Y = out;
-  hipLaunchKernelGGL((expert_tiled_kernel<GATEUP, FB, WAVES, TB, FP8, NTW, SELF>),
-                     dim3(tiled_grid<GATEUP, FB, WAVES, TB>(N)),
-                     dim3(TileShape<GATEUP, FB, WAVES, TB>::kThreads), 0, stream, A, W, idx,
-                     static_cast<int>(N), offsets, row2slot, H, Y, Ws, As);
+  // Token matrices below 2 GB are addressed with 32-bit offsets, padding
+  // rows with offset 2^31 (see the kernel); the one-block shapes serve at
+  // most 2,048 tokens, whose token matrices always are.
+  constexpr int kRowBytes = (GATEUP ? kHidden : kFF) * (FP8 ? 1 : 2);
+  const bool off32 = (GATEUP ? N : kTopK * N) * kRowBytes < (int64_t{1} << 31);
+  const dim3 grid(static_cast<unsigned>(tiled_grid<GATEUP, FB, WAVES, TB>(N)));
+  const dim3 block(TileShape<GATEUP, FB, WAVES, TB>::kThreads);
+  if constexpr (FB == 1) {
+    if (!off32) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((expert_tiled_kernel<GATEUP, FB, WAVES, TB, FP8, NTW, SELF, true>), grid, block, 0,
+                       stream, A, W, idx, static_cast<int>(N), offsets, row2slot, H, Y, Ws, As);
+  } else if (off32) {
+    hipLaunchKernelGGL((expert_tiled_kernel<GATEUP, FB, WAVES, TB, FP8, NTW, SELF, true>), grid, block, 0,
+                       stream, A, W, idx, static_cast<int>(N), offsets, row2slot, H, Y, Ws, As);
+  } else {
+    hipLaunchKernelGGL((expert_tiled_kernel<GATEUP, FB, WAVES, TB, FP8, NTW, SELF, false>), grid, block, 0,
+                       stream, A, W, idx, static_cast<int>(N), offsets, row2slot, H, Y, Ws, As);
+  }
   return hipGetLastError();
 }
 

@@ -327,6 +327,31 @@ def test_ragged_token_counts(moe, N):
     check_out(_np(out), expected_outputs(inp, r, np.arange(N), alt))
 
 
+def test_token_rows_beyond_2gb_sampled(moe):
+    """From 174,763 tokens the down kernels' hidden rows (4N x 1536 bf16)
+    pass 2 GB, and the grouped kernels read them through 64-bit row pointers
+    instead of 32-bit offsets into the token matrix (the gate/up kernels'
+    2,048-wide X rows stay below 2 GB: both forms in one call).  Every
+    output row is finite; 512 sampled tokens are checked against the oracle
+    (selections, weights and outputs)."""
+    N = 174_763
+    assert 4 * N * 1536 * 2 >= 1 << 31 > 4 * (N - 1) * 1536 * 2
+    inp0, dev0, _ = case("tiny_n32")
+    X = oracle.block_input(synth.hidden_states(N, 4242).numpy())
+    Xd = torch.from_numpy(X).to(torch.bfloat16).cuda()
+    _step(f"forward N={N} (hidden rows past 2 GB)")
+    out = moe.forward(Xd, dev0["W_r"], dev0["bias"], dev0["W_gateup"], dev0["W_down"])
+    idx, w = moe.route(Xd, dev0["W_r"], dev0["bias"])
+    del Xd
+    assert bool(torch.isfinite(out).all())
+    rng = np.random.default_rng(4242)
+    tokens = np.sort(np.concatenate([rng.choice(N, 500, replace=False), np.arange(N - 12, N)]))
+    sub = dict(inp0, X=X[tokens])
+    r = oracle.route(sub["X"], sub["W_r"], sub["bias"])
+    alt = check_route(_np(idx)[tokens], _np(w)[tokens], r)
+    check_out(_np(out)[tokens], expected_outputs(sub, r, np.arange(len(tokens)), alt))
+
+
 @pytest.mark.parametrize("N", [5, 96, 512, 1000])
 def test_every_token_on_the_same_four_experts(moe, N):
     """Degenerate routing: a large bias puts every token on experts 60..63
