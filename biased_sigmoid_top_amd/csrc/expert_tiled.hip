@@ -755,7 +755,8 @@ hipError_t launch_down_tiled_fp8(const uint8_t* Hq, const uint8_t* Wq, const flo
     return launch_tiled<false, 1, 4, 4, true, true>(Hq, Wq, nullptr, off, r2s, Y, N, stream, Ws, Hs);
   if (N <= kFp8NarrowTokens)
     return launch_tiled<false, 1, 4, 4, true>(Hq, Wq, nullptr, off, r2s, Y, N, stream, Ws, Hs);
-  // The two-block shapes spill a few registers, outside the stage loop.
+  // The two-block shapes spill a few registers (outside the stage loop)
+  // only with 64-bit row pointers (token matrices of 2 GB or more).
   if (N <= 6144)
     return launch_tiled<false, 2, 4, 4, true>(Hq, Wq, nullptr, off, r2s, Y, N, stream, Ws, Hs);
   return launch_tiled<false, 2, 8, 4, true>(Hq, Wq, nullptr, off, r2s, Y, N, stream, Ws, Hs);
