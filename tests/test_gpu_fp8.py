@@ -257,6 +257,40 @@ def test_fp8_forward_ragged(moe, N):
     _check_fp8_forward(moe, inp, dev, q, N)
 
 
+def test_fp8_token_rows_beyond_2gb_sampled(moe):
+    """From 349,526 tokens the FP8 down kernels' quantised hidden rows (4N x
+    1536 E4M3 codes) pass 2 GB, and the grouped kernels read them through
+    64-bit row pointers instead of 32-bit offsets (the gate/up kernels'
+    2,048-byte X code rows stay below 2 GB: both forms in one call).  Every
+    output row is finite; for 512 sampled tokens the selections are checked
+    against the oracle and the outputs by parity.fp8_output_check on the
+    GPU's own H."""
+    from biased_sigmoid_top_amd import _lib
+    N = 349_526
+    assert 4 * N * 1536 >= 1 << 31 > 4 * (N - 1) * 1536
+    inp0, dev0, q = _decode_case(moe)
+    X = oracle.block_input(synth.hidden_states(N, 4343).numpy())
+    Xd = torch.from_numpy(X).to(torch.bfloat16).cuda()
+    ws = moe.alloc_workspace(N)
+    _step(f"forward_fp8 N={N} (quantised hidden rows past 2 GB)")
+    out = moe.forward_fp8(Xd, dev0["W_r"], dev0["bias"], dev0["gateup_fp8"], dev0["down_fp8"], workspace=ws)
+    del Xd
+    assert bool(torch.isfinite(out).all())
+    rng = np.random.default_rng(4343)
+    tokens = np.sort(np.concatenate([rng.choice(N, 500, replace=False), np.arange(N - 12, N)]))
+    tk = torch.from_numpy(tokens).cuda()
+    slots = (tk[:, None] * 4 + torch.arange(4, device="cuda")).reshape(-1)
+    idx = _np(moe.workspace_view(ws, N, _lib.WS_IDX, torch.int32, (N, 4))[tk])
+    w = _np(moe.workspace_view(ws, N, _lib.WS_W, torch.float32, (N, 4))[tk]).astype(np.float64)
+    H = _np(moe.workspace_view(ws, N, _lib.WS_H, torch.bfloat16, (4 * N, 1536))[slots].float()).astype(np.float64)
+    o = _np(out[tk])
+    del ws, out
+    r = oracle.route(X[tokens], inp0["W_r"], inp0["bias"])
+    check_route(idx, w, r)
+    res = fp8_output_check(o, idx.astype(np.int64), w, H, X[tokens], q)
+    print(f"[fp8] N={N} sampled: {res}", flush=True)
+
+
 def test_fp8_zero_tokens(moe):
     inp, dev, q = _decode_case(moe)
     X = dev["X"][:0]
