@@ -19,13 +19,16 @@
 //    slice) and stores the partials to the workspace, route_select reduces
 //    them.  With N = 64 that is 64 wavefronts on 64 CUs, so the router
 //    matrix is pulled through many CUs at once.
-//  * Fused (above 2048 tokens): one 16-wavefront workgroup per tile, the
-//    partials staged in LDS -- one launch, no scratch traffic.  Each tile's
-//    CU then reads the whole 256 KB router matrix, which costs about 12 us
-//    however few tiles run (the rate at which one CU's misses are served),
-//    so it pays only once the split form's partial traffic is larger.
-//    Measured per call: N = 1024 split 9.2 us, fused 11.9; N = 4096 split
-//    18.6, fused 12.3.
+//  * Fused (above 2048 tokens): a 16-wavefront workgroup per tile, the
+//    partials staged in LDS -- one launch, no scratch traffic.  Each
+//    workgroup's CU reads the whole 256 KB router matrix, which costs about
+//    12 us however few tiles run (the rate at which one CU's misses are
+//    served), so it pays only once the split form's partial traffic is
+//    larger.  Measured per call: N = 1024 split 9.2 us, fused 11.9; N = 4096
+//    split 18.6, fused 12.3.  Beyond 256 tiles (4,096 tokens) a workgroup
+//    takes several tiles in turn with its wavefronts' router slices kept in
+//    registers, so that each CU reads the router matrix once: at N = 16,384
+//    four tiles per workgroup.
 // For the FP8 layer's grouped path the router also writes X's E4M3 codes
 // and group scales: a K slice of 128 is one activation group (the
 // inferencekey.com page on the 24B reasoning MoE, "Für Engineers" part, the
@@ -47,6 +50,7 @@ constexpr int kSelectThreads = kRouteTokens * kWave;  // one wavefront per token
 constexpr int kFusedThreads = kSlices * kWave;        // one wavefront per slice
 constexpr int kPartStride = kExperts + 4;             // LDS row pitch: conflict-free partial stores
 constexpr int64_t kSplitMaxTokens = 2048;
+constexpr int kFusedMaxWorkgroups = 256;              // one per CU
 static_assert(kSlices == kRouteTokens, "the fused kernel's wavefronts serve as slices, then tokens");
 
 // Orders floats like their values as unsigned integers.
@@ -97,6 +101,35 @@ __device__ __forceinline__ void quantize_slice(const uint4 (&a)[4], int tok, boo
   for (int i = 0; i < 4; ++i)
     *reinterpret_cast<uint2*>(row + 8 * (4 * i + slot)) = make_uint2(q4(a[i].x, a[i].y), q4(a[i].z, a[i].w));
   if (g == 0) S[static_cast<size_t>(tok) * kSlices + slice] = amax / 448.f;
+}
+
+// Router rows of K slice `slice` as the B operands of slice_product.
+__device__ __forceinline__ void slice_weights(const uint16_t* __restrict__ Wr, int slice, int lane,
+                                              uint4 (&b)[4][4]) {
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+#pragma unroll
+  for (int et = 0; et < 4; ++et) {
+    const uint16_t* wrow = Wr + static_cast<size_t>(et * 16 + r16) * kHidden + slice * 128;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[et][i] = ld16(wrow + (4 * i + g) * 8);
+  }
+}
+
+// The products of slice_partial on router rows already loaded by
+// slice_weights; the token row pieces are left in a (row tok of X).
+__device__ __forceinline__ void slice_product(const uint16_t* __restrict__ X, const uint4 (&b)[4][4],
+                                              int tok, int slice, int lane, uint4 (&a)[4], f32x4 (&acc)[4]) {
+  const int g = lane >> 4;
+  const uint16_t* xrow = X + static_cast<size_t>(tok) * kHidden + slice * 128;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = ld16(xrow + (4 * i + g) * 8);
+#pragma unroll
+  for (int et = 0; et < 4; ++et) acc[et] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int et = 0; et < 4; ++et) acc[et] = mfma16(a[i], b[et][i], acc[et]);
 }
 
 // Partial logits of token tile `tile` over K slice `slice`.  acc[et][r] of
@@ -173,14 +206,14 @@ __device__ __forceinline__ bool select_token(float l, float b_e, int lane, int t
 // Per-tile expert histogram: counts[t][lane] holds whether token t chose the
 // lane's expert; wavefront 0 adds them up after the barrier.
 __device__ __forceinline__ void store_histogram(int (&counts)[kRouteTokens][kExperts], int t, int lane,
-                                                bool chosen, int32_t* __restrict__ blockcounts) {
+                                                bool chosen, int tile, int32_t* __restrict__ blockcounts) {
   counts[t][lane] = chosen ? 1 : 0;
   __syncthreads();
   if (t == 0) {
     int c = 0;
 #pragma unroll
     for (int w = 0; w < kRouteTokens; ++w) c += counts[w][lane];
-    blockcounts[static_cast<size_t>(blockIdx.x) * kExperts + lane] = c;
+    blockcounts[static_cast<size_t>(tile) * kExperts + lane] = c;
   }
 }
 
@@ -215,33 +248,50 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(
 #pragma unroll
   for (int s = 0; s < kSlices; ++s) l += p[s];
   const bool chosen = select_token(l, bias[lane], lane, blockIdx.x * kRouteTokens + t, N, idx_out, w_out);
-  if (blockcounts != nullptr) store_histogram(counts, t, lane, chosen, blockcounts);
+  if (blockcounts != nullptr) store_histogram(counts, t, lane, chosen, blockIdx.x, blockcounts);
 }
 
+// Tiles blockIdx.x * tiles_per_wg ... + tiles_per_wg - 1 (those below N),
+// one after the other.  Wavefront w multiplies K slice w of every tile with
+// the router rows of that slice, loaded once; the partials of a tile go
+// through LDS to the wavefront of each token, in slice order.
 template <bool QUANT>
 __global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wr, const float* __restrict__ bias,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ blockcounts, int N,
-    uint8_t* __restrict__ Q, float* __restrict__ S) {
+    uint8_t* __restrict__ Q, float* __restrict__ S, int tiles_per_wg) {
   __shared__ float part[kSlices][kRouteTokens][kPartStride];
   __shared__ int counts[kRouteTokens][kExperts];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  {
-    f32x4 acc[4];
-    slice_partial<QUANT>(X, Wr, blockIdx.x, wave, N, lane, acc, Q, S);
+  const int tiles = (N + kRouteTokens - 1) / kRouteTokens;
+  uint4 b[4][4];
+  slice_weights(Wr, wave, lane, b);
+  for (int k = 0; k < tiles_per_wg; ++k) {
+    const int tile = blockIdx.x * tiles_per_wg + k;
+    if (tile >= tiles) break;  // the same in every wavefront
+    {
+      int tok = tile * kRouteTokens + (lane & 15);
+      const bool real = tok < N;
+      tok = real ? tok : N - 1;  // rows past N are computed and discarded
+      uint4 a[4];
+      f32x4 acc[4];
+      slice_product(X, b, tok, wave, lane, a, acc);
 #pragma unroll
-    for (int et = 0; et < 4; ++et)
+      for (int et = 0; et < 4; ++et)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) part[wave][4 * (lane >> 4) + r][et * 16 + (lane & 15)] = acc[et][r];
+        for (int r = 0; r < 4; ++r) part[wave][4 * (lane >> 4) + r][et * 16 + (lane & 15)] = acc[et][r];
+      if constexpr (QUANT) quantize_slice(a, tok, real, wave, lane, Q, S);
+    }
+    __syncthreads();
+    const int t = wave;  // now: the token of this wavefront within the tile
+    float l = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kSlices; ++s) l += part[s][t][lane];
+    const bool chosen = select_token(l, bias[lane], lane, tile * kRouteTokens + t, N, idx_out, w_out);
+    if (blockcounts != nullptr) store_histogram(counts, t, lane, chosen, tile, blockcounts);
+    __syncthreads();  // part and counts are rewritten by the next tile
   }
-  __syncthreads();
-  const int t = wave;  // now: the token of this wavefront within the tile
-  float l = 0.0f;
-#pragma unroll
-  for (int s = 0; s < kSlices; ++s) l += part[s][t][lane];
-  const bool chosen = select_token(l, bias[lane], lane, blockIdx.x * kRouteTokens + t, N, idx_out, w_out);
-  if (blockcounts != nullptr) store_histogram(counts, t, lane, chosen, blockcounts);
 }
 
 }  // namespace
@@ -260,8 +310,10 @@ hipError_t launch_route(const uint16_t* X, const uint16_t* Wr, const float* bias
   const int tiles = (N + kRouteTokens - 1) / kRouteTokens;
   const bool quant = Xq != nullptr;
   if (N > kSplitMaxTokens) {
-    hipLaunchKernelGGL(quant ? route_fused_kernel<true> : route_fused_kernel<false>, dim3(tiles),
-                       dim3(kFusedThreads), 0, stream, X, Wr, bias, idx, w, blockcounts, N, Xq, Xs);
+    const int per_wg = (tiles + kFusedMaxWorkgroups - 1) / kFusedMaxWorkgroups;
+    const int wgs = (tiles + per_wg - 1) / per_wg;
+    hipLaunchKernelGGL(quant ? route_fused_kernel<true> : route_fused_kernel<false>, dim3(wgs),
+                       dim3(kFusedThreads), 0, stream, X, Wr, bias, idx, w, blockcounts, N, Xq, Xs, per_wg);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(quant ? route_partial_kernel<true> : route_partial_kernel<false>,
