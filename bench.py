@@ -164,7 +164,9 @@ def prepare_fp8(p):
     return q
 
 
-def time_steps(p, steps, warmup):
+def time_steps(p, steps, warmup, min_warm_ms=0.0):
+    """warmup untimed steps (continued, for a large workload, until they have
+    taken min_warm_ms), then the timed steps."""
     import torch
     import biased_sigmoid_top_amd as moe
     c = len(p["Wgu"])
@@ -175,9 +177,15 @@ def time_steps(p, steps, warmup):
         else:
             moe.forward(p["X"], p["W_r"], p["bias"], p["Wgu"][i % c], p["Wd"][i % c], p["out"])
 
+    tw = time.perf_counter()
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+    i = warmup
+    while (time.perf_counter() - tw) * 1e3 < min_warm_ms:
+        step(i)
+        i += 1
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         step(i)
@@ -272,12 +280,12 @@ def summarize_fp8(p, wall_ms, per_kernel, label, note):
                 kernel_ms=per_kernel, roofline=roof, note=note)
 
 
-def measure_fp8(p, steps, warmup, label, note, q=None):
+def measure_fp8(p, steps, warmup, label, note, q=None, min_warm_ms=0.0):
     """FP8 steps on workload p (packing its experts unless q, a prepare_fp8
     result of the same layer, is given)."""
     q = prepare_fp8(p) if q is None else dict(q, N=p["N"], X=p["X"], out=p["out"], counts=p["counts"])
     log(f"timing {label} (FP8 experts, {p['name']}): {steps} steps")
-    w, k = time_steps(q, steps, warmup)
+    w, k = time_steps(q, steps, warmup, min_warm_ms)
     e = summarize_fp8(q, w, k, label, note)
     log(json.dumps(e))
     del q
@@ -465,7 +473,7 @@ def main():
         p2 = prepare(args.secondary, args.copies)
         steps2 = max(5, args.steps // 10)
         log(f"timing {args.secondary}: {steps2} steps")
-        w2, k2 = time_steps(p2, steps2, max(2, args.warmup // 10))
+        w2, k2 = time_steps(p2, steps2, long_warmup(args), LONG_WARM_MS)
         second = summarize(p2, w2, k2)
         log(json.dumps(second))
         del p2
@@ -485,7 +493,7 @@ def main():
         p3 = prepare("skewed_n16384", args.copies)
         steps3 = max(5, args.steps // 10)
         log(f"timing skewed_n16384: {steps3} steps")
-        w3, k3 = time_steps(p3, steps3, max(2, args.warmup // 10))
+        w3, k3 = time_steps(p3, steps3, long_warmup(args), LONG_WARM_MS)
         s3 = summarize(p3, w3, k3)
         line["skewed"] = dict(config_entry("C3", s3), workload="skewed_n16384",
                               roofline=roofline(s3, "skewed_n16384"))
@@ -497,6 +505,17 @@ def main():
     if args.configs:
         line["configs"] = measure_configs(args)
     print(json.dumps(line), flush=True)
+
+
+def long_warmup(args):
+    """Untimed steps before the few timed steps of a large workload: at least
+    two passes over the weight copies, and at least LONG_WARM_MS of them, so
+    that no copy is first used, and the clock is not still rising, inside
+    the timed region."""
+    return max(2 * args.copies, args.warmup // 10)
+
+
+LONG_WARM_MS = 30.0
 
 
 def build_line(args, h, seed, second=None, cpu=None):
@@ -666,7 +685,8 @@ def measure_configs(args):
         p = prepare(name, args.copies, zero_bias)
         steps = args.steps if p["N"] <= 512 else max(5, args.steps // 10)
         log(f"timing {label} ({name}): {steps} steps")
-        w, k = time_steps(p, steps, max(2, args.warmup // (1 if p["N"] <= 512 else 10)))
+        w, k = (time_steps(p, steps, args.warmup) if p["N"] <= 512 else
+                time_steps(p, steps, long_warmup(args), LONG_WARM_MS))
         e = config_entry(label, summarize(p, w, k), note)
         log(json.dumps(e))
         out.append(e)
@@ -674,9 +694,9 @@ def measure_configs(args):
             out.append(measure_fp8(p, steps, args.warmup, "F1u",
                                    "supplementary: C1u with FP8 block-scaled experts"))
         if label == "C2":
-            out.append(measure_fp8(p, steps, max(2, args.warmup // 10), "F2",
+            out.append(measure_fp8(p, steps, long_warmup(args), "F2",
                                    "supplementary: C2 with FP8 block-scaled experts (grouped kernels "
-                                   "in FP8 mode)"))
+                                   "in FP8 mode)", min_warm_ms=LONG_WARM_MS))
         del p
         torch.cuda.empty_cache()
     e = measure_stack(max(3, args.steps // 40), 1)
