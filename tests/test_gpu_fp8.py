@@ -244,6 +244,9 @@ def test_fp8_forward_skewed_all_tokens(moe):
     print(f"  all {N} tokens ({len(alt)} near ties with another accepted set): out vs FP8 oracle on the "
           f"GPU's H {res['same_codes']:.2e}, end to end {res['end_to_end']:.4f} ({res['code_flips']} H codes "
           f"and {res['scale_flips']} group scales differ)", flush=True)
+    # The router quantises X here four 16-token tiles per workgroup, the
+    # dispatch-sized path's byte order included.
+    _check_quantised_regions(moe, ws, N, inp["X"], H)
 
 
 @pytest.mark.parametrize("N", [1, 4, 5, 17, 33, 95, 96, 97, 160, 255, 256, 257, 700, 2049, 4096])
